@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the W12 tree-verification pass on one MI355X.
+
+Workload: the 27B-like dense target (64 layers, hidden 5120, GQA 40/8 x 128,
+SwiGLU 17408, vocab 151936, random-init W12 weights), committed context 4096,
+32-node best-first draft trees whose tokens come from the target's own top-4
+(p = 0.7), one ``verify_step`` per step (forward over all nodes, LM-head
+argmax, acceptance walk, KV commit) plus the readback of the accepted length.
+
+Prints one JSON line: verify steps/s (``value``), tokens/s, the achieved HBM
+GB/s of the whole step, the roofline entry of the dominant kernel (the fused
+gate/up W12 GEMM, timed with HIP events on its own stream) and the CPU
+oracle's rate on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W12 tree-verify steps/s + achieved HBM GB/s (27B-like, 32-node tree), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def w12_algorithmic_bytes(n_out: int, k_in: int, n_esc: int) -> int:
+    """Bytes of the canonical W12 format: planes, base, escape pointers, 4 per escape."""
+    return n_out * k_in + n_out * ((k_in + 1) // 2) + n_out + 4 * (n_out + 1) + 4 * n_esc
+
+
+def build_model(cfg, seed: int, s_max: int, max_nodes: int):
+    import torch
+
+    from synth.configs import gen_embed, gen_final_norm, gen_kv_context, gen_layer, gen_lm_head
+    from tree_verification_pass_amd.model import DeviceModel, Dims
+
+    dev = torch.device("cuda:0")
+    esc = {}
+
+    def layer_fn(layer):
+        if layer % 8 == 0:
+            log(f"bench: converting layer {layer}/{cfg.n_layers} to W12")
+        return gen_layer(cfg, seed, layer, device=dev, gains="ones")
+
+    def kv_fn(layer):
+        return gen_kv_context(cfg, seed, layer, cfg.ctx_len, s_max, device=dev)
+
+    t0 = time.perf_counter()
+    dm = DeviceModel(Dims.of(cfg), gen_embed(cfg, seed, dev), gen_final_norm(cfg, seed, dev),
+                     gen_lm_head(cfg, seed, dev), layer_fn, kv_fn, s_max=s_max, max_nodes=max_nodes)
+    torch.cuda.synchronize()
+    log(f"bench: model ready in {time.perf_counter() - t0:.1f} s")
+    return dm
+
+
+def make_trees(dm, cfg, n_trees: int, seed: int):
+    import torch
+
+    import tree_verification_pass_amd as tvp
+    from synth import best_first_topology
+    from synth.trees import assign_tokens_by_depth
+
+    rng = np.random.default_rng(seed)
+    dev = torch.device("cuda:0")
+    trees = []
+    for _ in range(n_trees):
+        parents, rank, _ = best_first_topology(rng, cfg.n_nodes)
+        root = int(rng.integers(cfg.vocab))
+
+        def topk_fn(tokens, par):
+            r = tvp.verify_step(dm.plan, cfg.ctx_len, torch.as_tensor(tokens, device=dev),
+                                torch.as_tensor(par, device=dev), commit=False, want_logits=True)
+            return torch.topk(r.logits, 4, dim=1).indices.cpu().numpy()
+
+        tokens = assign_tokens_by_depth(rng, parents, rank, root, cfg.vocab, topk_fn, p_top=0.7)
+        trees.append((torch.as_tensor(tokens.astype(np.int32), device=dev),
+                      torch.as_tensor(parents.astype(np.int32), device=dev)))
+    return trees
+
+
+def step_bytes(dm, cfg, mean_accepted: float) -> float:
+    """Algorithmic HBM bytes of one step (W12 stream + KV + embedding rows + commit)."""
+    n, L, hkv, d = cfg.n_nodes, cfg.ctx_len, cfg.n_kv_heads, cfg.head_dim
+    w = 0
+    for p in [dm.lm_head] + [x for Lr in dm.layers for x in (Lr.wqkv, Lr.wo, Lr.wgu, Lr.wdown)]:
+        w += w12_algorithmic_bytes(p.n_out, p.k_in, int(p.desc.n_esc))
+    per_layer_kv = 2 * (L + n) * hkv * d * 2 + 2 * n * hkv * d * 2
+    commit = cfg.n_layers * 2 * 2 * mean_accepted * hkv * d * 2
+    return float(w + cfg.n_layers * per_layer_kv + n * cfg.hidden * 2 + commit)
+
+
+def time_gateup(dm, cfg, iters: int):
+    """Dominant kernel: the fused gate/up W12 GEMM, rotated over the 64 layers'
+    distinct weights (no cache reuse), timed with HIP events on its stream."""
+    import torch
+
+    import tree_verification_pass_amd as tvp
+
+    dev = torch.device("cuda:0")
+    n, H, F = cfg.n_nodes, cfg.hidden, cfg.ffn
+    x = torch.randn(n, H, device=dev).to(torch.bfloat16)
+    u = torch.empty(n, F, dtype=torch.bfloat16, device=dev)
+    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=u.data_ptr(), ldy=F)
+    layers = dm.layers
+    for i in range(len(layers)):
+        tvp.w12_gemm_ex(x, layers[i].wgu, epi)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        tvp.w12_gemm_ex(x, layers[i % len(layers)].wgu, epi)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / iters
+    p = layers[0].wgu
+    nbytes = (sum(w12_algorithmic_bytes(L.wgu.n_out, L.wgu.k_in, int(L.wgu.desc.n_esc)) for L in layers)
+              / len(layers) + n * H * 2 + n * F * 2)
+    return ms, nbytes, p
+
+
+def cpu_baseline(dm, cfg, seed: int, tree):
+    """The oracle (untuned) on one of the 64 decoder layers of one step: W12
+    decode of the layer's four weights plus the layer's forward over the 32
+    nodes; the step estimate scales that by total/layer streamed weights."""
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import model as om
+    from oracle import w12 as ow12
+    from synth.configs import gen_layer
+    from synth.weights import bf16_bits_numpy
+
+    dev = torch.device("cuda:0")
+    layer = gen_layer(cfg, seed, 0, device=dev, gains="ones")
+    bits = {k: bf16_bits_numpy(v) for k, v in layer.items()}
+    del layer
+    enc = {k: (ow12.encode(v) if k in ("wqkv", "wo", "wgu", "wdown") else v) for k, v in bits.items()}
+    tokens, parents = (t.cpu().numpy() for t in tree)
+    h_bits = bf16_bits_numpy(dm.embed[torch.as_tensor(tokens.astype(np.int64), device=dev)])
+    kc = bf16_bits_numpy(dm.layers[0].k_cache[:, : cfg.ctx_len])
+    vc = bf16_bits_numpy(dm.layers[0].v_cache[:, : cfg.ctx_len])
+    dims = om.Dims.of(cfg)
+    from oracle.bf16 import from_bits
+    t0 = time.perf_counter()
+    model = om.OracleModel.from_w12(dims, np.zeros((1, cfg.hidden), np.uint16), [enc], bits["attn_norm"][:1],
+                                    None)
+    h = from_bits(h_bits)
+    pos = cfg.ctx_len + om._accept.depths(parents)
+    om.layer_forward(model, 0, h, pos, from_bits(kc), from_bits(vc), om.ancestor_mask(parents))
+    t_layer = time.perf_counter() - t0
+    w_layer = sum(a * b for a, b in cfg.linear_shapes().values())
+    est = t_layer * cfg.streamed_params() / w_layer
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": 1.0 / est, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"1 of {cfg.n_layers} decoder layers of one 32-node verify step (W12 decode of its 4 "
+                       f"weights + fp64 forward, ctx {cfg.ctx_len}): {t_layer:.2f} s, scaled by streamed "
+                       f"weights ({cfg.streamed_params() / w_layer:.2f}x) to a whole step of {est:.1f} s")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="27b")
+    ap.add_argument("--trees", type=int, default=8)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--gemm-iters", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: the verification pass runs on one GPU "
+              f"(one GPU's weights and KV cache, no collectives); run with --gpus 1", flush=True)
+        return 2
+
+    import torch
+
+    import tree_verification_pass_amd as tvp
+    from synth.configs import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    s_max = cfg.ctx_len + 64
+    dm = build_model(cfg, args.seed, s_max, cfg.n_nodes)
+    log("bench: drafting trees from the target's top-4")
+    trees = make_trees(dm, cfg, args.trees, args.seed + 1)
+    out = tvp._alloc_out(dm.plan, cfg.n_nodes, 1, False)
+
+    def step(i):
+        tokens, parents = trees[i % len(trees)]
+        tvp.verify_step(dm.plan, cfg.ctx_len, tokens, parents, commit=True, out=out)
+        return int(out.n_accepted.item())  # the step's one device-to-host readback
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    acc = []
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        acc.append(step(i))
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1000.0 / args.steps
+    dev_ms = ev0.elapsed_time(ev1) / args.steps
+    mean_acc = float(np.mean(acc))
+    steps_s = 1000.0 / ms
+    nbytes = step_bytes(dm, cfg, mean_acc)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"bench: {ms:.3f} ms/step, {steps_s:.1f} steps/s, {gbs:.0f} GB/s, mean accepted {mean_acc:.2f}")
+
+    g_ms, g_bytes, _ = time_gateup(dm, cfg, args.gemm_iters)
+    g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
+    log(f"bench: gate/up W12 GEMM {g_ms * 1000:.1f} us/launch, {g_gbs:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a sample")
+        cpu = cpu_baseline(dm, cfg, args.seed, trees[0])
+
+    line = {
+        "metric": METRIC,
+        "value": round(steps_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "device_ms_per_step": round(dev_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "tokens_per_s": round(steps_s * (mean_acc + 1.0), 2),
+        "mean_accepted": round(mean_acc, 3),
+        "achieved_hbm_gbs": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "bytes_per_step": int(nbytes),
+        "config": {"workload": f"{cfg.name}-like verify step, {cfg.n_nodes}-node best-first tree, ctx {cfg.ctx_len}",
+                   "n_layers": cfg.n_layers, "hidden": cfg.hidden, "heads": f"{cfg.n_heads}/{cfg.n_kv_heads}x{cfg.head_dim}",
+                   "ffn": cfg.ffn, "vocab": cfg.vocab, "nodes": cfg.n_nodes, "ctx_len": cfg.ctx_len,
+                   "weights": "W12 (random-init bf16, per-channel sigma log-uniform [0.005,0.05], 1% zeros, "
+                              "0.05% outliers x1000)", "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "w12_gemm_kernel (fused gate/up + SwiGLU, 34816x5120)", "bound": "hbm",
+                     "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "us_per_launch": round(g_ms * 1000.0, 2), "bytes_per_launch": int(g_bytes)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,291 @@
+/*
+ * tvp.h -- C ABI of the tree-verification pass with W12 weights on MI355X (gfx950).
+ *
+ * Sources (cited by page and section; "SpecPilot summary" is the onedev.kr
+ * page on SpecPilot, "SpecPilot review" the blog.secrett2633.cloud review):
+ *   - W12, its per-channel escape list and the register-decode GEMM kept
+ *     deterministic by stream-K: SpecPilot summary, section 무엇과 다른가;
+ *   - one forward pass of the target over every draft-tree token, then the
+ *     matched path and one bonus token: SpecPilot summary, sections 무엇인가
+ *     and 무엇과 다른가; SpecPilot review, section 3;
+ *   - "lossless" up to near-tie flips from reduction order (GEMM tiling, tree
+ *     attention): SpecPilot summary, section 전제와 한계.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named in comments as "device" point to GPU memory; "host" to
+ *     CPU memory.  All device buffers are owned by the caller; the library
+ *     never allocates device memory (scratch comes in through `ws`).
+ *   - Work is enqueued on `stream` and is complete when the stream is.  Only
+ *     w12_encode_count and w12_pack synchronise (documented there).
+ *   - Shapes, nulls and capacities are validated on the host before anything
+ *     is launched; a failure returns an error code and launches nothing.
+ *     Launch failures return TVP_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Handles are not thread-safe; calls that share a workspace must not
+ *     overlap in time.
+ *   - bf16 values are passed as their raw 16-bit patterns (uint16_t).
+ */
+#ifndef TVP_H
+#define TVP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status codes */
+enum {
+  TVP_OK = 0,
+  TVP_ERR_ARG = 1,       /* null pointer or invalid scalar argument */
+  TVP_ERR_SHAPE = 2,     /* dimensions inconsistent or unsupported */
+  TVP_ERR_TREE = 3,      /* malformed draft tree (also reported on device) */
+  TVP_ERR_CAPACITY = 4,  /* more nodes / context than the plan was built for */
+  TVP_ERR_FORMAT = 5,    /* W12 tensor fields out of range */
+  TVP_ERR_WORKSPACE = 6, /* workspace missing or too small */
+  TVP_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed */
+};
+
+/* Static string naming a status code. */
+const char* tvp_status_string(int status);
+
+/* ------------------------------------------------------------- W12 tensors
+ * Canonical W12 layout of a bf16 weight W[n_out][k_in] (one "channel" is one
+ * output row).  SpecPilot summary, section 무엇과 다른가: a per-channel
+ * 16-binade window [base, base+15] of normal exponents; each in-window weight
+ * is the 12-bit record  sign<<11 | (exp-base)<<7 | mantissa ; zeros,
+ * subnormals, infinities, NaNs and out-of-window values are escapes whose raw
+ * bf16 bits are listed per channel (escaped slots hold record 0).
+ *   hi      device uint8  [n_out][k_in]          record >> 4
+ *   lo      device uint8  [n_out][(k_in+1)/2]    record & 15, even k in the low nibble
+ *   base    device uint8  [n_out]                window base, 1..239
+ *   esc_ptr device uint32 [n_out+1]              CSR offsets into esc_idx/esc_val
+ *   esc_idx device uint16 [n_esc]                column, ascending per channel
+ *   esc_val device uint16 [n_esc]                raw bf16 bits
+ * The window is the one holding the most weights, the smallest base on ties.
+ * k_in must be <= 65536 (uint16 escape columns). */
+typedef struct tvp_w12 {
+  int64_t n_out;
+  int64_t k_in;
+  int64_t n_esc;
+  uint8_t* hi;
+  uint8_t* lo;
+  uint8_t* base;
+  uint32_t* esc_ptr;
+  uint16_t* esc_idx;
+  uint16_t* esc_val;
+} tvp_w12;
+
+/* Phase 1 of the offline conversion (SpecPilot summary, section 무엇과 다른가:
+ * models are converted to W12 ahead of serving).  From device bf16 weights
+ * `w` [n_out][k_in] (row-major), writes device `base` [n_out] and `esc_ptr`
+ * [n_out+1], then synchronises `stream` and returns the total number of
+ * escapes in *h_n_esc (host).  The caller sizes esc_idx/esc_val from it. */
+int w12_encode_count(const uint16_t* w, int64_t n_out, int64_t k_in, uint8_t* base,
+                     uint32_t* esc_ptr, int64_t* h_n_esc, hipStream_t stream);
+
+/* Phase 2: writes t->hi, t->lo, t->esc_idx, t->esc_val of the tensor whose
+ * base/esc_ptr w12_encode_count produced (t->n_esc must equal its count). */
+int w12_encode(const uint16_t* w, const tvp_w12* t, hipStream_t stream);
+
+/* Exact decode back to bf16 bits, device `out` [n_out][k_in] (test hook). */
+int w12_decode(const tvp_w12* t, uint16_t* out, hipStream_t stream);
+
+/* -------------------------------------------------- packed (GPU) W12 layout
+ * The GEMM streams W12 from a tiled copy of the same records: tiles of 32
+ * channels x 64 k, each 3072 contiguous bytes laid out in the order the
+ * 64 lanes of a wavefront load and decode them, plus per-tile-block escape
+ * lists.  It decodes to exactly the same bf16 values as the canonical layout
+ * (checked by w12_gemm parity).  `chan_map` chooses which canonical row lands
+ * in each packed channel, so fused epilogues find their operands in one tile:
+ *   TVP_CHAN_PLAIN   packed channel p = row p
+ *   TVP_CHAN_GATEUP  rows [gate F | up F]: tile t = gate rows 16t..16t+15 then
+ *                    up rows 16t..16t+15 (map_a = F)
+ *   TVP_CHAN_QKV     rows [q heads | k heads | v heads] of head size d:
+ *                    q/k tiles pair dims i and i+d/2 (16 each) for RoPE, v
+ *                    tiles are plain (map_a = n_heads, map_b = n_kv_heads,
+ *                    map_c = d; d % 32 == 0)                                  */
+enum { TVP_CHAN_PLAIN = 0, TVP_CHAN_GATEUP = 1, TVP_CHAN_QKV = 2 };
+
+typedef struct tvp_w12_packed {
+  int64_t n_out, k_in, n_esc;
+  int32_t n_tiles, n_kb; /* ceil over 32 packed channels, ceil(k_in/64) */
+  int32_t chan_map, map_a, map_b, map_c;
+  void* blob;            /* device, `bytes` long, caller-owned, 256-B aligned */
+  size_t bytes;
+  size_t off_rec, off_escoff, off_esc, off_b2, off_rowmap; /* offsets in blob */
+} tvp_w12_packed;
+
+/* Fills every field of *p except `blob` for the given shape and map. */
+int w12_pack_size(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, int32_t map_a,
+                  int32_t map_b, int32_t map_c, tvp_w12_packed* p);
+
+/* Builds the packed copy of canonical tensor `t` into p->blob (p from
+ * w12_pack_size with p->blob set).  Device scratch `ws` of
+ * w12_pack_workspace() bytes.  Synchronises `stream` once (the channel map
+ * is uploaded from host memory). */
+size_t w12_pack_workspace(int64_t n_out, int64_t k_in);
+int w12_pack(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ W12 GEMM
+ * Y[m][n_out] = X[m][k_in] . W^T with bf16 inputs and fp32 accumulation, the
+ * weights decoded from W12 in registers (SpecPilot summary, section
+ * 무엇과 다른가).  Split-K partial sums are reduced in a fixed order, so the
+ * result is bitwise identical from run to run (the page's deterministic
+ * stream-K requirement).  1 <= m <= 192.
+ *   x      device bf16 [m][ldx], 16-byte aligned, ldx >= k_in, ldx % 8 == 0
+ *   y      device, [m][ldy] fp32 if y_fp32 else bf16 (ldy >= n_out); rows
+ *          follow the canonical channel order whatever p->chan_map is
+ *   ws     device scratch of w12_gemm_workspace() bytes.  Its first 256 KiB
+ *          hold completion counters: they must be zero before the first call
+ *          and every call leaves them zero; the rest is scratch.  Do not share
+ *          one workspace between w12_gemm and other entry points.             */
+size_t w12_gemm_workspace(int64_t m, const tvp_w12_packed* w);
+int w12_gemm(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w, void* y,
+             int64_t ldy, int y_fp32, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Same GEMM with a fused epilogue (used by verify_step; exposed for tests). */
+enum {
+  TVP_EPI_F32 = 0,     /* y fp32 */
+  TVP_EPI_BF16 = 1,    /* y bf16 */
+  TVP_EPI_RESID = 2,   /* y bf16 = bf16(resid + acc); resid may alias y */
+  TVP_EPI_SWIGLU = 3,  /* TVP_CHAN_GATEUP: y bf16 [m][F] = bf16(silu(gate) * up) */
+  TVP_EPI_QKV = 4,     /* TVP_CHAN_QKV: RoPE on q and k at positions pos[m];
+                          q -> y bf16 [m][n_heads][d]; k, v -> caches at slot[m] */
+  TVP_EPI_ARGMAX = 5   /* argmax (int32 [m], ties -> smallest id) + optional fp32 logits */
+};
+
+typedef struct tvp_gemm_epilogue {
+  int32_t mode;
+  void* y;                 /* F32/BF16/RESID/SWIGLU/QKV output (see modes) */
+  int64_t ldy;
+  const uint16_t* resid;   /* RESID: bf16 [m][ldr] */
+  int64_t ldr;
+  const int32_t* pos;      /* QKV: device int32 [m] RoPE positions */
+  const int32_t* slot;     /* QKV: device int32 [m] cache slots for k and v */
+  uint16_t* k_cache;       /* QKV: device bf16 [n_kv_heads][s_stride][d] */
+  uint16_t* v_cache;
+  int64_t s_stride;
+  double rope_theta;
+  int32_t* argmax;         /* ARGMAX: device int32 [m] */
+  float* logits;           /* ARGMAX: optional device fp32 [m][ldl] (NULL = none) */
+  int64_t ldl;
+} tvp_gemm_epilogue;
+
+int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
+                const tvp_gemm_epilogue* epi, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------- tree attention
+ * Attention of n draft-tree nodes over a committed context and their own
+ * ancestors (SpecPilot summary, section 전제와 한계 names tree attention as
+ * one of the reduction orders that may flip near-ties).  Node i attends to
+ * cache slots [0, ctx_len) and to tree slots ctx_len + j for every ancestor
+ * j of i and i itself, where the tree's own keys/values are already in the
+ * cache at slots ctx_len + j.  Scores q.k/sqrt(d), softmax in fp32, GQA
+ * q-head h -> kv-head h / (hq/hkv).  Split over the keys with a fixed-order
+ * merge: deterministic.
+ *   q        device bf16 [n][hq][d] (already rotated)
+ *   k_cache  device bf16 [hkv][s_stride][d] (v_cache likewise)
+ *   parents  device int32 [n]: parents[0] = -1, 0 <= parents[i] < i
+ *   out      device bf16 [n][hq][d]
+ *   status   device int32 [1]: TVP_OK or TVP_ERR_TREE (then out is zero)
+ * n <= 64, d in {64, 128}, hq % hkv == 0, n * hq / hkv <= 256.
+ * ws: tree_attention_workspace() bytes, its first 256 bytes zero before the
+ * first call (left zero); not shared with other entry points.                */
+size_t tree_attention_workspace(int32_t n, int32_t hq, int32_t d, int32_t max_keys);
+int tree_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                   int64_t s_stride, int32_t ctx_len, const int32_t* parents, int32_t n, int32_t hq,
+                   int32_t hkv, int32_t d, uint16_t* out, int32_t* status, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------- acceptance
+ * Greedy acceptance (SpecPilot summary, section 무엇과 다른가: the matched
+ * path plus a bonus token).  acc[0] = 1; acc[i] = acc[parents[i]] and
+ * tokens[i] == argmax[parents[i]].  The deepest accepted node (smallest index
+ * on ties) ends the path; bonus = argmax at that node.  One workgroup.
+ *   argmax, tokens, parents  device int32 [n], n <= 1024
+ *   path        device int32 [n]: path[0..n_accepted] = root .. deepest node
+ *   n_accepted, bonus, status  device int32 [1]
+ * A malformed tree sets *status = TVP_ERR_TREE, n_accepted = 0, path[0] = 0,
+ * bonus = argmax[0].                                                          */
+int accept_path(const int32_t* argmax, const int32_t* tokens, const int32_t* parents, int32_t n,
+                int32_t* path, int32_t* n_accepted, int32_t* bonus, int32_t* status,
+                hipStream_t stream);
+
+/* ------------------------------------------------------ the verify pass */
+typedef struct tvp_layer {
+  tvp_w12_packed wqkv;   /* TVP_CHAN_QKV, [(hq+2hkv)d][hidden] */
+  tvp_w12_packed wo;     /* TVP_CHAN_PLAIN, [hidden][hq d] */
+  tvp_w12_packed wgu;    /* TVP_CHAN_GATEUP, [2 ffn][hidden] */
+  tvp_w12_packed wdown;  /* TVP_CHAN_PLAIN, [hidden][ffn] */
+  const uint16_t* attn_norm; /* device bf16 [hidden] */
+  const uint16_t* ffn_norm;  /* device bf16 [hidden] */
+  uint16_t* k_cache;     /* device bf16 [hkv][s_max][d] */
+  uint16_t* v_cache;     /* device bf16 [hkv][s_max][d] */
+} tvp_layer;
+
+typedef struct tvp_model_desc {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rope_theta, norm_eps;
+  int32_t s_max;               /* KV slots per layer and head */
+  const uint16_t* embed;       /* device bf16 [vocab][hidden] */
+  const uint16_t* final_norm;  /* device bf16 [hidden] */
+  tvp_w12_packed lm_head;      /* TVP_CHAN_PLAIN, [vocab][hidden] */
+  const tvp_layer* layers;     /* host array [n_layers]; copied by tvp_plan_create */
+} tvp_model_desc;
+
+typedef struct tvp_plan tvp_plan;
+
+/* Validates the description and builds host state for trees of up to
+ * max_nodes nodes in total (all requests of a batch together, <= 192). */
+int tvp_plan_create(const tvp_model_desc* desc, int32_t max_nodes, tvp_plan** plan);
+void tvp_plan_destroy(tvp_plan* plan);
+
+/* Device scratch needed by verify_step / verify_step_batched on this plan.
+ * It must be zero-filled before its first use; its counter region is left
+ * zero by every call.  Use it for this plan only. */
+size_t verify_step_workspace(const tvp_plan* plan);
+
+typedef struct tvp_verify_out {
+  int32_t* argmax;     /* device int32 [n] */
+  int32_t* path;       /* device int32 [n] */
+  int32_t* n_accepted; /* device int32 [1] */
+  int32_t* bonus;      /* device int32 [1] */
+  int32_t* status;     /* device int32 [1] */
+  float* logits;       /* optional device fp32 [n][vocab] (NULL = not written) */
+} tvp_verify_out;
+
+/* One verification pass of draft tree (tokens, parents) after ctx_len
+ * committed tokens: every node's next-token logits in one forward pass
+ * (node i at position ctx_len + depth(i), its K/V written to cache slot
+ * ctx_len + i), greedy acceptance, and -- if `commit` -- the accepted nodes'
+ * K/V moved to slots ctx_len .. ctx_len + n_accepted, so the next committed
+ * length is ctx_len + n_accepted + 1 and the bonus token is the next root.
+ *   tokens, parents  device int32 [n]; tokens[0] is the root token (the last
+ *                    committed-but-unprocessed token, e.g. the previous bonus)
+ * Requires ctx_len + n <= s_max and n <= max_nodes; depth <= 63.            */
+int verify_step(tvp_plan* plan, int32_t ctx_len, const int32_t* tokens, const int32_t* parents,
+                int32_t n, int32_t commit, const tvp_verify_out* out, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/* Batched pass (SpecPilot summary, section 무엇과 다른가: requests share one
+ * node budget): n_req requests, request r owning nodes node_ptr[r] ..
+ * node_ptr[r+1]-1 of the concatenated tokens/parents (parents are
+ * request-local), its own context length ctx_len[r] and its own KV cache
+ * region: slots [r*s_req, (r+1)*s_req) of every layer's cache.  Every GEMM
+ * runs once over all Σ n_r rows; attention, acceptance and commit run per
+ * request.  Outputs are per request: path [node_ptr[r] ..] (request-local
+ * node indices), n_accepted/bonus/status [r]; argmax/logits per global node.
+ *   ctx_len, node_ptr  host int32 arrays ([n_req], [n_req+1])              */
+int verify_step_batched(tvp_plan* plan, int32_t n_req, const int32_t* ctx_len,
+                        const int32_t* node_ptr, int32_t s_req, const int32_t* tokens,
+                        const int32_t* parents, int32_t commit, const tvp_verify_out* out,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TVP_H */

@@ -1,0 +1,315 @@
+"""GPU parity of the individual kernels against the CPU oracle (through the C ABI).
+
+W12 encoder bytes and decode: bit-exact.  GEMM: within the logits tolerance
+(max-abs-rel 2e-3) and within an fp32 accumulation bound, and bitwise
+reproducible.  Tree attention: within bf16 rounding bounds.  Acceptance: exact.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import w12 as ow12
+from oracle import model as om
+from oracle.accept import accept as oaccept
+from oracle.bf16 import from_bits, round_bf16
+from synth import LinearRecipe, best_first_topology, gen_linear_bf16, make_generator
+from synth.configs import LARGE_RECIPE, TINY_RECIPE
+from synth.weights import bf16_bits_numpy
+from tests.parity import row_max_abs_rel
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "w12_handworked.json")
+
+
+@pytest.fixture(scope="module")
+def tvp():
+    import tree_verification_pass_amd as m
+    return m
+
+
+def _u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _gpu_w12_equals_oracle(t, o: ow12.W12Tensor):
+    assert t.n_esc == o.n_esc
+    assert np.array_equal(t.hi.cpu().numpy(), o.hi)
+    assert np.array_equal(t.lo.cpu().numpy(), o.lo)
+    assert np.array_equal(t.base.cpu().numpy(), o.base)
+    assert np.array_equal(t.esc_ptr.cpu().numpy().view(np.uint32), o.esc_ptr)
+    if o.n_esc:
+        assert np.array_equal(_u16(t.esc_idx)[: o.n_esc], o.esc_idx)
+        assert np.array_equal(_u16(t.esc_val)[: o.n_esc], o.esc_val)
+
+
+def _cases():
+    g = json.load(open(GOLDEN))
+    hand = np.array([[int(x, 16) for x in r] for r in g["weights"]], dtype=np.uint16)
+    allpat = np.random.default_rng(7).permutation(65536).astype(np.uint16)
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((37, 1000)) * 10.0 ** rng.uniform(-6, 2, (37, 1))).astype(np.float32)
+    x[rng.random(x.shape) < 0.03] = 0
+    ragged = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    ragged[rng.random(ragged.shape) < 0.005] = 0x7FC1
+    cfg_w = bf16_bits_numpy(gen_linear_bf16(make_generator(3), 96, 5120, LARGE_RECIPE))
+    tiny_w = bf16_bits_numpy(gen_linear_bf16(make_generator(4), 64, 512, TINY_RECIPE))
+    return {"handworked": hand, "all_patterns_row": allpat[None, :], "all_patterns_256": allpat.reshape(256, 256),
+            "ragged": ragged, "large_recipe": cfg_w, "tiny_recipe": tiny_w}
+
+
+@pytest.mark.parametrize("name", list(_cases().keys()))
+def test_encoder_bytes_and_decode_bit_exact(tvp, cuda, name):
+    w = _cases()[name]
+    print(f"[w12 codec] {name} shape={w.shape}", flush=True)
+    wt = torch.from_numpy(w.view(np.int16).copy()).view(torch.bfloat16).to(cuda)
+    t = tvp.w12_encode(wt)
+    _gpu_w12_equals_oracle(t, ow12.encode(w))
+    assert np.array_equal(_u16(tvp.w12_decode(t)), w)
+
+
+def _packed(tvp, w_bits: np.ndarray, cuda, chan_map=0, a=0, b=0, c=0):
+    wt = torch.from_numpy(w_bits.view(np.int16).copy()).view(torch.bfloat16).to(cuda)
+    return tvp.w12_pack(tvp.w12_encode(wt), chan_map, a, b, c)
+
+
+def _x(m, k, seed, cuda):
+    g = make_generator(seed)
+    return torch.randn(m, k, generator=g).to(torch.bfloat16).to(cuda)
+
+
+def _check_gemm(y_fp32: np.ndarray, x_bits: np.ndarray, w_bits: np.ndarray):
+    xv, wv = from_bits(x_bits), from_bits(w_bits)
+    ref = xv @ wv.T
+    bound = np.abs(xv) @ np.abs(wv).T
+    k = xv.shape[1]
+    err = np.abs(y_fp32 - ref)
+    assert np.all(err <= 4.0 * k * 2.0 ** -24 * bound + 1e-30), float((err / (bound + 1e-30)).max())
+    assert row_max_abs_rel(y_fp32, ref).max() <= 2e-3
+    return ref
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 32, 33, 100, 192])
+def test_gemm_ragged_shapes(tvp, cuda, m):
+    w_bits = bf16_bits_numpy(gen_linear_bf16(make_generator(8), 1000, 1000, TINY_RECIPE))
+    print(f"[gemm] m={m} n=1000 k=1000", flush=True)
+    pw = _packed(tvp, w_bits, cuda)
+    x = _x(m, 1000, 100 + m, cuda)
+    y32 = tvp.w12_gemm(x, pw, out_fp32=True)
+    y16 = tvp.w12_gemm(x, pw, out_fp32=False)
+    torch.cuda.synchronize()
+    ref = _check_gemm(y32.cpu().numpy().astype(np.float64), _u16(x), w_bits)
+    # bf16 output is the fp32 result rounded once
+    assert np.array_equal(_u16(y16), np.asarray(
+        torch.from_numpy(y32.cpu().numpy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)))
+    # ... so it is within half a bf16 ulp of the fp32 result
+    g16 = from_bits(_u16(y16))
+    assert np.all(np.abs(g16 - y32.cpu().numpy()) <= 2.0 ** -8 * np.abs(y32.cpu().numpy()))
+    # bitwise reproducible
+    y32b = tvp.w12_gemm(x, pw, out_fp32=True)
+    assert torch.equal(y32, y32b)
+
+
+@pytest.mark.parametrize("n_out,k_in", [(17408, 5120), (5120, 17408), (6144, 5120)])
+@pytest.mark.parametrize("m", [1, 16, 32])
+def test_gemm_27b_shapes_sampled(tvp, cuda, n_out, k_in, m):
+    """Full 27B-like GEMM shapes (weights [K x N] read as K_in x N_out): every
+    output row is checked on a sample of 256 channels against the oracle."""
+    print(f"[gemm 27b] n_out={n_out} k_in={k_in} m={m}", flush=True)
+    g = make_generator(1000 + n_out + k_in, "cuda")
+    w = gen_linear_bf16(g, n_out, k_in, LARGE_RECIPE)
+    t = tvp.w12_encode(w)
+    pw = tvp.w12_pack(t)
+    x = _x(m, k_in, 7 + m, cuda)
+    y = tvp.w12_gemm(x, pw, out_fp32=True)
+    torch.cuda.synchronize()
+    cols = np.sort(np.random.default_rng(n_out + m).choice(n_out, 256, replace=False))
+    w_s = bf16_bits_numpy(w[torch.as_tensor(cols, device=cuda)])
+    _check_gemm(y.cpu().numpy()[:, cols].astype(np.float64), _u16(x), w_s)
+    # the encoder is checked byte for byte on the same sampled channels
+    o = ow12.encode(w_s)
+    assert np.array_equal(t.base.cpu().numpy()[cols], o.base)
+    assert np.array_equal(t.hi.cpu().numpy()[cols], o.hi)
+    y2 = tvp.w12_gemm(x, pw, out_fp32=True)
+    assert torch.equal(y, y2)
+
+
+def test_gemm_fused_epilogues(tvp, cuda):
+    H, F, hq, hkv, d = 1000, 1000, 6, 2, 64
+    m = 13
+    print("[gemm epilogues] resid/swiglu/qkv/argmax", flush=True)
+    rng = np.random.default_rng(0)
+    # residual
+    w_o = bf16_bits_numpy(gen_linear_bf16(make_generator(21), H, hq * d, TINY_RECIPE))
+    x = _x(m, hq * d, 1, cuda)
+    res = _x(m, H, 2, cuda)
+    y = res.clone()
+    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_RESID, y=y.data_ptr(), ldy=H, resid=y.data_ptr(), ldr=H)
+    tvp.w12_gemm_ex(x, _packed(tvp, w_o, cuda), epi)
+    torch.cuda.synchronize()
+    acc = from_bits(_u16(x)) @ from_bits(w_o).T
+    ref = round_bf16(from_bits(_u16(res)) + acc)
+    got = from_bits(_u16(y))
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-30)
+    assert np.mean(got == ref) > 0.98
+    # swiglu with the gate/up channel map
+    w_gu = bf16_bits_numpy(gen_linear_bf16(make_generator(22), 2 * F, H, TINY_RECIPE))
+    xb = _x(m, H, 3, cuda)
+    u = torch.zeros(m, F, dtype=torch.bfloat16, device=cuda)
+    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=u.data_ptr(), ldy=F)
+    tvp.w12_gemm_ex(xb, _packed(tvp, w_gu, cuda, tvp.TVP_CHAN_GATEUP, F), epi)
+    torch.cuda.synchronize()
+    gu = from_bits(_u16(xb)) @ from_bits(w_gu).T
+    ref = round_bf16(om.silu(gu[:, :F]) * gu[:, F:])
+    got = from_bits(_u16(u))
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+    # qkv: rope at positions, k and v written to cache slots
+    w_qkv = bf16_bits_numpy(gen_linear_bf16(make_generator(23), (hq + 2 * hkv) * d, H, TINY_RECIPE))
+    xa = _x(m, H, 4, cuda)
+    s_max = 64
+    kc = torch.zeros(hkv, s_max, d, dtype=torch.bfloat16, device=cuda)
+    vc = torch.zeros_like(kc)
+    q = torch.zeros(m, hq * d, dtype=torch.bfloat16, device=cuda)
+    pos = rng.integers(0, 9000, m).astype(np.int32)
+    slot = rng.permutation(s_max)[:m].astype(np.int32)
+    pos_t, slot_t = torch.as_tensor(pos, device=cuda), torch.as_tensor(slot, device=cuda)
+    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_QKV, y=q.data_ptr(), ldy=hq * d, pos=pos_t.data_ptr(),
+                              slot=slot_t.data_ptr(), k_cache=kc.data_ptr(), v_cache=vc.data_ptr(),
+                              s_stride=s_max, rope_theta=1e6)
+    tvp.w12_gemm_ex(xa, _packed(tvp, w_qkv, cuda, tvp.TVP_CHAN_QKV, hq, hkv, d), epi)
+    torch.cuda.synchronize()
+    qkv = from_bits(_u16(xa)) @ from_bits(w_qkv).T
+    q_ref = round_bf16(om.rope(qkv[:, : hq * d].reshape(m, hq, d), pos, 1e6)).reshape(m, hq * d)
+    k_ref = round_bf16(om.rope(qkv[:, hq * d: (hq + hkv) * d].reshape(m, hkv, d), pos, 1e6))
+    v_ref = round_bf16(qkv[:, (hq + hkv) * d:].reshape(m, hkv, d))
+    for got, ref in ((from_bits(_u16(q)), q_ref),
+                     (from_bits(_u16(kc)).transpose(1, 0, 2)[slot], k_ref),
+                     (from_bits(_u16(vc)).transpose(1, 0, 2)[slot], v_ref)):
+        assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-4 * np.abs(ref).max())
+        assert np.mean(got == ref) > 0.97
+    # argmax over a vocabulary, ties to the smallest id, plus the logits dump
+    V = 3000
+    w_lm = bf16_bits_numpy(gen_linear_bf16(make_generator(24), V, H, TINY_RECIPE))
+    w_lm[:, :] = w_lm[:, :]
+    am = torch.zeros(m, dtype=torch.int32, device=cuda)
+    lg = torch.zeros(m, V, dtype=torch.float32, device=cuda)
+    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_ARGMAX, argmax=am.data_ptr(), logits=lg.data_ptr(), ldl=V)
+    tvp.w12_gemm_ex(xa, _packed(tvp, w_lm, cuda), epi)
+    torch.cuda.synchronize()
+    lg_np = lg.cpu().numpy().astype(np.float64)
+    ref = from_bits(_u16(xa)) @ from_bits(w_lm).T
+    assert row_max_abs_rel(lg_np, ref).max() <= 2e-3
+    assert np.array_equal(am.cpu().numpy(), np.argmax(lg.cpu().numpy(), axis=1))
+
+
+def test_argmax_ties_go_to_smallest_id(tvp, cuda):
+    # identical channels produce exactly equal logits: the smallest id must win
+    H, V = 256, 2048
+    base = bf16_bits_numpy(gen_linear_bf16(make_generator(31), 1, H, TINY_RECIPE))
+    w = np.repeat(base, V, axis=0)
+    rng = np.random.default_rng(2)
+    w[rng.permutation(V)[:1500]] = bf16_bits_numpy(gen_linear_bf16(make_generator(32), 1500, H, TINY_RECIPE))
+    x = _x(4, H, 9, cuda)
+    am = torch.zeros(4, dtype=torch.int32, device=cuda)
+    lg = torch.zeros(4, V, dtype=torch.float32, device=cuda)
+    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_ARGMAX, argmax=am.data_ptr(), logits=lg.data_ptr(), ldl=V)
+    tvp.w12_gemm_ex(x, _packed(tvp, w, cuda), epi)
+    torch.cuda.synchronize()
+    lgn = lg.cpu().numpy()
+    assert np.array_equal(am.cpu().numpy(), np.argmax(lgn, axis=1))  # numpy: first maximum
+
+
+def _attn_case(cuda, n, hq, hkv, d, L, seed, parents=None):
+    rng = np.random.default_rng(seed)
+    if parents is None:
+        parents, _, _ = best_first_topology(rng, n)
+    s_max = L + n + 5
+    g = make_generator(seed)
+    q = torch.randn(n, hq, d, generator=g).to(torch.bfloat16)
+    kc = torch.randn(hkv, s_max, d, generator=g).to(torch.bfloat16)
+    vc = torch.randn(hkv, s_max, d, generator=g).to(torch.bfloat16)
+    return parents, q, kc, vc
+
+
+def _attn_ref(parents, q, kc, vc, L):
+    n = len(parents)
+    qv = from_bits(_u16(q))
+    kv = from_bits(_u16(kc))[:, : L + n]
+    vv = from_bits(_u16(vc))[:, : L + n]
+    vis = np.concatenate([np.ones((n, L), bool), om.ancestor_mask(parents)], axis=1)
+    return round_bf16(om.attention(qv, kv, vv, vis)), np.abs(vv).max()
+
+
+@pytest.mark.parametrize("n,hq,hkv,d,L", [(32, 40, 8, 128, 4096), (32, 32, 8, 128, 2048), (8, 8, 8, 64, 256),
+                                          (13, 6, 2, 64, 300), (1, 4, 4, 128, 0), (64, 4, 1, 64, 700),
+                                          (5, 10, 2, 128, 513)])
+def test_tree_attention_matches_oracle(tvp, cuda, n, hq, hkv, d, L):
+    print(f"[tree_attention] n={n} hq={hq} hkv={hkv} d={d} L={L}", flush=True)
+    parents, q, kc, vc = _attn_case(cuda, n, hq, hkv, d, L, seed=n + L)
+    out, st = tvp.tree_attention(q.to(cuda), kc.to(cuda), vc.to(cuda), L, torch.as_tensor(parents, device=cuda))
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    ref, vmax = _attn_ref(parents, q, kc, vc, L)
+    got = from_bits(_u16(out))
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * vmax + 2.0 ** -7 * np.abs(ref)), float(np.abs(got - ref).max())
+    out2, _ = tvp.tree_attention(q.to(cuda), kc.to(cuda), vc.to(cuda), L, torch.as_tensor(parents, device=cuda))
+    assert torch.equal(out, out2)
+
+
+def test_tree_attention_chain_equals_causal_and_star(tvp, cuda):
+    n, hq, hkv, d, L = 16, 8, 2, 128, 100
+    for parents in (np.arange(-1, n - 1, dtype=np.int32), np.array([-1] + [0] * (n - 1), dtype=np.int32)):
+        _, q, kc, vc = _attn_case(cuda, n, hq, hkv, d, L, seed=3, parents=parents)
+        out, st = tvp.tree_attention(q.to(cuda), kc.to(cuda), vc.to(cuda), L, torch.as_tensor(parents, device=cuda))
+        ref, vmax = _attn_ref(parents, q, kc, vc, L)
+        got = from_bits(_u16(out))
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * vmax + 2.0 ** -7 * np.abs(ref))
+
+
+def test_tree_attention_malformed_tree_status(tvp, cuda):
+    _, q, kc, vc = _attn_case(cuda, 4, 4, 4, 64, 10, seed=1, parents=np.array([-1, 0, 1, 2]))
+    bad = torch.as_tensor(np.array([-1, 0, 3, 1], dtype=np.int32), device=cuda)
+    out, st = tvp.tree_attention(q.to(cuda), kc.to(cuda), vc.to(cuda), 10, bad)
+    torch.cuda.synchronize()
+    assert int(st.item()) == tvp.TVP_ERR_TREE
+    assert torch.isfinite(out.float()).all()
+
+
+def test_accept_path_exact(tvp, cuda):
+    rng = np.random.default_rng(4)
+    print("[accept_path] random trees", flush=True)
+    for trial in range(200):
+        n = int(rng.integers(1, 100))
+        parents = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, n)], dtype=np.int32)
+        tokens = rng.integers(0, 3, n).astype(np.int32)
+        am = rng.integers(0, 3, n).astype(np.int32)
+        path, na, bonus, st = tvp.accept_path(torch.as_tensor(am, device=cuda), torch.as_tensor(tokens, device=cuda),
+                                              torch.as_tensor(parents, device=cuda))
+        p_ref, a_ref, b_ref = oaccept(am, tokens, parents)
+        a = int(na.item())
+        assert int(st.item()) == 0
+        assert a == a_ref and int(bonus.item()) == b_ref
+        assert path.cpu().numpy()[: a + 1].tolist() == p_ref
+    for bad in ([0, 0], [-1, 1], [-1, 0, 2]):
+        b = np.array(bad, dtype=np.int32)
+        path, na, bonus, st = tvp.accept_path(torch.as_tensor(b, device=cuda), torch.as_tensor(b, device=cuda),
+                                              torch.as_tensor(b, device=cuda))
+        assert int(st.item()) == tvp.TVP_ERR_TREE and int(na.item()) == 0
+
+
+def test_host_validation_launches_nothing(tvp, cuda):
+    pw = _packed(tvp, bf16_bits_numpy(gen_linear_bf16(make_generator(1), 64, 64, TINY_RECIPE)), cuda)
+    with pytest.raises(tvp.TvpError) as e:
+        tvp.w12_gemm(_x(200, 64, 1, cuda), pw)
+    assert e.value.status == tvp.TVP_ERR_SHAPE
+    with pytest.raises(tvp.TvpError) as e:
+        tvp.w12_gemm_ex(_x(4, 64, 1, cuda), pw, tvp.TvpGemmEpilogue(mode=99))
+    assert e.value.status == tvp.TVP_ERR_ARG
+    with pytest.raises(tvp.TvpError) as e:  # SwiGLU needs the gate/up channel map
+        y = torch.zeros(4, 64, dtype=torch.bfloat16, device=cuda)
+        tvp.w12_gemm_ex(_x(4, 64, 1, cuda), pw, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=y.data_ptr(), ldy=64))
+    assert e.value.status == tvp.TVP_ERR_ARG

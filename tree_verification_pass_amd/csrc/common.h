@@ -1,0 +1,67 @@
+// Shared device/host helpers of the tvp library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tvp.h"
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+#define TVP_CHECK_HIP(expr)                         \
+  do {                                              \
+    hipError_t e_ = (expr);                         \
+    if (e_ != hipSuccess) return TVP_ERR_HIP;       \
+  } while (0)
+
+#define TVP_LAUNCH_CHECK()                          \
+  do {                                              \
+    if (hipGetLastError() != hipSuccess) return TVP_ERR_HIP; \
+  } while (0)
+
+namespace tvp {
+
+constexpr int kTileN = 32;      // channels per packed tile
+constexpr int kBlockK = 64;     // k per packed block
+constexpr int kBlockBytes = 3072;  // 32 x 64 x 12 bits
+
+constexpr int kMaxReq = 64;      // requests per batched pass
+
+// Per-request bookkeeping passed by value to the batched kernels.
+struct ReqInfo {
+  int32_t n_req;
+  int32_t ctx_len[kMaxReq];
+  int32_t node_ptr[kMaxReq + 1];
+};
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// bf16 bits -> fp32 (exact)
+__device__ inline float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> quiet NaN with the sign kept.
+__device__ inline uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x0040u) & 0xFFFFu;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// 16-byte streaming load (non-temporal hint: the weight stream is read once).
+__device__ inline uint4 load_nt(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Order every LDS access of this wavefront issued before the call ahead of
+// those issued after it, without waiting on outstanding global loads.
+__device__ inline void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+}  // namespace tvp

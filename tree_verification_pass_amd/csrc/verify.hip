@@ -1,0 +1,431 @@
+// The verification pass: embedding gather, RMSNorm, the per-layer sequence of
+// fused W12 GEMMs and tree attention, the LM-head argmax, the acceptance walk
+// and the KV commit, for one request or a batch sharing one node budget.
+//
+// SpecPilot summary (onedev.kr): section 무엇인가 -- the target processes every
+// draft token in one forward pass and most of a step is spent reading the
+// target's weights; section 무엇과 다른가 -- the pass returns the matched path
+// plus a bonus token, and a batch can share one node budget across requests.
+// The KV commit is the dense-model counterpart of the page's commit kernel
+// (which replays the accepted path into recurrent layers): the accepted
+// nodes' keys and values are moved to the committed slots.
+#include <math.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "internal.h"
+
+namespace tvp {
+
+constexpr int kMaxLayers = 120;
+
+// ------------------------------------------------------------ small kernels
+
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
+                                                    const uint16_t* __restrict__ embed, int hidden,
+                                                    int vocab, uint16_t* __restrict__ h, int ldh,
+                                                    int32_t* __restrict__ bad) {
+  const int i = blockIdx.x;
+  const int32_t t = tokens[i];
+  const bool ok = t >= 0 && t < vocab;
+  if (threadIdx.x == 0) bad[i] = ok ? 0 : 1;
+  const uint16_t* src = embed + (int64_t)(ok ? t : 0) * hidden;
+  for (int k = threadIdx.x; k < hidden; k += 256) h[(int64_t)i * ldh + k] = src[k];
+}
+
+// y = bf16(x * (mean(x^2) + eps)^-1/2 * g), fp32 with a fixed reduction order.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x, int ldx,
+                                                      const uint16_t* __restrict__ g, int hidden,
+                                                      float eps, uint16_t* __restrict__ y, int ldy) {
+  __shared__ float ws[4];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* xr = x + (int64_t)i * ldx;
+  float ss = 0.0f;
+  for (int k = tid; k < hidden; k += 256) {
+    const float v = bf16_to_f32(xr[k]);
+    ss += v * v;
+  }
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((tid & 63) == 0) ws[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+  const float r = 1.0f / sqrtf(tot / (float)hidden + eps);
+  uint16_t* yr = y + (int64_t)i * ldy;
+  for (int k = tid; k < hidden; k += 256)
+    yr[k] = (uint16_t)f32_to_bf16(bf16_to_f32(xr[k]) * r * bf16_to_f32(g[k]));
+}
+
+// One workgroup per request; the walk is sequential over nodes (parents[i] < i).
+__global__ __launch_bounds__(64) void accept_kernel(const int32_t* __restrict__ argmax,
+                                                    const int32_t* __restrict__ tokens,
+                                                    const int32_t* __restrict__ parents, ReqInfo ri,
+                                                    const int32_t* __restrict__ bad_token,
+                                                    int32_t* __restrict__ path, int32_t* __restrict__ n_acc,
+                                                    int32_t* __restrict__ bonus, int32_t* __restrict__ status) {
+  __shared__ int32_t depth[1024];
+  __shared__ uint8_t okf[1024];
+  const int r = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  const int nb = ri.node_ptr[r], n = ri.node_ptr[r + 1] - nb;
+  bool valid = n >= 1 && n <= 1024 && parents[nb] == -1;
+  for (int i = 1; valid && i < n; ++i) {
+    const int p = parents[nb + i];
+    valid = p >= 0 && p < i;
+  }
+  int st = valid ? TVP_OK : TVP_ERR_TREE;
+  if (valid && bad_token) {
+    for (int i = 0; i < n; ++i)
+      if (bad_token[nb + i]) st = TVP_ERR_ARG;
+  }
+  if (st != TVP_OK) {
+    status[r] = st;
+    n_acc[r] = 0;
+    if (n >= 1) {
+      path[nb] = 0;
+      bonus[r] = argmax[nb];
+    } else {
+      bonus[r] = -1;
+    }
+    return;
+  }
+  depth[0] = 0;
+  okf[0] = 1;
+  int best = 0;
+  for (int i = 1; i < n; ++i) {
+    const int p = parents[nb + i];
+    depth[i] = depth[p] + 1;
+    okf[i] = okf[p] && tokens[nb + i] == argmax[nb + p];
+    if (okf[i] && depth[i] > depth[best]) best = i;
+  }
+  const int a = depth[best];
+  int v = best;
+  for (int j = a; j >= 0; --j) {
+    path[nb + j] = v;
+    v = j > 0 ? parents[nb + v] : 0;
+  }
+  n_acc[r] = a;
+  bonus[r] = argmax[nb + best];
+  status[r] = TVP_OK;
+}
+
+struct CacheTable {
+  int n_layers;
+  uint16_t* kc[kMaxLayers];
+  uint16_t* vc[kMaxLayers];
+};
+
+// Moves accepted rows: slot base + L + j <- slot base + L + path[j], j = 1..a,
+// for every layer, K and V, kv head.  Reads every source row of a kv head
+// before writing any (sources and destinations may overlap).
+__global__ __launch_bounds__(256) void kv_commit_kernel(CacheTable ct, ReqInfo ri, int32_t s_req,
+                                                        int64_t s_stride, int hkv, int d,
+                                                        const int32_t* __restrict__ path,
+                                                        const int32_t* __restrict__ n_acc,
+                                                        const int32_t* __restrict__ status) {
+  __shared__ uint16_t buf[64 * 128];
+  const int r = blockIdx.x;
+  const int layer = blockIdx.y >> 1, which = blockIdx.y & 1;
+  if (status[r] != TVP_OK) return;
+  const int a = n_acc[r];
+  if (a <= 0) return;
+  const int nb = ri.node_ptr[r];
+  const int64_t base = (int64_t)r * s_req + ri.ctx_len[r];
+  uint16_t* cache = which ? ct.vc[layer] : ct.kc[layer];
+  const int total = a * d;
+  for (int kh = 0; kh < hkv; ++kh) {
+    uint16_t* hc = cache + (int64_t)kh * s_stride * d;
+    for (int e = threadIdx.x; e < total; e += 256) {
+      const int j = 1 + e / d, dd = e % d;
+      buf[e] = hc[(base + path[nb + j]) * d + dd];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < total; e += 256) {
+      const int j = 1 + e / d, dd = e % d;
+      hc[(base + j) * d + dd] = buf[e];
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace tvp
+
+using namespace tvp;
+
+struct tvp_plan {
+  tvp_model_desc desc;
+  std::vector<tvp_layer> layers;
+  int32_t max_nodes;
+  int ld_h, ld_q, ld_u;
+  // workspace layout
+  size_t off_gcnt, off_gcnt2, off_acnt, zero_end;
+  size_t off_h, off_a, off_q, off_o, off_u;
+  size_t off_anc, off_pos, off_slot, off_tstat, off_bad;
+  size_t off_gscr, gscr_bytes;
+  size_t off_ascr, ascr_bytes;
+  size_t bytes;
+};
+
+static int check_packed(const tvp_w12_packed& w, int64_t n_out, int64_t k_in, int32_t map) {
+  if (!w.blob || w.n_out != n_out || w.k_in != k_in || w.chan_map != map) return TVP_ERR_FORMAT;
+  return TVP_OK;
+}
+
+extern "C" {
+
+int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) {
+  if (!d || !out || !d->layers || !d->embed || !d->final_norm) return TVP_ERR_ARG;
+  *out = nullptr;
+  if (d->n_layers < 1 || d->n_layers > kMaxLayers || d->hidden < 1 || d->n_heads < 1 || d->n_kv_heads < 1 ||
+      d->n_heads % d->n_kv_heads || (d->head_dim != 64 && d->head_dim != 128) || d->ffn < 1 || d->vocab < 1 ||
+      d->s_max < 1 || !(d->rope_theta > 0) || !(d->norm_eps >= 0))
+    return TVP_ERR_SHAPE;
+  if (d->hidden > 65536 || d->ffn > 65536 || d->n_heads * d->head_dim > 65536) return TVP_ERR_SHAPE;
+  if (max_nodes < 1 || max_nodes > 192) return TVP_ERR_CAPACITY;
+  const int hq = d->n_heads, hkv = d->n_kv_heads, hd = d->head_dim, H = d->hidden, F = d->ffn;
+  const int G = hq / hkv;
+  if (G * std::min(max_nodes, 64) > 256) return TVP_ERR_SHAPE;
+  int st = check_packed(d->lm_head, d->vocab, H, TVP_CHAN_PLAIN);
+  if (st) return st;
+  for (int l = 0; l < d->n_layers; ++l) {
+    const tvp_layer& L = d->layers[l];
+    if (!L.attn_norm || !L.ffn_norm || !L.k_cache || !L.v_cache) return TVP_ERR_ARG;
+    if ((st = check_packed(L.wqkv, (int64_t)(hq + 2 * hkv) * hd, H, TVP_CHAN_QKV))) return st;
+    if (L.wqkv.map_a != hq || L.wqkv.map_b != hkv || L.wqkv.map_c != hd) return TVP_ERR_FORMAT;
+    if ((st = check_packed(L.wo, H, (int64_t)hq * hd, TVP_CHAN_PLAIN))) return st;
+    if ((st = check_packed(L.wgu, 2LL * F, H, TVP_CHAN_GATEUP))) return st;
+    if (L.wgu.map_a != F) return TVP_ERR_FORMAT;
+    if ((st = check_packed(L.wdown, H, F, TVP_CHAN_PLAIN))) return st;
+    if (((uintptr_t)L.k_cache | (uintptr_t)L.v_cache) % 16) return TVP_ERR_ARG;
+  }
+  tvp_plan* p = new (std::nothrow) tvp_plan();
+  if (!p) return TVP_ERR_ARG;
+  p->desc = *d;
+  p->layers.assign(d->layers, d->layers + d->n_layers);
+  p->desc.layers = nullptr;
+  p->max_nodes = max_nodes;
+  p->ld_h = (int)align_up(H, 8);
+  p->ld_q = (int)align_up((size_t)hq * hd, 8);
+  p->ld_u = (int)align_up(F, 8);
+  // counters and scratch over every GEMM at every row count up to max_nodes
+  int gmax = 1;
+  size_t gscr = 256;
+  auto need = [&](const tvp_w12_packed& w) {
+    for (int m = 1; m <= max_nodes; ++m) {
+      int g;
+      size_t b;
+      gemm_requirements(m, &w, &g, &b);
+      gmax = std::max(gmax, g);
+      gscr = std::max(gscr, b);
+    }
+  };
+  need(d->lm_head);
+  for (int l = 0; l < d->n_layers; ++l) {
+    need(p->layers[l].wqkv);
+    need(p->layers[l].wo);
+    need(p->layers[l].wgu);
+    need(p->layers[l].wdown);
+  }
+  const int mn = max_nodes;
+  size_t off = 0;
+  p->off_gcnt = off;
+  off = align_up(off + (size_t)gmax * 4, 256);
+  p->off_gcnt2 = off;
+  off += 256;
+  p->off_acnt = off;
+  off = align_up(off + (size_t)kMaxReq * hkv * 4, 256);
+  p->zero_end = off;
+  p->off_h = off;
+  off = align_up(off + (size_t)mn * p->ld_h * 2, 256);
+  p->off_a = off;
+  off = align_up(off + (size_t)mn * p->ld_h * 2, 256);
+  p->off_q = off;
+  off = align_up(off + (size_t)mn * p->ld_q * 2, 256);
+  p->off_o = off;
+  off = align_up(off + (size_t)mn * p->ld_q * 2, 256);
+  p->off_u = off;
+  off = align_up(off + (size_t)mn * p->ld_u * 2, 256);
+  p->off_anc = off;
+  off = align_up(off + (size_t)mn * 8, 256);
+  p->off_pos = off;
+  off = align_up(off + (size_t)mn * 4, 256);
+  p->off_slot = off;
+  off = align_up(off + (size_t)mn * 4, 256);
+  p->off_tstat = off;
+  off = align_up(off + (size_t)kMaxReq * 4, 256);
+  p->off_bad = off;
+  off = align_up(off + (size_t)mn * 4, 256);
+  p->off_gscr = off;
+  p->gscr_bytes = gscr;
+  off = align_up(off + gscr, 256);
+  p->off_ascr = off;
+  p->ascr_bytes = attention_scratch_bytes(hkv, G, hd, G * std::min(mn, 64), mn, d->s_max);
+  off = align_up(off + p->ascr_bytes, 256);
+  p->bytes = off;
+  *out = p;
+  return TVP_OK;
+}
+
+void tvp_plan_destroy(tvp_plan* p) { delete p; }
+
+size_t verify_step_workspace(const tvp_plan* p) { return p ? p->bytes : 0; }
+
+}  // extern "C"
+
+// Runs the whole pass for the requests described by `ri`.
+static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t* tokens,
+                    const int32_t* parents, int32_t commit, const tvp_verify_out* out, void* ws,
+                    hipStream_t stream) {
+  const tvp_model_desc& d = p->desc;
+  const int hq = d.n_heads, hkv = d.n_kv_heads, hd = d.head_dim, H = d.hidden, F = d.ffn;
+  const int G = hq / hkv;
+  const int n_total = ri.node_ptr[ri.n_req];
+  int max_n = 0, max_keys = 0;
+  for (int r = 0; r < ri.n_req; ++r) {
+    const int n = ri.node_ptr[r + 1] - ri.node_ptr[r];
+    max_n = std::max(max_n, n);
+    max_keys = std::max(max_keys, ri.ctx_len[r] + n);
+  }
+  uint8_t* w = (uint8_t*)ws;
+  uint32_t* gcnt = (uint32_t*)(w + p->off_gcnt);
+  uint32_t* gcnt2 = (uint32_t*)(w + p->off_gcnt2);
+  uint32_t* acnt = (uint32_t*)(w + p->off_acnt);
+  uint16_t* h = (uint16_t*)(w + p->off_h);
+  uint16_t* a = (uint16_t*)(w + p->off_a);
+  uint16_t* q = (uint16_t*)(w + p->off_q);
+  uint16_t* o = (uint16_t*)(w + p->off_o);
+  uint16_t* u = (uint16_t*)(w + p->off_u);
+  uint64_t* anc = (uint64_t*)(w + p->off_anc);
+  int32_t* pos = (int32_t*)(w + p->off_pos);
+  int32_t* slot = (int32_t*)(w + p->off_slot);
+  int32_t* tstat = (int32_t*)(w + p->off_tstat);
+  int32_t* bad = (int32_t*)(w + p->off_bad);
+  void* gscr = w + p->off_gscr;
+  void* ascr = w + p->off_ascr;
+  int st;
+
+  if ((st = launch_tree_prep(parents, ri, s_req, anc, pos, slot, tstat, stream))) return st;
+  embed_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(tokens, d.embed, H, d.vocab, h, p->ld_h, bad);
+  TVP_LAUNCH_CHECK();
+  for (int l = 0; l < d.n_layers; ++l) {
+    const tvp_layer& L = p->layers[l];
+    rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, L.attn_norm, H, d.norm_eps, a, p->ld_h);
+    TVP_LAUNCH_CHECK();
+    tvp_gemm_epilogue e{};
+    e.mode = TVP_EPI_QKV;
+    e.y = q;
+    e.ldy = p->ld_q;
+    e.pos = pos;
+    e.slot = slot;
+    e.k_cache = L.k_cache;
+    e.v_cache = L.v_cache;
+    e.s_stride = d.s_max;
+    e.rope_theta = d.rope_theta;
+    if ((st = gemm_run(a, n_total, p->ld_h, &L.wqkv, &e, gcnt, gcnt2, gscr, p->gscr_bytes, stream))) return st;
+    if ((st = launch_tree_attention(q, L.k_cache, L.v_cache, d.s_max, ri, s_req, anc, hq, hkv, hd, G * max_n,
+                                    max_keys, o, acnt, ascr, p->ascr_bytes, stream)))
+      return st;
+    e = tvp_gemm_epilogue{};
+    e.mode = TVP_EPI_RESID;
+    e.y = h;
+    e.ldy = p->ld_h;
+    e.resid = h;
+    e.ldr = p->ld_h;
+    if ((st = gemm_run(o, n_total, p->ld_q, &L.wo, &e, gcnt, gcnt2, gscr, p->gscr_bytes, stream))) return st;
+    rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, L.ffn_norm, H, d.norm_eps, a, p->ld_h);
+    TVP_LAUNCH_CHECK();
+    e = tvp_gemm_epilogue{};
+    e.mode = TVP_EPI_SWIGLU;
+    e.y = u;
+    e.ldy = p->ld_u;
+    if ((st = gemm_run(a, n_total, p->ld_h, &L.wgu, &e, gcnt, gcnt2, gscr, p->gscr_bytes, stream))) return st;
+    e = tvp_gemm_epilogue{};
+    e.mode = TVP_EPI_RESID;
+    e.y = h;
+    e.ldy = p->ld_h;
+    e.resid = h;
+    e.ldr = p->ld_h;
+    if ((st = gemm_run(u, n_total, p->ld_u, &L.wdown, &e, gcnt, gcnt2, gscr, p->gscr_bytes, stream))) return st;
+  }
+  rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, d.final_norm, H, d.norm_eps, a, p->ld_h);
+  TVP_LAUNCH_CHECK();
+  tvp_gemm_epilogue e{};
+  e.mode = TVP_EPI_ARGMAX;
+  e.argmax = out->argmax;
+  e.logits = out->logits;
+  e.ldl = d.vocab;
+  if ((st = gemm_run(a, n_total, p->ld_h, &d.lm_head, &e, gcnt, gcnt2, gscr, p->gscr_bytes, stream))) return st;
+  accept_kernel<<<dim3(ri.n_req), dim3(64), 0, stream>>>(out->argmax, tokens, parents, ri, bad, out->path,
+                                                         out->n_accepted, out->bonus, out->status);
+  TVP_LAUNCH_CHECK();
+  if (commit) {
+    CacheTable ct{};
+    ct.n_layers = d.n_layers;
+    for (int l = 0; l < d.n_layers; ++l) {
+      ct.kc[l] = p->layers[l].k_cache;
+      ct.vc[l] = p->layers[l].v_cache;
+    }
+    kv_commit_kernel<<<dim3(ri.n_req, 2 * d.n_layers), dim3(256), 0, stream>>>(
+        ct, ri, s_req, d.s_max, hkv, hd, out->path, out->n_accepted, out->status);
+    TVP_LAUNCH_CHECK();
+  }
+  (void)tstat;
+  return TVP_OK;
+}
+
+extern "C" {
+
+int verify_step(tvp_plan* p, int32_t ctx_len, const int32_t* tokens, const int32_t* parents, int32_t n,
+                int32_t commit, const tvp_verify_out* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!p || !tokens || !parents || !out) return TVP_ERR_ARG;
+  if (!out->argmax || !out->path || !out->n_accepted || !out->bonus || !out->status) return TVP_ERR_ARG;
+  if (n < 1 || ctx_len < 0) return TVP_ERR_SHAPE;
+  if (n > p->max_nodes || n > 64) return TVP_ERR_CAPACITY;
+  if ((int64_t)ctx_len + n > p->desc.s_max) return TVP_ERR_CAPACITY;
+  if (!ws || ws_bytes < p->bytes) return TVP_ERR_WORKSPACE;
+  ReqInfo ri{};
+  ri.n_req = 1;
+  ri.ctx_len[0] = ctx_len;
+  ri.node_ptr[0] = 0;
+  ri.node_ptr[1] = n;
+  return run_pass(p, ri, 0, tokens, parents, commit, out, ws, stream);
+}
+
+int verify_step_batched(tvp_plan* p, int32_t n_req, const int32_t* ctx_len, const int32_t* node_ptr,
+                        int32_t s_req, const int32_t* tokens, const int32_t* parents, int32_t commit,
+                        const tvp_verify_out* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!p || !ctx_len || !node_ptr || !tokens || !parents || !out) return TVP_ERR_ARG;
+  if (!out->argmax || !out->path || !out->n_accepted || !out->bonus || !out->status) return TVP_ERR_ARG;
+  if (n_req < 1 || n_req > kMaxReq || s_req < 1) return TVP_ERR_SHAPE;
+  if ((int64_t)n_req * s_req > p->desc.s_max) return TVP_ERR_CAPACITY;
+  if (node_ptr[0] != 0) return TVP_ERR_SHAPE;
+  ReqInfo ri{};
+  ri.n_req = n_req;
+  for (int r = 0; r < n_req; ++r) {
+    const int n = node_ptr[r + 1] - node_ptr[r];
+    if (n < 1 || ctx_len[r] < 0) return TVP_ERR_SHAPE;
+    if (n > 64 || (int64_t)ctx_len[r] + n > s_req) return TVP_ERR_CAPACITY;
+    ri.ctx_len[r] = ctx_len[r];
+    ri.node_ptr[r] = node_ptr[r];
+  }
+  ri.node_ptr[n_req] = node_ptr[n_req];
+  if (node_ptr[n_req] > p->max_nodes) return TVP_ERR_CAPACITY;
+  if (!ws || ws_bytes < p->bytes) return TVP_ERR_WORKSPACE;
+  return run_pass(p, ri, s_req, tokens, parents, commit, out, ws, stream);
+}
+
+int accept_path(const int32_t* argmax, const int32_t* tokens, const int32_t* parents, int32_t n,
+                int32_t* path, int32_t* n_accepted, int32_t* bonus, int32_t* status, hipStream_t stream) {
+  if (!argmax || !tokens || !parents || !path || !n_accepted || !bonus || !status) return TVP_ERR_ARG;
+  if (n < 1 || n > 1024) return TVP_ERR_SHAPE;
+  ReqInfo ri{};
+  ri.n_req = 1;
+  ri.node_ptr[0] = 0;
+  ri.node_ptr[1] = n;
+  accept_kernel<<<dim3(1), dim3(64), 0, stream>>>(argmax, tokens, parents, ri, nullptr, path, n_accepted, bonus,
+                                                  status);
+  TVP_LAUNCH_CHECK();
+  return TVP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,619 @@
+// Skinny W12 GEMM for gfx950: Y[m][n] = X[m][k] . W[n][k]^T, W streamed as
+// 12-bit records and decoded in registers (SpecPilot summary, section
+// 무엇과 다른가: the GEMM decodes records in registers so the decode hides
+// behind the weight stream; stream-K keeps it deterministic).
+//
+// MI355X design (not the page's Hopper kernel):
+//  * Each wavefront streams whole packed tile blocks (32 channels x 64 k =
+//    3072 B, lane-contiguous 16-byte loads), one or two tiles at a time, with
+//    the next step's records and escape entries prefetched while the current
+//    step is decoded and multiplied.
+//  * Decode: 4 VALU ops per pair of weights (rotate, mask, byte spread, add)
+//    into bf16 halfwords; the decoded 32x64 tile goes through the wave's LDS
+//    scratch so escape values (about 1% of weights) are patched with one
+//    16-bit LDS store each, then the fragments feed v_mfma_f32_32x32x16_bf16
+//    (m > 16) or v_mfma_f32_16x16x32_bf16 (m <= 16).
+//  * X is staged through LDS in chunks of the workgroup's K range and shared
+//    by the 4 wavefronts (4 or 8 tiles), so activation traffic is a small
+//    fraction of the weight stream.
+//  * Split-K over workgroups; fp32 partials go to a workspace and the last
+//    workgroup of each tile group (atomic counter) reduces them in split order
+//    and applies the epilogue: results are bitwise reproducible.
+#include <math.h>
+
+#include "internal.h"
+
+namespace tvp {
+
+struct GemmArgs {
+  const uint16_t* x;
+  int64_t ldx;
+  int m, k_in;
+  const uint8_t* rec;
+  const uint32_t* escoff;
+  const uint32_t* esc;
+  const uint32_t* b2;
+  const int32_t* rowmap;
+  int n_tiles, n_kb, n_pad;
+  int groups, splits, kbs;
+  float* part;
+  uint32_t* cnt;
+  uint32_t* cnt2;
+  float* amax_v;
+  int32_t* amax_i;
+  int mode;
+  void* y;
+  int64_t ldy;
+  const uint16_t* resid;
+  int64_t ldr;
+  const int32_t* pos;
+  const int32_t* slot;
+  uint16_t* kc;
+  uint16_t* vc;
+  int64_t s_stride;
+  double theta;
+  int hq, hkv, d;
+  int32_t* argmax;
+  float* logits;
+  int64_t ldl;
+};
+
+__device__ inline uint32_t rotl32(uint32_t x, int r) { return r == 0 ? x : (x << r) | (x >> (32 - r)); }
+
+// 12 record dwords of one lane -> 16 bf16-pair dwords (K-step s = o[4s..4s+3]).
+__device__ inline void decode_block(const uint4 (&r)[3], uint32_t b2, uint32_t (&o)[16]) {
+  const uint32_t lb[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+  const uint32_t hn[4] = {r[2].x, r[2].y, r[2].z, r[2].w};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t L = lb[2 * s + q];
+      o[4 * s + 2 * q] = (rotl32(hn[s], 8 * q) & 0x87008700u) + (L & 0x00FF00FFu) + b2;
+      o[4 * s + 2 * q + 1] = (rotl32(hn[s], 8 * q + 4) & 0x87008700u) + ((L >> 8) & 0x00FF00FFu) + b2;
+    }
+  }
+}
+
+__device__ inline bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ inline float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+template <int ROWS>
+struct XChunk {
+  static constexpr int CB = ROWS <= 16 ? 8 : (ROWS <= 32 ? 4 : 2);  // blocks per X chunk
+};
+
+template <int MT, int RB, int TPW>
+__global__ __launch_bounds__(256) void w12_gemm_kernel(GemmArgs a) {
+  constexpr int ROWS = MT * RB;
+  constexpr int CB = XChunk<ROWS>::CB;
+  constexpr int TG = 4 * TPW;
+  constexpr int KG = CB * 8;  // 16-byte k groups per X chunk
+  __shared__ uint4 xs[KG * ROWS];
+  __shared__ uint4 scr[4][2][256];
+  __shared__ uint32_t s_last;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
+  const int kb0 = sp * a.kbs;
+  const int kb1 = min(a.n_kb, kb0 + a.kbs);
+  const int nblk = kb1 > kb0 ? kb1 - kb0 : 0;
+  const int tw = g * TG + wave * TPW;
+  const int nsteps = TPW == 2 ? nblk : (nblk + 1) / 2;
+
+  constexpr int NACC = MT == 32 ? 16 : 4;
+  constexpr int NCH = MT == 32 ? 1 : 2;
+  typedef float accv __attribute__((ext_vector_type(NACC)));
+  accv acc[TPW][RB][NCH];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+        for (int v = 0; v < NACC; ++v) acc[t][rb][ch][v] = 0.0f;
+
+  uint32_t b2v[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) b2v[t] = (tw + t < a.n_tiles) ? a.b2[(tw + t) * 32 + (lane & 31)] : 0u;
+
+  auto unit_tile = [&](int u) { return TPW == 2 ? tw + u : tw; };
+  auto unit_blk = [&](int st, int u) { return TPW == 2 ? kb0 + st : kb0 + 2 * st + u; };
+  auto unit_ok = [&](int st, int u) { return unit_tile(u) < a.n_tiles && unit_blk(st, u) < kb1; };
+
+  uint4 R[2][3], Rn[2][3];
+  uint32_t E[2], En[2];
+  uint32_t eo[2], ec[2], eon[2], ecn[2];
+
+  auto load_escoff = [&](int st, uint32_t (&o)[2], uint32_t (&c)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      o[u] = 0;
+      c[u] = 0;
+      if (st < nsteps && unit_ok(st, u)) {
+        const int64_t un = (int64_t)unit_tile(u) * a.n_kb + unit_blk(st, u);
+        o[u] = a.escoff[un];
+        c[u] = a.escoff[un + 1] - o[u];
+      }
+    }
+  };
+  auto load_recs = [&](int st, const uint32_t (&o)[2], const uint32_t (&c)[2], uint4 (&r)[2][3],
+                       uint32_t (&e)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      e[u] = 0;
+      if (st < nsteps && unit_ok(st, u)) {
+        const int64_t un = (int64_t)unit_tile(u) * a.n_kb + unit_blk(st, u);
+        const uint4* blk = (const uint4*)(a.rec + un * kBlockBytes);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) r[u][i] = load_nt(blk + i * 64 + lane);
+        if ((uint32_t)lane < c[u]) e[u] = a.esc[o[u] + lane];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) r[u][i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  load_escoff(0, eo, ec);
+  load_recs(0, eo, ec, R, E);
+  load_escoff(1, eon, ecn);
+
+  for (int st = 0; st < nsteps; ++st) {
+    // prefetch the next step
+    load_recs(st + 1, eon, ecn, Rn, En);
+    uint32_t eonn[2], ecnn[2];
+    load_escoff(st + 2, eonn, ecnn);
+
+    const int blk_first = unit_blk(st, 0);
+    const int jj = (blk_first - kb0) % CB;  // block index inside the X chunk
+    if (jj == 0) {
+      __syncthreads();
+      const int64_t k0 = (int64_t)blk_first * kBlockK;
+      for (int idx = tid; idx < KG * ROWS; idx += 256) {
+        const int row = idx / KG, kg = idx % KG;
+        const int64_t k = k0 + 8 * kg;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < a.m) {
+          const uint16_t* src = a.x + (int64_t)row * a.ldx + k;
+          if (k + 8 <= a.k_in) {
+            v = *(const uint4*)src;
+          } else if (k < a.k_in) {
+            uint32_t h[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) h[i] = (k + i < a.k_in) ? src[i] : 0u;
+            v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+          }
+        }
+        xs[kg * ROWS + row] = v;
+      }
+      __syncthreads();
+    }
+
+    // decode into LDS, then patch escapes
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (unit_ok(st, u)) {
+        uint32_t o[16];
+        decode_block(R[u], b2v[TPW == 2 ? u : 0], o);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          scr[wave][u][64 * s + lane] = make_uint4(o[4 * s], o[4 * s + 1], o[4 * s + 2], o[4 * s + 3]);
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (unit_ok(st, u) && ec[u] > 0) {
+        uint16_t* sh = (uint16_t*)&scr[wave][u][0];
+        if ((uint32_t)lane < ec[u]) sh[E[u] & 0x7FFu] = (uint16_t)(E[u] >> 16);
+        for (uint32_t e = 64 + lane; e < ec[u]; e += 64) {
+          const uint32_t ent = a.esc[eo[u] + e];
+          sh[ent & 0x7FFu] = (uint16_t)(ent >> 16);
+        }
+      }
+    }
+    wave_lds_sync();
+
+    // MFMA over the step's units
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (unit_ok(st, u)) {
+        const int ti = TPW == 2 ? u : 0;
+        const int jb = TPW == 2 ? jj : jj + u;
+        if constexpr (MT == 32) {
+          const int h = lane >> 5;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8_t B = as_bf16x8(scr[wave][u][64 * ks + lane]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+              const bf16x8_t A = as_bf16x8(xs[(jb * 8 + 2 * ks + h) * ROWS + rb * 32 + (lane & 31)]);
+              acc[ti][rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[ti][rb][0], 0, 0, 0);
+            }
+          }
+        } else {
+          const int q = lane >> 4;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+              const bf16x8_t B = as_bf16x8(scr[wave][u][(4 * ks + q) * 32 + 16 * ch + (lane & 15)]);
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb) {
+                const bf16x8_t A = as_bf16x8(xs[(jb * 8 + 4 * ks + q) * ROWS + rb * 16 + (lane & 15)]);
+                acc[ti][rb][ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[ti][rb][ch], 0, 0, 0);
+              }
+            }
+          }
+        }
+      }
+    }
+    wave_lds_sync();
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      E[u] = En[u];
+      eo[u] = eon[u];
+      ec[u] = ecn[u];
+      eon[u] = eonn[u];
+      ecn[u] = ecnn[u];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) R[u][i] = Rn[u][i];
+    }
+  }
+
+  // partial sums of this split
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    if (tw + t >= a.n_tiles) continue;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+        for (int v = 0; v < NACC; ++v) {
+          int row, col;
+          if constexpr (MT == 32) {
+            row = rb * 32 + (v >> 2) * 8 + 4 * (lane >> 5) + (v & 3);
+            col = (tw + t) * 32 + (lane & 31);
+          } else {
+            row = rb * 16 + 4 * (lane >> 4) + v;
+            col = (tw + t) * 32 + 16 * ch + (lane & 15);
+          }
+          if (row < a.m) a.part[((int64_t)sp * a.m + row) * a.n_pad + col] = acc[t][rb][ch][v];
+        }
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = atomicAdd(&a.cnt[g], 1u);
+    s_last = (old == (uint32_t)a.splits - 1u) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (tid == 0) a.cnt[g] = 0u;
+
+  // ---------------------------------------------- reduction + epilogue
+  const int c0 = g * TG * 32;
+  const int c1 = min(a.n_pad, c0 + TG * 32);
+  const int nc = c1 - c0;
+  const int M = a.m;
+  auto red = [&](int row, int col) {
+    float v = 0.0f;
+    for (int s = 0; s < a.splits; ++s) v += a.part[((int64_t)s * M + row) * a.n_pad + col];
+    return v;
+  };
+
+  if (a.mode == TVP_EPI_F32 || a.mode == TVP_EPI_BF16 || a.mode == TVP_EPI_RESID) {
+    for (int idx = tid; idx < M * nc; idx += 256) {
+      const int row = idx / nc, col = c0 + idx % nc;
+      const int32_t r = a.rowmap[col];
+      if (r < 0) continue;
+      const float v = red(row, col);
+      if (a.mode == TVP_EPI_F32) {
+        ((float*)a.y)[row * a.ldy + r] = v;
+      } else if (a.mode == TVP_EPI_BF16) {
+        ((uint16_t*)a.y)[row * a.ldy + r] = (uint16_t)f32_to_bf16(v);
+      } else {
+        const float rv = bf16_to_f32(a.resid[row * a.ldr + r]);
+        ((uint16_t*)a.y)[row * a.ldy + r] = (uint16_t)f32_to_bf16(rv + v);
+      }
+    }
+  } else if (a.mode == TVP_EPI_SWIGLU) {
+    const int half = nc / 2;  // nc is a multiple of 32
+    for (int idx = tid; idx < M * half; idx += 256) {
+      const int row = idx / half, p = idx % half;
+      const int col = c0 + (p / 16) * 32 + (p % 16);
+      const int32_t r = a.rowmap[col];
+      if (r < 0) continue;
+      const float gv = red(row, col), uv = red(row, col + 16);
+      ((uint16_t*)a.y)[row * a.ldy + r] = (uint16_t)f32_to_bf16(silu_f32(gv) * uv);
+    }
+  } else if (a.mode == TVP_EPI_QKV) {
+    const int d = a.d, tph = d / 32;
+    const int rot_tiles = (a.hq + a.hkv) * tph;
+    for (int idx = tid; idx < M * nc; idx += 256) {
+      const int row = idx / nc, cc = idx % nc;
+      const int col = c0 + cc;
+      const int t = col / 32, c = col % 32;
+      if (t >= a.n_tiles) continue;
+      if (t < rot_tiles) {
+        if (c >= 16) continue;
+        const int head = t / tph, u = t % tph;
+        const int da = 16 * u + c, db = d / 2 + 16 * u + c;
+        const float xa = red(row, col), xb = red(row, col + 16);
+        const double ang = (double)a.pos[row] * pow(a.theta, -2.0 * (double)da / (double)d);
+        const float cs = (float)cos(ang), sn = (float)sin(ang);
+        const float oa = xa * cs - xb * sn, ob = xb * cs + xa * sn;
+        if (head < a.hq) {
+          uint16_t* q = (uint16_t*)a.y + (int64_t)row * a.ldy + (int64_t)head * d;
+          q[da] = (uint16_t)f32_to_bf16(oa);
+          q[db] = (uint16_t)f32_to_bf16(ob);
+        } else {
+          uint16_t* kr = a.kc + ((int64_t)(head - a.hq) * a.s_stride + a.slot[row]) * d;
+          kr[da] = (uint16_t)f32_to_bf16(oa);
+          kr[db] = (uint16_t)f32_to_bf16(ob);
+        }
+      } else {
+        const int vr = (t - rot_tiles) * 32 + c;
+        if (vr >= a.hkv * d) continue;
+        const int kh = vr / d, dim = vr % d;
+        a.vc[((int64_t)kh * a.s_stride + a.slot[row]) * d + dim] = (uint16_t)f32_to_bf16(red(row, col));
+      }
+    }
+  } else if (a.mode == TVP_EPI_ARGMAX) {
+    __shared__ float bv[4];
+    __shared__ int32_t bi[4];
+    for (int row = 0; row < M; ++row) {
+      float best = -INFINITY;
+      int32_t besti = 0x7FFFFFFF;
+      for (int cc = tid; cc < nc; cc += 256) {
+        const int col = c0 + cc;
+        const int32_t r = a.rowmap[col];
+        if (r < 0) continue;
+        const float v = red(row, col);
+        if (a.logits) a.logits[row * a.ldl + r] = v;
+        if (v > best || (v == best && r < besti)) { best = v; besti = r; }
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(best, off);
+        const int32_t oi = __shfl_xor(besti, off);
+        if (ov > best || (ov == best && oi < besti)) { best = ov; besti = oi; }
+      }
+      if (lane == 0) { bv[wave] = best; bi[wave] = besti; }
+      __syncthreads();
+      if (tid == 0) {
+        for (int w = 1; w < 4; ++w)
+          if (bv[w] > best || (bv[w] == best && bi[w] < besti)) { best = bv[w]; besti = bi[w]; }
+        a.amax_v[(int64_t)g * M + row] = best;
+        a.amax_i[(int64_t)g * M + row] = besti;
+      }
+      __syncthreads();
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t old = atomicAdd(a.cnt2, 1u);
+      s_last = (old == (uint32_t)a.groups - 1u) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (tid == 0) *a.cnt2 = 0u;
+    for (int row = wave; row < M; row += 4) {
+      float best = -INFINITY;
+      int32_t besti = 0x7FFFFFFF;
+      for (int gg = lane; gg < a.groups; gg += 64) {
+        const float v = a.amax_v[(int64_t)gg * M + row];
+        const int32_t i = a.amax_i[(int64_t)gg * M + row];
+        if (v > best || (v == best && i < besti)) { best = v; besti = i; }
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(best, off);
+        const int32_t oi = __shfl_xor(besti, off);
+        if (ov > best || (ov == best && oi < besti)) { best = ov; besti = oi; }
+      }
+      if (lane == 0) a.argmax[row] = besti;
+    }
+  }
+}
+
+struct GemmPlan {
+  int MT, RB, TPW, TG, groups, splits, kbs;
+  size_t off_av, off_ai, off_part, scratch_bytes;
+};
+
+static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w) {
+  GemmPlan p{};
+  p.MT = m <= 16 ? 16 : 32;
+  p.RB = (int)ceil_div(m, p.MT);
+  p.TPW = (p.RB == 1 && w->n_tiles >= 768) ? 2 : 1;
+  p.TG = 4 * p.TPW;
+  p.groups = (int)ceil_div(w->n_tiles, p.TG);
+  const int target = 1024;  // workgroups per launch, about 4 per CU
+  int s = (int)((target + p.groups / 2) / p.groups);
+  s = s < 1 ? 1 : s;
+  const int smax = (int)ceil_div(w->n_kb, 2);
+  if (s > smax) s = smax < 1 ? 1 : smax;
+  int kbs = (int)ceil_div(w->n_kb, s);
+  kbs += kbs & 1;
+  p.kbs = kbs;
+  p.splits = kbs > 0 ? (int)ceil_div(w->n_kb, kbs) : 1;
+  if (p.splits < 1) p.splits = 1;
+  const int64_t n_pad = (int64_t)w->n_tiles * 32;
+  size_t off = 0;
+  p.off_av = off;
+  off = align_up(off + (size_t)p.groups * m * 4, 256);
+  p.off_ai = off;
+  off = align_up(off + (size_t)p.groups * m * 4, 256);
+  p.off_part = off;
+  off = align_up(off + (size_t)p.splits * m * n_pad * 4, 256);
+  p.scratch_bytes = off;
+  return p;
+}
+
+template <int MT, int RB, int TPW>
+static void launch(const GemmArgs& a, hipStream_t stream) {
+  w12_gemm_kernel<MT, RB, TPW><<<dim3((unsigned)(a.groups * a.splits)), dim3(256), 0, stream>>>(a);
+}
+
+static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+  if (p.MT == 16) {
+    if (p.TPW == 2) launch<16, 1, 2>(a, stream);
+    else launch<16, 1, 1>(a, stream);
+  } else {
+    switch (p.RB) {
+      case 1:
+        if (p.TPW == 2) launch<32, 1, 2>(a, stream);
+        else launch<32, 1, 1>(a, stream);
+        break;
+      case 2: launch<32, 2, 1>(a, stream); break;
+      case 3: launch<32, 3, 1>(a, stream); break;
+      case 4: launch<32, 4, 1>(a, stream); break;
+      case 5: launch<32, 5, 1>(a, stream); break;
+      case 6: launch<32, 6, 1>(a, stream); break;
+      default: return TVP_ERR_SHAPE;
+    }
+  }
+  TVP_LAUNCH_CHECK();
+  return TVP_OK;
+}
+
+void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes) {
+  const GemmPlan p = make_plan(m, w);
+  *groups = p.groups;
+  *scratch_bytes = p.scratch_bytes;
+}
+
+int gemm_run(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
+             const tvp_gemm_epilogue* epi, uint32_t* cnt, uint32_t* cnt2, void* scratch,
+             size_t scratch_bytes, hipStream_t stream) {
+  if (!w || !epi || !w->blob || !cnt || !cnt2) return TVP_ERR_ARG;
+  if (m < 1 || m > 192) return TVP_ERR_SHAPE;
+  if (w->k_in > 0 && (!x || ldx < w->k_in)) return TVP_ERR_ARG;
+  if (w->k_in > 0 && (((uintptr_t)x) % 16 != 0 || ldx % 8 != 0)) return TVP_ERR_ARG;
+  const GemmPlan p = make_plan(m, w);
+  if (!scratch || scratch_bytes < p.scratch_bytes) return TVP_ERR_WORKSPACE;
+  GemmArgs a{};
+  const uint8_t* blob = (const uint8_t*)w->blob;
+  a.x = x;
+  a.ldx = ldx;
+  a.m = (int)m;
+  a.k_in = (int)w->k_in;
+  a.rec = blob + w->off_rec;
+  a.escoff = (const uint32_t*)(blob + w->off_escoff);
+  a.esc = (const uint32_t*)(blob + w->off_esc);
+  a.b2 = (const uint32_t*)(blob + w->off_b2);
+  a.rowmap = (const int32_t*)(blob + w->off_rowmap);
+  a.n_tiles = w->n_tiles;
+  a.n_kb = w->n_kb;
+  a.n_pad = w->n_tiles * 32;
+  a.groups = p.groups;
+  a.splits = p.splits;
+  a.kbs = p.kbs;
+  uint8_t* sb = (uint8_t*)scratch;
+  a.cnt = cnt;
+  a.cnt2 = cnt2;
+  a.amax_v = (float*)(sb + p.off_av);
+  a.amax_i = (int32_t*)(sb + p.off_ai);
+  a.part = (float*)(sb + p.off_part);
+  a.mode = epi->mode;
+  a.y = epi->y;
+  a.ldy = epi->ldy;
+  a.resid = epi->resid;
+  a.ldr = epi->ldr;
+  a.pos = epi->pos;
+  a.slot = epi->slot;
+  a.kc = epi->k_cache;
+  a.vc = epi->v_cache;
+  a.s_stride = epi->s_stride;
+  a.theta = epi->rope_theta;
+  a.argmax = epi->argmax;
+  a.logits = epi->logits;
+  a.ldl = epi->ldl;
+  switch (epi->mode) {
+    case TVP_EPI_F32:
+    case TVP_EPI_BF16:
+      if (!epi->y || epi->ldy < w->n_out) return TVP_ERR_ARG;
+      break;
+    case TVP_EPI_RESID:
+      if (!epi->y || !epi->resid || epi->ldy < w->n_out || epi->ldr < w->n_out) return TVP_ERR_ARG;
+      break;
+    case TVP_EPI_SWIGLU:
+      if (w->chan_map != TVP_CHAN_GATEUP) return TVP_ERR_ARG;
+      if (!epi->y || epi->ldy < w->map_a) return TVP_ERR_ARG;
+      break;
+    case TVP_EPI_QKV:
+      if (w->chan_map != TVP_CHAN_QKV) return TVP_ERR_ARG;
+      if (!epi->y || !epi->pos || !epi->slot || !epi->k_cache || !epi->v_cache) return TVP_ERR_ARG;
+      if (epi->ldy < (int64_t)w->map_a * w->map_c || epi->s_stride < 1 || !(epi->rope_theta > 0))
+        return TVP_ERR_ARG;
+      a.hq = w->map_a;
+      a.hkv = w->map_b;
+      a.d = w->map_c;
+      break;
+    case TVP_EPI_ARGMAX:
+      if (!epi->argmax) return TVP_ERR_ARG;
+      if (epi->logits && epi->ldl < w->n_out) return TVP_ERR_ARG;
+      break;
+    default:
+      return TVP_ERR_ARG;
+  }
+  return dispatch(p, a, stream);
+}
+
+}  // namespace tvp
+
+using namespace tvp;
+
+// Standalone GEMM workspace: a fixed counter region (so that calls on tensors
+// of different shapes sharing one workspace never see another call's scratch
+// where their counters live), then the scratch for partial sums.
+constexpr size_t kGemmMaxGroups = 65536;
+constexpr size_t kGemmCntBytes = kGemmMaxGroups * 4;
+
+static size_t gemm_ws_layout(int64_t m, const tvp_w12_packed* w, size_t* off_cnt2, size_t* off_scr,
+                             size_t* scr_bytes, int* groups) {
+  gemm_requirements(m, w, groups, scr_bytes);
+  *off_cnt2 = kGemmCntBytes;
+  *off_scr = kGemmCntBytes + 256;
+  return *off_scr + *scr_bytes;
+}
+
+extern "C" {
+
+size_t w12_gemm_workspace(int64_t m, const tvp_w12_packed* w) {
+  if (!w || m < 1 || m > 192) return 0;
+  size_t a, b, c;
+  int g;
+  return gemm_ws_layout(m, w, &a, &b, &c, &g);
+}
+
+int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
+                const tvp_gemm_epilogue* epi, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!w || !epi) return TVP_ERR_ARG;
+  if (m < 1 || m > 192) return TVP_ERR_SHAPE;
+  size_t off_cnt2, off_scr, scr_bytes;
+  int groups;
+  const size_t need = gemm_ws_layout(m, w, &off_cnt2, &off_scr, &scr_bytes, &groups);
+  if ((size_t)groups > kGemmMaxGroups) return TVP_ERR_SHAPE;
+  if (!ws || ws_bytes < need) return TVP_ERR_WORKSPACE;
+  uint8_t* b = (uint8_t*)ws;
+  return gemm_run(x, m, ldx, w, epi, (uint32_t*)b, (uint32_t*)(b + off_cnt2), b + off_scr, scr_bytes,
+                  stream);
+}
+
+int w12_gemm(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w, void* y,
+             int64_t ldy, int y_fp32, void* ws, size_t ws_bytes, hipStream_t stream) {
+  tvp_gemm_epilogue e{};
+  e.mode = y_fp32 ? TVP_EPI_F32 : TVP_EPI_BF16;
+  e.y = y;
+  e.ldy = ldy;
+  return w12_gemm_ex(x, m, ldx, w, &e, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
