@@ -256,7 +256,7 @@ def main() -> int:
                    "ffn": cfg.ffn, "vocab": cfg.vocab, "nodes": cfg.n_nodes, "ctx_len": cfg.ctx_len,
                    "weights": "W12 (random-init bf16, per-channel sigma log-uniform [0.005,0.05], 1% zeros, "
                               "0.05% outliers x1000)", "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "w12_gemm_kernel (fused gate/up + SwiGLU, 34816x5120)", "bound": "hbm",
+        "roofline": {"kernel": "w12_skinny_kernel<32,2,2,SWIGLU> (fused gate/up, 34816x5120)", "bound": "hbm",
                      "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "us_per_launch": round(g_ms * 1000.0, 2), "bytes_per_launch": int(g_bytes)},

@@ -1,13 +1,20 @@
-"""An independent fp32 evaluation of the oracle's definition (torch CPU library
-routines, bf16 rounding at the same points), with a seeded permutation of every
-matmul's summation order.
+"""Rounding-noise envelope of the verification pass.
 
-It is used to measure the rounding noise that *any* fp32-accumulating
-implementation of the definition has against the fp64 oracle: with bf16
-rounding points inside the pass, an fp32 sum that lands on the other side of
-a bf16 rounding boundary flips one ulp, and on weights with large outliers a
-single flip can move a logit by a few 1e-3 of the row maximum.  The end-to-end
-logit comparison uses that measured envelope (never below 2e-3).
+With bf16 rounding points inside the pass, an fp32-accumulated value that
+lands on the other side of a bf16 rounding boundary than the fp64 oracle's
+flips one ulp, and on weights with large outliers a single flip can move a
+logit by a few 1e-3 of the row maximum.  Two independent estimates of that
+noise, both computed from the oracle's definition alone:
+
+* ``forward_fp32``: an fp32 evaluation from torch CPU library routines, with a
+  seeded permutation of every matmul's summation order;
+* ``noisy_oracle``: the oracle itself with every value perturbed by a random
+  relative amount of at most ``eta`` (fp32-accumulation level) just before
+  each bf16 rounding point.
+
+The end-to-end logit comparison allows max(2e-3, 1.5 x the larger envelope);
+the kernel-level parity tests, which see identical inputs, keep the plain
+bound.
 """
 
 from __future__ import annotations
@@ -61,16 +68,36 @@ def forward_fp32(m: om.OracleModel, cache: om.KVCache, L: int, tokens, parents, 
     return mm(f, T(m.lm_head)).double().numpy()
 
 
+def noisy_oracle(m, cache, L, tokens, parents, seed: int, eta: float = 2.0 ** -18) -> np.ndarray:
+    """Oracle logits with each pre-rounding value scaled by (1 + u), |u| <= eta."""
+    from oracle import bf16 as obf
+
+    rng = np.random.default_rng(seed)
+    orig = om.round_bf16
+
+    def noisy(x):
+        x = np.asarray(x, dtype=np.float64)
+        return obf.round_bf16(x * (1.0 + eta * (2.0 * rng.random(x.shape) - 1.0)))
+
+    om.round_bf16 = noisy
+    try:
+        return om.forward_tree(m, cache, L, tokens, parents)[0]
+    finally:
+        om.round_bf16 = orig
+
+
 def noise_envelope(m, cache, L, tokens, parents, ref_logits: np.ndarray, runs: int = 4) -> float:
-    """Largest row max-abs-rel deviation from the fp64 oracle over `runs`
-    fp32 evaluations with different summation orders."""
+    """Largest row max-abs-rel deviation from the fp64 oracle over `runs` fp32
+    evaluations with different summation orders and `runs` noisy-rounding
+    oracle evaluations."""
     from tests.parity import row_max_abs_rel
     worst = 0.0
     for s in range(runs):
-        g = forward_fp32(m, cache, L, tokens, parents, seed=1000 + s)
-        worst = max(worst, float(row_max_abs_rel(g, ref_logits).max()))
+        for g in (forward_fp32(m, cache, L, tokens, parents, seed=1000 + s),
+                  noisy_oracle(m, cache, L, tokens, parents, seed=2000 + s)):
+            worst = max(worst, float(row_max_abs_rel(g, ref_logits).max()))
     return worst
 
 
 def logit_tolerance(envelope: float, floor: float = 2e-3) -> float:
-    return max(floor, 2.0 * envelope)
+    return max(floor, 1.5 * envelope)

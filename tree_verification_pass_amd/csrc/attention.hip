@@ -69,18 +69,17 @@ struct AttnArgs {
   float* po;
   float* pm;
   float* pl;
-  uint32_t* cnt;
+  int row_blocks;  // merge: 16-row blocks per (request, kv head)
   uint16_t* out;
 };
 
-template <int D>
-__global__ __launch_bounds__(512) void tree_attn_kernel(AttnArgs a) {
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
   constexpr int KC = 64;        // keys per LDS stage
   constexpr int CH = D / 8;     // 16-byte chunks per K row
   constexpr int NDB = D / 32;   // d blocks of the P V product
   __shared__ uint4 ks[KC * CH];              // K [key][chunk ^ (key % CH)]
   __shared__ uint2 vt[D * (KC / 4)];         // V^T [d][4-key chunk ^ (d % 16)]
-  __shared__ uint32_t s_last;
 
   const int split = blockIdx.x % a.max_splits;
   const int kh = (blockIdx.x / a.max_splits) % a.hkv;
@@ -91,7 +90,7 @@ __global__ __launch_bounds__(512) void tree_attn_kernel(AttnArgs a) {
   if (split >= nsplit) return;
   const int k0 = split * a.kr, k1 = min(T, k0 + a.kr);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
-  const int nthr = blockDim.x;
+  constexpr int nthr = NT;
   const int row = wave * 32 + (lane & 31);
   const bool row_ok = row < R;
   const int gq = row_ok ? row / n : 0, node = row_ok ? row % n : 0;
@@ -116,105 +115,133 @@ __global__ __launch_bounds__(512) void tree_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[db][v] = 0.0f;
 
-  for (int sub = k0; sub < k1; sub += KC) {
-    __syncthreads();
-    for (int idx = tid; idx < KC * CH; idx += nthr) {
-      const int key = idx / CH, c = idx % CH;
-      const int kk = sub + key;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (kk < k1) {
-        kv = *(const uint4*)(kbase + (int64_t)kk * D + 8 * c);
-        vv = *(const uint4*)(vbase + (int64_t)kk * D + 8 * c);
+  // K/V of the next 64 keys are fetched into registers while the current
+  // ones are used (nthr is 256 or 512, so at most PER chunks per thread).
+  constexpr int PER = KC * CH / NT;
+  uint4 kpre[PER], vpre[PER];
+  auto fetch = [&](int sub) {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int idx = tid + it * nthr;
+      kpre[it] = make_uint4(0, 0, 0, 0);
+      vpre[it] = make_uint4(0, 0, 0, 0);
+      if (idx < KC * CH) {
+        const int kk = sub + idx / CH, c = idx % CH;
+        if (kk < k1) {
+          kpre[it] = *(const uint4*)(kbase + (int64_t)kk * D + 8 * c);
+          vpre[it] = *(const uint4*)(vbase + (int64_t)kk * D + 8 * c);
+        }
       }
-      ks[key * CH + (c ^ (key % CH))] = kv;
+    }
+  };
+  auto stash = [&]() {
+    uint16_t* vts = (uint16_t*)vt;
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int idx = tid + it * nthr;
+      if (idx >= KC * CH) continue;
+      const int key = idx / CH, c = idx % CH;
+      ks[key * CH + (c ^ (key % CH))] = kpre[it];
+      const uint4 vv = vpre[it];
       const uint32_t hv[8] = {vv.x & 0xFFFFu, vv.x >> 16, vv.y & 0xFFFFu, vv.y >> 16,
                               vv.z & 0xFFFFu, vv.z >> 16, vv.w & 0xFFFFu, vv.w >> 16};
-      uint16_t* vts = (uint16_t*)vt;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int dd = 8 * c + e;
         vts[(dd * (KC / 4) + ((key >> 2) ^ (dd & 15))) * 4 + (key & 3)] = (uint16_t)hv[e];
       }
     }
+  };
+
+  fetch(k0);
+  for (int sub = k0; sub < k1; sub += KC) {
     __syncthreads();
+    stash();
+    __syncthreads();
+    if (sub + KC < k1) fetch(sub + KC);
     if (wave * 32 >= R) continue;
 
-    // scores S^T[key][row] for two 32-key blocks
-    f32x16_t s[2];
+    // one 32-key block at a time: scores S^T[key][row], online softmax, P V
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      f32x16_t sc;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = 0.0f;
-      const int key = kb * 32 + (lane & 31);
+      for (int v = 0; v < 16; ++v) sc[v] = 0.0f;
+      {
+        const int key = kb * 32 + (lane & 31);
 #pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds) {
-        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ks[key * CH + ((2 * ds + h) ^ (key % CH))]);
-        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, qf[ds]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, s[kb], 0, 0, 0);
+        for (int ds = 0; ds < D / 16; ++ds) {
+          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ks[key * CH + ((2 * ds + h) ^ (key % CH))]);
+          const bf16x8_t B = __builtin_bit_cast(bf16x8_t, qf[ds]);
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, sc, 0, 0, 0);
+        }
       }
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      float mloc = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = sub + kb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
         bool vis = row_ok && key < k1;
         if (vis && key >= L) vis = (anc >> (key - L)) & 1ull;
-        const float x = vis ? s[kb][v] * a.scale_log2 : -INFINITY;
-        s[kb][v] = x;
+        const float x = vis ? sc[v] * a.scale_log2 : -INFINITY;
+        sc[v] = x;
         mloc = fmaxf(mloc, x);
       }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float base = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = exp2f(m_run - base);
-    // P is split into two bf16 pieces (hi = bf16(p), lo = bf16(p - hi)) so the
-    // P V product on bf16 MFMA keeps 16 significant bits of every weight.
-    float lsum = 0.0f;
-    uint32_t pk[2][8], pl[2][8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      const float m_new = fmaxf(m_run, mloc);
+      const float base = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = exp2f(m_run - base);
+      // P is split into two bf16 pieces (hi = bf16(p), lo = bf16(p - hi)) so the
+      // P V product on bf16 MFMA keeps 16 significant bits of every weight.
+      float lsum = 0.0f;
+      uint32_t pk[8], pl[8];
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
-        const float p0 = exp2f(s[kb][v] - base), p1 = exp2f(s[kb][v + 1] - base);
+        const float p0 = exp2f(sc[v] - base), p1 = exp2f(sc[v + 1] - base);
         lsum += p0 + p1;
         const uint32_t h0 = f32_to_bf16(p0), h1 = f32_to_bf16(p1);
-        pk[kb][v / 2] = h0 | (h1 << 16);
-        pl[kb][v / 2] = f32_to_bf16(p0 - bf16_to_f32(h0)) | (f32_to_bf16(p1 - bf16_to_f32(h1)) << 16);
+        pk[v / 2] = h0 | (h1 << 16);
+        pl[v / 2] = f32_to_bf16(p0 - bf16_to_f32(h0)) | (f32_to_bf16(p1 - bf16_to_f32(h1)) << 16);
       }
-    lsum += __shfl_xor(lsum, 32);
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
+      lsum += __shfl_xor(lsum, 32);
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
 
-    // O^T[d][row] += V^T[d][key] P^T[key][row]; MFMA q of key block kb covers
-    // keys kb*32 + 16 q + 8 (i/4) + 4 h + i%4 for k-index 8 h + i.
+      // O^T[d][row] += V^T[d][key] P^T[key][row]; MFMA q of this key block
+      // covers keys kb*32 + 16 q + 8 (i/4) + 4 h + i%4 for k-index 8 h + i.
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int dd = db * 32 + (lane & 31);
+      for (int q = 0; q < 2; ++q) {
+        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]));
+        const bf16x8_t Bl = __builtin_bit_cast(bf16x8_t, make_uint4(pl[4 * q], pl[4 * q + 1], pl[4 * q + 2], pl[4 * q + 3]));
+        const int c8 = 8 * kb + 4 * q + h;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int c8 = 8 * kb + 4 * q + h;
+        for (int db = 0; db < NDB; ++db) {
+          const int dd = db * 32 + (lane & 31);
           const uint2 lo = vt[dd * (KC / 4) + (c8 ^ (dd & 15))];
           const uint2 hi = vt[dd * (KC / 4) + ((c8 + 2) ^ (dd & 15))];
           const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          const bf16x8_t B = __builtin_bit_cast(
-              bf16x8_t, make_uint4(pk[kb][4 * q], pk[kb][4 * q + 1], pk[kb][4 * q + 2], pk[kb][4 * q + 3]));
-          const bf16x8_t Bl = __builtin_bit_cast(
-              bf16x8_t, make_uint4(pl[kb][4 * q], pl[kb][4 * q + 1], pl[kb][4 * q + 2], pl[kb][4 * q + 3]));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, o[db], 0, 0, 0);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bl, o[db], 0, 0, 0);
         }
+      }
     }
   }
 
-  // partials
+  // single split: normalise and store; otherwise write (max, sum, O) partials
+  if (nsplit == 1) {
+    if (row_ok) {
+      const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+      uint16_t* op = a.out + ((int64_t)(nb + node) * a.hq + kh * a.G + gq) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) op[db * 32 + 8 * (v >> 2) + 4 * h + (v & 3)] = (uint16_t)f32_to_bf16(o[db][v] * inv);
+    }
+    return;
+  }
   // partial rows: [kv head][split][G * global node], request r's rows start at G * nb
   const int64_t pbase = ((int64_t)kh * a.max_splits + split) * a.rows_total + (int64_t)a.G * nb;
   if (row_ok) {
@@ -230,33 +257,58 @@ __global__ __launch_bounds__(512) void tree_attn_kernel(AttnArgs a) {
       a.pl[pbase + row] = l_run;
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&a.cnt[r * a.hkv + kh], 1u);
-    s_last = (old == (uint32_t)nsplit - 1u) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid == 0) a.cnt[r * a.hkv + kh] = 0u;
+}
 
-  // merge the splits of this (request, kv head) in split order
+// Merge of the key splits, in split order (a separate launch: the kernel
+// boundary makes every split's partials visible).  One workgroup per
+// (request, kv head, 16 query rows).
+template <int D>
+__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
+  __shared__ float wts[16 * 32];
+  const int rb = blockIdx.x % a.row_blocks;
+  const int kh = (blockIdx.x / a.row_blocks) % a.hkv;
+  const int r = blockIdx.x / (a.row_blocks * a.hkv);
+  const int L = a.ri.ctx_len[r], nb = a.ri.node_ptr[r], n = a.ri.node_ptr[r + 1] - nb;
+  const int R = a.G * n;
+  const int nsplit = (L + n + a.kr - 1) / a.kr;
+  if (nsplit <= 1 || rb * 16 >= R) return;
+  const int tid = threadIdx.x;
   const int64_t hb = (int64_t)kh * a.max_splits * a.rows_total + (int64_t)a.G * nb;
-  for (int idx = tid; idx < R * D; idx += nthr) {
-    const int rr = idx / D, dd = idx % D;
+  const int r0 = rb * 16, nr = min(16, R - r0);
+  if (tid < nr) {
+    const int rr = r0 + tid;
     float mx = -INFINITY;
     for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, a.pm[hb + (int64_t)sp * a.rows_total + rr]);
     const float bse = mx == -INFINITY ? 0.0f : mx;
-    float num = 0.0f, den = 0.0f;
+    float den = 0.0f;
     for (int sp = 0; sp < nsplit; ++sp) {
       const int64_t pr = hb + (int64_t)sp * a.rows_total + rr;
       const float w = exp2f(a.pm[pr] - bse);
+      wts[tid * 32 + sp] = w;
       den += a.pl[pr] * w;
-      num += a.po[pr * D + dd] * w;
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    for (int sp = 0; sp < nsplit; ++sp) wts[tid * 32 + sp] *= inv;
+  }
+  __syncthreads();
+  for (int q4 = tid; q4 < nr * (D / 4); q4 += 256) {
+    const int lr = q4 / (D / 4), dd = (q4 % (D / 4)) * 4;
+    const int rr = r0 + lr;
+    float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float4 v = *(const float4*)&a.po[(hb + (int64_t)sp * a.rows_total + rr) * D + dd];
+      const float w = wts[lr * 32 + sp];
+      acc4.x += v.x * w;
+      acc4.y += v.y * w;
+      acc4.z += v.z * w;
+      acc4.w += v.w * w;
     }
     const int g2 = rr / n, nd = rr % n;
-    a.out[((int64_t)(nb + nd) * a.hq + kh * a.G + g2) * D + dd] = (uint16_t)f32_to_bf16(den > 0.0f ? num / den : 0.0f);
+    uint16_t* op = a.out + ((int64_t)(nb + nd) * a.hq + kh * a.G + g2) * D + dd;
+    op[0] = (uint16_t)f32_to_bf16(acc4.x);
+    op[1] = (uint16_t)f32_to_bf16(acc4.y);
+    op[2] = (uint16_t)f32_to_bf16(acc4.z);
+    op[3] = (uint16_t)f32_to_bf16(acc4.w);
   }
 }
 
@@ -270,10 +322,10 @@ struct AttnPlan {
 static AttnPlan attn_plan(int hkv, int G, int d, int r_max, int n_total, int max_keys) {
   AttnPlan p{};
   p.kr = 512;
+  while (max_keys > 32 * p.kr) p.kr *= 2;  // at most 32 splits (merge weights live in LDS)
   p.max_splits = max_keys > 0 ? (max_keys + p.kr - 1) / p.kr : 1;
   p.rows_total = G * n_total;
-  const int nw = (r_max + 31) / 32;
-  p.nthreads = (nw < 1 ? 1 : nw) * 64;
+  p.nthreads = r_max <= 128 ? 256 : 512;
   const size_t rows = (size_t)hkv * p.max_splits * p.rows_total;
   size_t off = 0;
   p.off_po = off;
@@ -322,12 +374,22 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
   a.po = (float*)(sb + p.off_po);
   a.pm = (float*)(sb + p.off_pm);
   a.pl = (float*)(sb + p.off_pl);
-  a.cnt = attn_cnt;
+  (void)attn_cnt;
   a.out = out;
+  a.row_blocks = (r_max + 15) / 16;
   const dim3 grid((unsigned)(n_req * hkv * p.max_splits));
-  if (d == 128) tree_attn_kernel<128><<<grid, dim3(p.nthreads), 0, stream>>>(a);
-  else if (d == 64) tree_attn_kernel<64><<<grid, dim3(p.nthreads), 0, stream>>>(a);
-  else return TVP_ERR_SHAPE;
+  const dim3 mgrid((unsigned)(n_req * hkv * a.row_blocks));
+  if (d == 128) {
+    if (p.nthreads == 256) tree_attn_kernel<128, 256><<<grid, dim3(256), 0, stream>>>(a);
+    else tree_attn_kernel<128, 512><<<grid, dim3(512), 0, stream>>>(a);
+    if (p.max_splits > 1) tree_attn_merge_kernel<128><<<mgrid, dim3(256), 0, stream>>>(a);
+  } else if (d == 64) {
+    if (p.nthreads == 256) tree_attn_kernel<64, 256><<<grid, dim3(256), 0, stream>>>(a);
+    else tree_attn_kernel<64, 512><<<grid, dim3(512), 0, stream>>>(a);
+    if (p.max_splits > 1) tree_attn_merge_kernel<64><<<mgrid, dim3(256), 0, stream>>>(a);
+  } else {
+    return TVP_ERR_SHAPE;
+  }
   TVP_LAUNCH_CHECK();
   return TVP_OK;
 }

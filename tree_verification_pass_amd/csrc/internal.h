@@ -5,10 +5,17 @@
 
 namespace tvp {
 
-// W12 GEMM with caller-provided counters (`cnt`: groups entries, `cnt2`: one
-// entry; both zero on entry and left zero) and scratch for partials.
+// Zero region of a GEMM: completion counters (kGemmMaxGroups entries), then
+// argmax buckets (192 rows x 64 u64).  Zero on entry, left zero by every call.
+constexpr size_t kGemmMaxGroups = 32768;
+constexpr size_t kGemmKeyBytes = 192 * 64 * 8;
+constexpr size_t kGemmZeroBytes = 256 * 1024;
+static_assert(kGemmMaxGroups * 4 + kGemmKeyBytes <= kGemmZeroBytes, "zero region");
+
+// W12 GEMM with caller-provided counters (`cnt`, groups entries), argmax
+// buckets (`keys`) and scratch for partial sums.
 int gemm_run(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
-             const tvp_gemm_epilogue* epi, uint32_t* cnt, uint32_t* cnt2, void* scratch,
+             const tvp_gemm_epilogue* epi, uint32_t* cnt, unsigned long long* keys, void* scratch,
              size_t scratch_bytes, hipStream_t stream);
 // Counter entries and scratch bytes gemm_run needs for m rows.
 void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes);

@@ -35,25 +35,58 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 }
 
 // y = bf16(x * (mean(x^2) + eps)^-1/2 * g), fp32 with a fixed reduction order.
+// One workgroup per row; rows of 8-element chunks (16-byte loads) when the
+// row length and pitches allow it, element by element otherwise.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x, int ldx,
                                                       const uint16_t* __restrict__ g, int hidden,
                                                       float eps, uint16_t* __restrict__ y, int ldy) {
   __shared__ float ws[4];
   const int i = blockIdx.x, tid = threadIdx.x;
   const uint16_t* xr = x + (int64_t)i * ldx;
+  uint16_t* yr = y + (int64_t)i * ldy;
+  const bool vec = (hidden % 8) == 0 && (ldx % 8) == 0 && (ldy % 8) == 0;
   float ss = 0.0f;
-  for (int k = tid; k < hidden; k += 256) {
-    const float v = bf16_to_f32(xr[k]);
-    ss += v * v;
+  if (vec) {
+    const int nc = hidden / 8;
+    for (int c = tid; c < nc; c += 256) {
+      const uint4 v = *(const uint4*)(xr + 8 * c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a0 = bf16_to_f32(w[e] & 0xFFFFu), a1 = bf16_to_f32(w[e] >> 16);
+        ss += a0 * a0 + a1 * a1;
+      }
+    }
+  } else {
+    for (int k = tid; k < hidden; k += 256) {
+      const float v = bf16_to_f32(xr[k]);
+      ss += v * v;
+    }
   }
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   if ((tid & 63) == 0) ws[tid >> 6] = ss;
   __syncthreads();
   const float tot = (ws[0] + ws[1]) + (ws[2] + ws[3]);
   const float r = 1.0f / sqrtf(tot / (float)hidden + eps);
-  uint16_t* yr = y + (int64_t)i * ldy;
-  for (int k = tid; k < hidden; k += 256)
-    yr[k] = (uint16_t)f32_to_bf16(bf16_to_f32(xr[k]) * r * bf16_to_f32(g[k]));
+  if (vec) {
+    const int nc = hidden / 8;
+    for (int c = tid; c < nc; c += 256) {
+      const uint4 v = *(const uint4*)(xr + 8 * c);
+      const uint4 gv = *(const uint4*)(g + 8 * c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = f32_to_bf16(bf16_to_f32(w[e] & 0xFFFFu) * r * bf16_to_f32(gw[e] & 0xFFFFu));
+        const uint32_t hi = f32_to_bf16(bf16_to_f32(w[e] >> 16) * r * bf16_to_f32(gw[e] >> 16));
+        o[e] = lo | (hi << 16);
+      }
+      *(uint4*)(yr + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  } else {
+    for (int k = tid; k < hidden; k += 256)
+      yr[k] = (uint16_t)f32_to_bf16(bf16_to_f32(xr[k]) * r * bf16_to_f32(g[k]));
+  }
 }
 
 // One workgroup per request; the walk is sequential over nodes (parents[i] < i).
@@ -158,7 +191,7 @@ struct tvp_plan {
   int32_t max_nodes;
   int ld_h, ld_q, ld_u;
   // workspace layout
-  size_t off_gcnt, off_gcnt2, off_acnt, zero_end;
+  size_t off_gcnt, off_gkeys, off_acnt, zero_end;
   size_t off_h, off_a, off_q, off_o, off_u;
   size_t off_anc, off_pos, off_slot, off_tstat, off_bad;
   size_t off_gscr, gscr_bytes;
@@ -185,6 +218,7 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   const int hq = d->n_heads, hkv = d->n_kv_heads, hd = d->head_dim, H = d->hidden, F = d->ffn;
   const int G = hq / hkv;
   if (G * std::min(max_nodes, 64) > 256) return TVP_ERR_SHAPE;
+  if ((uintptr_t)d->final_norm % 16) return TVP_ERR_ARG;
   int st = check_packed(d->lm_head, d->vocab, H, TVP_CHAN_PLAIN);
   if (st) return st;
   for (int l = 0; l < d->n_layers; ++l) {
@@ -196,7 +230,8 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
     if ((st = check_packed(L.wgu, 2LL * F, H, TVP_CHAN_GATEUP))) return st;
     if (L.wgu.map_a != F) return TVP_ERR_FORMAT;
     if ((st = check_packed(L.wdown, H, F, TVP_CHAN_PLAIN))) return st;
-    if (((uintptr_t)L.k_cache | (uintptr_t)L.v_cache) % 16) return TVP_ERR_ARG;
+    if (((uintptr_t)L.k_cache | (uintptr_t)L.v_cache | (uintptr_t)L.attn_norm | (uintptr_t)L.ffn_norm) % 16)
+      return TVP_ERR_ARG;
   }
   tvp_plan* p = new (std::nothrow) tvp_plan();
   if (!p) return TVP_ERR_ARG;
@@ -230,8 +265,8 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   size_t off = 0;
   p->off_gcnt = off;
   off = align_up(off + (size_t)gmax * 4, 256);
-  p->off_gcnt2 = off;
-  off += 256;
+  p->off_gkeys = off;
+  off = align_up(off + kGemmKeyBytes, 256);
   p->off_acnt = off;
   off = align_up(off + (size_t)kMaxReq * hkv * 4, 256);
   p->zero_end = off;
@@ -288,7 +323,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   }
   uint8_t* w = (uint8_t*)ws;
   uint32_t* gcnt = (uint32_t*)(w + p->off_gcnt);
-  uint32_t* gcnt2 = (uint32_t*)(w + p->off_gcnt2);
+  unsigned long long* gkeys = (unsigned long long*)(w + p->off_gkeys);
   uint32_t* acnt = (uint32_t*)(w + p->off_acnt);
   uint16_t* h = (uint16_t*)(w + p->off_h);
   uint16_t* a = (uint16_t*)(w + p->off_a);
@@ -321,7 +356,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     e.v_cache = L.v_cache;
     e.s_stride = d.s_max;
     e.rope_theta = d.rope_theta;
-    if ((st = gemm_run(a, n_total, p->ld_h, &L.wqkv, &e, gcnt, gcnt2, gscr, p->gscr_bytes, stream))) return st;
+    if ((st = gemm_run(a, n_total, p->ld_h, &L.wqkv, &e, gcnt, gkeys, gscr, p->gscr_bytes, stream))) return st;
     if ((st = launch_tree_attention(q, L.k_cache, L.v_cache, d.s_max, ri, s_req, anc, hq, hkv, hd, G * max_n,
                                     max_keys, o, acnt, ascr, p->ascr_bytes, stream)))
       return st;
@@ -331,21 +366,21 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     e.ldy = p->ld_h;
     e.resid = h;
     e.ldr = p->ld_h;
-    if ((st = gemm_run(o, n_total, p->ld_q, &L.wo, &e, gcnt, gcnt2, gscr, p->gscr_bytes, stream))) return st;
+    if ((st = gemm_run(o, n_total, p->ld_q, &L.wo, &e, gcnt, gkeys, gscr, p->gscr_bytes, stream))) return st;
     rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, L.ffn_norm, H, d.norm_eps, a, p->ld_h);
     TVP_LAUNCH_CHECK();
     e = tvp_gemm_epilogue{};
     e.mode = TVP_EPI_SWIGLU;
     e.y = u;
     e.ldy = p->ld_u;
-    if ((st = gemm_run(a, n_total, p->ld_h, &L.wgu, &e, gcnt, gcnt2, gscr, p->gscr_bytes, stream))) return st;
+    if ((st = gemm_run(a, n_total, p->ld_h, &L.wgu, &e, gcnt, gkeys, gscr, p->gscr_bytes, stream))) return st;
     e = tvp_gemm_epilogue{};
     e.mode = TVP_EPI_RESID;
     e.y = h;
     e.ldy = p->ld_h;
     e.resid = h;
     e.ldr = p->ld_h;
-    if ((st = gemm_run(u, n_total, p->ld_u, &L.wdown, &e, gcnt, gcnt2, gscr, p->gscr_bytes, stream))) return st;
+    if ((st = gemm_run(u, n_total, p->ld_u, &L.wdown, &e, gcnt, gkeys, gscr, p->gscr_bytes, stream))) return st;
   }
   rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, d.final_norm, H, d.norm_eps, a, p->ld_h);
   TVP_LAUNCH_CHECK();
@@ -354,7 +389,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   e.argmax = out->argmax;
   e.logits = out->logits;
   e.ldl = d.vocab;
-  if ((st = gemm_run(a, n_total, p->ld_h, &d.lm_head, &e, gcnt, gcnt2, gscr, p->gscr_bytes, stream))) return st;
+  if ((st = gemm_run(a, n_total, p->ld_h, &d.lm_head, &e, gcnt, gkeys, gscr, p->gscr_bytes, stream))) return st;
   accept_kernel<<<dim3(ri.n_req), dim3(64), 0, stream>>>(out->argmax, tokens, parents, ri, bad, out->path,
                                                          out->n_accepted, out->bonus, out->status);
   TVP_LAUNCH_CHECK();

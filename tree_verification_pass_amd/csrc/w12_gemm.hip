@@ -21,6 +21,9 @@
 //    and applies the epilogue: results are bitwise reproducible.
 #include <math.h>
 
+#include <algorithm>
+#include <type_traits>
+
 #include "internal.h"
 
 namespace tvp {
@@ -35,12 +38,10 @@ struct GemmArgs {
   const uint32_t* b2;
   const int32_t* rowmap;
   int n_tiles, n_kb, n_pad;
-  int groups, splits, kbs;
+  int groups, splits, kbs, ntasks;
   float* part;
   uint32_t* cnt;
-  uint32_t* cnt2;
-  float* amax_v;
-  int32_t* amax_i;
+  unsigned long long* keys;  // ARGMAX: [m][64] packed (value, -id) maxima, zero on entry
   int mode;
   void* y;
   int64_t ldy;
@@ -57,6 +58,8 @@ struct GemmArgs {
   float* logits;
   int64_t ldl;
 };
+
+constexpr int kArgmaxBuckets = 64;
 
 __device__ inline uint32_t rotl32(uint32_t x, int r) { return r == 0 ? x : (x << r) | (x >> (32 - r)); }
 
@@ -79,13 +82,346 @@ __device__ inline bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8
 
 __device__ inline float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
+// Compiler-level ordering of LDS accesses within one wavefront.  The
+// wavefront's LDS instructions execute in issue order, so no wait is needed;
+// the clobber keeps the compiler from reordering or forwarding across it.
+__device__ inline void lds_order() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// (value, id) packed so that a 64-bit unsigned max picks the largest value
+// and, among equal values, the smallest id.
+__device__ inline unsigned long long argmax_key(float v, int32_t id) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)id);
+}
+
+// Epilogue over packed channels [c0, c0+nc) x rows [0, M) by `nthr` threads
+// (thread index `tid`), reading fp32 results through V(row, col).
+template <int MODE, typename Get>
+__device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int tid, int nthr, int bucket,
+                                Get V) {
+  if constexpr (MODE == TVP_EPI_F32 || MODE == TVP_EPI_BF16 || MODE == TVP_EPI_RESID) {
+    for (int idx = tid; idx < M * nc; idx += nthr) {
+      const int row = idx / nc, col = c0 + idx % nc;
+      const int32_t r = a.rowmap[col];
+      if (r < 0) continue;
+      const float v = V(row, col);
+      if constexpr (MODE == TVP_EPI_F32) {
+        ((float*)a.y)[row * a.ldy + r] = v;
+      } else if constexpr (MODE == TVP_EPI_BF16) {
+        ((uint16_t*)a.y)[row * a.ldy + r] = (uint16_t)f32_to_bf16(v);
+      } else {
+        const float rv = bf16_to_f32(a.resid[row * a.ldr + r]);
+        ((uint16_t*)a.y)[row * a.ldy + r] = (uint16_t)f32_to_bf16(rv + v);
+      }
+    }
+  } else if constexpr (MODE == TVP_EPI_SWIGLU) {
+    const int half = nc / 2;  // nc is a multiple of 32
+    for (int idx = tid; idx < M * half; idx += nthr) {
+      const int row = idx / half, p = idx % half;
+      const int col = c0 + (p / 16) * 32 + (p % 16);
+      const int32_t r = a.rowmap[col];
+      if (r < 0) continue;
+      const float gv = V(row, col), uv = V(row, col + 16);
+      ((uint16_t*)a.y)[row * a.ldy + r] = (uint16_t)f32_to_bf16(silu_f32(gv) * uv);
+    }
+  } else if constexpr (MODE == TVP_EPI_QKV) {
+    const int d = a.d, tph = d / 32;
+    const int rot_tiles = (a.hq + a.hkv) * tph;
+    for (int idx = tid; idx < M * nc; idx += nthr) {
+      const int row = idx / nc, col = c0 + idx % nc;
+      const int t = col / 32, c = col % 32;
+      if (t >= a.n_tiles) continue;
+      if (t < rot_tiles) {
+        if (c >= 16) continue;
+        const int head = t / tph, u = t % tph;
+        const int da = 16 * u + c, db = d / 2 + 16 * u + c;
+        const float xa = V(row, col), xb = V(row, col + 16);
+        const double ang = (double)a.pos[row] * pow(a.theta, -2.0 * (double)da / (double)d);
+        const float cs = (float)cos(ang), sn = (float)sin(ang);
+        const float oa = xa * cs - xb * sn, ob = xb * cs + xa * sn;
+        if (head < a.hq) {
+          uint16_t* q = (uint16_t*)a.y + (int64_t)row * a.ldy + (int64_t)head * d;
+          q[da] = (uint16_t)f32_to_bf16(oa);
+          q[db] = (uint16_t)f32_to_bf16(ob);
+        } else {
+          uint16_t* kr = a.kc + ((int64_t)(head - a.hq) * a.s_stride + a.slot[row]) * d;
+          kr[da] = (uint16_t)f32_to_bf16(oa);
+          kr[db] = (uint16_t)f32_to_bf16(ob);
+        }
+      } else {
+        const int vr = (t - rot_tiles) * 32 + c;
+        if (vr >= a.hkv * d) continue;
+        const int kh = vr / d, dim = vr % d;
+        a.vc[((int64_t)kh * a.s_stride + a.slot[row]) * d + dim] = (uint16_t)f32_to_bf16(V(row, col));
+      }
+    }
+  } else {  // ARGMAX: per row the best (value, smallest id), merged by a 64-bit atomic max
+    for (int row = 0; row < M; ++row) {
+      unsigned long long best = 0ull;
+      for (int cc = tid; cc < nc; cc += nthr) {
+        const int col = c0 + cc;
+        const int32_t r = a.rowmap[col];
+        if (r < 0) continue;
+        const float v = V(row, col);
+        if (a.logits) a.logits[row * a.ldl + r] = v;
+        const unsigned long long k = argmax_key(v, r);
+        best = k > best ? k : best;
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(best, off);
+        best = o > best ? o : best;
+      }
+      if ((tid & 63) == 0 && best) atomicMax(&a.keys[row * kArgmaxBuckets + bucket], best);
+    }
+  }
+}
+
+// One workgroup: argmax[row] from the bucket maxima, then the buckets are
+// cleared for the next launch.
+__global__ __launch_bounds__(256) void argmax_finalize_kernel(unsigned long long* __restrict__ keys, int m,
+                                                              int32_t* __restrict__ argmax) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int row = wave; row < m; row += 4) {
+    unsigned long long k = keys[row * kArgmaxBuckets + lane];
+    for (int off = 32; off > 0; off >>= 1) {
+      const unsigned long long o = __shfl_xor(k, off);
+      k = o > k ? o : k;
+    }
+    if (lane == 0) argmax[row] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)) : 0;
+    keys[row * kArgmaxBuckets + lane] = 0ull;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Skinny kernel (m <= 32): a workgroup owns TPW tiles; its KW wavefronts split
+// the K range and stream independently.  Records, escape entries and
+// activation fragments for block i + RD - 1 are in flight while block i is
+// decoded and multiplied (a register ring, unrolled so no copies tie the
+// prefetch to the use).  Activation fragments come straight from global
+// memory (a few hundred KB, they stay in L2).  The escape offsets of a
+// wave's blocks sit in one VGPR per tile (lane i = block kb0 + i) and are read
+// with readlane, so no load in the loop depends on another.  At the end the
+// waves' fp32 partial tiles meet in LDS and are summed in wave order: no
+// global partial sums, no atomics, no device-scope fences.
+template <int MT, int TPW, int RD, int MODE>
+__global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
+  constexpr int NACC = MT == 32 ? 16 : 4;
+  constexpr int NCH = MT == 32 ? 1 : 2;
+  constexpr int KS = MT == 32 ? 4 : 2;  // MFMA K-steps per 64-column block
+  typedef float accv __attribute__((ext_vector_type(NACC)));
+  extern __shared__ uint4 dsm[];  // KW x TPW x 4 KB: decode scratch, then the partial tiles
+  typedef uint4 scr_t[TPW][256];
+  scr_t* scr = (scr_t*)dsm;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int KW = blockDim.x >> 6;
+  const int grp = blockIdx.x;
+  const int t0 = grp * TPW;
+  const int kb0 = wave * a.kbs;
+  const int kb1 = min(a.n_kb, kb0 + a.kbs);
+  const int nblk = kb1 > kb0 ? kb1 - kb0 : 0;  // <= 63
+
+  // Tiles past the end are computed on a clamped tile and dropped at the end,
+  // so the streaming loop has no data-dependent branches around its loads
+  // (the compiler's wait counters then stay exact and the ring stays full).
+  int tt[TPW];
+  uint32_t ewin[TPW], b2v[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    tt[t] = min(t0 + t, a.n_tiles - 1);
+    ewin[t] = a.escoff[(int64_t)tt[t] * a.n_kb + min(kb0 + min(lane, nblk), a.n_kb)];
+    b2v[t] = a.b2[tt[t] * 32 + (lane & 31)];
+    asm volatile("" ::"v"(ewin[t]), "v"(b2v[t]));  // complete these loads before the ring starts
+  }
+  accv acc[TPW][NCH];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int v = 0; v < NACC; ++v) acc[t][ch][v] = 0.0f;
+
+  const int xrow = MT == 32 ? (lane & 31) : (lane & 15);
+  const int xsub = MT == 32 ? 8 * (lane >> 5) : 8 * (lane >> 4);
+  const bool xrow_ok = xrow < a.m;
+  const uint16_t* xr = a.x + (int64_t)min(xrow, a.m - 1) * a.ldx;
+  // the last block of a ragged K range is handled on its own, with guards
+  const bool ragged_tail = nblk > 0 && kb1 == a.n_kb && (a.k_in & 63) != 0;
+  const int nfast = nblk - (ragged_tail ? 1 : 0);
+
+  uint4 R[RD][TPW][3];
+  uint4 A[RD][KS];
+  uint32_t E[RD][TPW];
+
+  auto issue_recs = [&](int i, int slot) {
+    const int j = kb0 + i;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int64_t un = (int64_t)tt[t] * a.n_kb + j;
+      const uint4* blk = (const uint4*)(a.rec + un * kBlockBytes);
+#pragma unroll
+      for (int q = 0; q < 3; ++q) R[slot][t][q] = load_nt(blk + q * 64 + lane);
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const uint32_t eo = __builtin_amdgcn_readlane(ewin[t], i);
+      const uint32_t ec = __builtin_amdgcn_readlane(ewin[t], i + 1) - eo;
+      // lanes past the count read a neighbour (the blob continues past the
+      // escape list) and are never used
+      E[slot][t] = a.esc[(uint32_t)lane < ec ? eo + lane : eo];
+    }
+  };
+  // full blocks: every activation load is in range
+  auto issue_fast = [&](int i, int slot) {
+    i = min(i, nfast - 1);  // past the end: re-read the last block (cached), result unused
+    issue_recs(i, slot);
+    const int j = kb0 + i;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int64_t k = 64LL * j + (MT == 32 ? 16 : 32) * ks + xsub;
+      // rows past m repeat row m-1; their outputs are never stored
+      A[slot][ks] = *(const uint4*)(xr + k);
+    }
+  };
+  auto issue_tail = [&](int i, int slot) {
+    issue_recs(i, slot);
+    const int j = kb0 + i;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int64_t k = 64LL * j + (MT == 32 ? 16 : 32) * ks + xsub;
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = (xrow_ok && k + e < a.k_in) ? xr[k + e] : 0u;
+      A[slot][ks] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    }
+  };
+
+  auto process = [&](int i, int slot, auto slow) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      uint32_t o[16];
+      decode_block(R[slot][t], b2v[t], o);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        scr[wave][t][64 * s + lane] = make_uint4(o[4 * s], o[4 * s + 1], o[4 * s + 2], o[4 * s + 3]);
+    }
+    lds_order();
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const uint32_t eo = __builtin_amdgcn_readlane(ewin[t], i);
+      const uint32_t ec = __builtin_amdgcn_readlane(ewin[t], i + 1) - eo;
+      uint16_t* sh = (uint16_t*)&scr[wave][t][0];
+      if ((uint32_t)lane < ec) sh[E[slot][t] & 0x7FFu] = (uint16_t)(E[slot][t] >> 16);
+      if constexpr (decltype(slow)::value) {  // more escapes than lanes in some tile block
+        for (uint32_t e = 64 + lane; e < ec; e += 64) {
+          const uint32_t ent = a.esc[eo + e];
+          sh[ent & 0x7FFu] = (uint16_t)(ent >> 16);
+        }
+      }
+    }
+    lds_order();
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      if constexpr (MT == 32) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8_t B = as_bf16x8(scr[wave][t][64 * ks + lane]);
+          acc[t][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[slot][ks]), B, acc[t][0], 0, 0, 0);
+        }
+      } else {
+        const int q = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int ch = 0; ch < 2; ++ch) {
+            const bf16x8_t B = as_bf16x8(scr[wave][t][(4 * ks + q) * 32 + 16 * ch + (lane & 15)]);
+            acc[t][ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A[slot][ks]), B, acc[t][ch], 0, 0, 0);
+          }
+      }
+    }
+    lds_order();
+  };
+
+  // Tasks where some tile block has more escapes than lanes take a simple
+  // unpipelined loop; all others stream through the register ring, whose
+  // body then holds no loop with loads of its own.
+  uint32_t mx = 0;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const uint32_t nxt = __shfl_down(ewin[t], 1);
+    const uint32_t c = lane < nblk ? nxt - ewin[t] : 0u;
+    mx = c > mx ? c : mx;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(mx, off);
+    mx = o > mx ? o : mx;
+  }
+  const bool slow = __builtin_amdgcn_readfirstlane(mx) > 64u;
+  if (!slow) {
+    if (nfast > 0) {
+#pragma unroll
+      for (int p = 0; p < RD - 1; ++p) issue_fast(p, p);
+      for (int i0 = 0; i0 < nfast; i0 += RD) {
+#pragma unroll
+        for (int r = 0; r < RD; ++r) {
+          issue_fast(i0 + r + RD - 1, (r + RD - 1) % RD);
+          if (i0 + r < nfast) process(i0 + r, r, std::false_type{});
+        }
+      }
+    }
+  } else {
+    for (int i = 0; i < nfast; ++i) {
+      issue_fast(i, 0);
+      process(i, 0, std::true_type{});
+    }
+  }
+  if (ragged_tail) {
+    issue_tail(nblk - 1, 0);
+    process(nblk - 1, 0, std::true_type{});
+  }
+
+  // ------------------------------------------------------------- results
+  const int M = a.m;
+  const int NC = TPW * 32;
+  __syncthreads();  // every wave is done with its decode scratch
+  float* P = (float*)dsm;  // [KW][M][NC] fp32 partial tiles
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int v = 0; v < NACC; ++v) {
+        int row, col;
+        if constexpr (MT == 32) {
+          row = (v >> 2) * 8 + 4 * (lane >> 5) + (v & 3);
+          col = t * 32 + (lane & 31);
+        } else {
+          row = 4 * (lane >> 4) + v;
+          col = t * 32 + 16 * ch + (lane & 15);
+        }
+        if (row < M) P[(wave * M + row) * NC + col] = acc[t][ch][v];
+      }
+  __syncthreads();
+  epilogue<MODE>(a, t0 * 32, min(NC, a.n_pad - t0 * 32), M, threadIdx.x, KW * 64, grp & (kArgmaxBuckets - 1),
+                 [&](int row, int col) {
+                   const int c = col - t0 * 32;
+                   float v = 0.0f;
+                   for (int w = 0; w < KW; ++w) v += P[(w * M + row) * NC + c];
+                   return v;
+                 });
+}
+
 template <int ROWS>
 struct XChunk {
   static constexpr int CB = ROWS <= 16 ? 8 : (ROWS <= 32 ? 4 : 2);  // blocks per X chunk
 };
 
 template <int MT, int RB, int TPW>
-__global__ __launch_bounds__(256) void w12_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256) void w12_wide_kernel(GemmArgs a) {
   constexpr int ROWS = MT * RB;
   constexpr int CB = XChunk<ROWS>::CB;
   constexpr int TG = 4 * TPW;
@@ -307,179 +643,114 @@ __global__ __launch_bounds__(256) void w12_gemm_kernel(GemmArgs a) {
     for (int s = 0; s < a.splits; ++s) v += a.part[((int64_t)s * M + row) * a.n_pad + col];
     return v;
   };
-
-  if (a.mode == TVP_EPI_F32 || a.mode == TVP_EPI_BF16 || a.mode == TVP_EPI_RESID) {
-    for (int idx = tid; idx < M * nc; idx += 256) {
-      const int row = idx / nc, col = c0 + idx % nc;
-      const int32_t r = a.rowmap[col];
-      if (r < 0) continue;
-      const float v = red(row, col);
-      if (a.mode == TVP_EPI_F32) {
-        ((float*)a.y)[row * a.ldy + r] = v;
-      } else if (a.mode == TVP_EPI_BF16) {
-        ((uint16_t*)a.y)[row * a.ldy + r] = (uint16_t)f32_to_bf16(v);
-      } else {
-        const float rv = bf16_to_f32(a.resid[row * a.ldr + r]);
-        ((uint16_t*)a.y)[row * a.ldy + r] = (uint16_t)f32_to_bf16(rv + v);
-      }
-    }
-  } else if (a.mode == TVP_EPI_SWIGLU) {
-    const int half = nc / 2;  // nc is a multiple of 32
-    for (int idx = tid; idx < M * half; idx += 256) {
-      const int row = idx / half, p = idx % half;
-      const int col = c0 + (p / 16) * 32 + (p % 16);
-      const int32_t r = a.rowmap[col];
-      if (r < 0) continue;
-      const float gv = red(row, col), uv = red(row, col + 16);
-      ((uint16_t*)a.y)[row * a.ldy + r] = (uint16_t)f32_to_bf16(silu_f32(gv) * uv);
-    }
-  } else if (a.mode == TVP_EPI_QKV) {
-    const int d = a.d, tph = d / 32;
-    const int rot_tiles = (a.hq + a.hkv) * tph;
-    for (int idx = tid; idx < M * nc; idx += 256) {
-      const int row = idx / nc, cc = idx % nc;
-      const int col = c0 + cc;
-      const int t = col / 32, c = col % 32;
-      if (t >= a.n_tiles) continue;
-      if (t < rot_tiles) {
-        if (c >= 16) continue;
-        const int head = t / tph, u = t % tph;
-        const int da = 16 * u + c, db = d / 2 + 16 * u + c;
-        const float xa = red(row, col), xb = red(row, col + 16);
-        const double ang = (double)a.pos[row] * pow(a.theta, -2.0 * (double)da / (double)d);
-        const float cs = (float)cos(ang), sn = (float)sin(ang);
-        const float oa = xa * cs - xb * sn, ob = xb * cs + xa * sn;
-        if (head < a.hq) {
-          uint16_t* q = (uint16_t*)a.y + (int64_t)row * a.ldy + (int64_t)head * d;
-          q[da] = (uint16_t)f32_to_bf16(oa);
-          q[db] = (uint16_t)f32_to_bf16(ob);
-        } else {
-          uint16_t* kr = a.kc + ((int64_t)(head - a.hq) * a.s_stride + a.slot[row]) * d;
-          kr[da] = (uint16_t)f32_to_bf16(oa);
-          kr[db] = (uint16_t)f32_to_bf16(ob);
-        }
-      } else {
-        const int vr = (t - rot_tiles) * 32 + c;
-        if (vr >= a.hkv * d) continue;
-        const int kh = vr / d, dim = vr % d;
-        a.vc[((int64_t)kh * a.s_stride + a.slot[row]) * d + dim] = (uint16_t)f32_to_bf16(red(row, col));
-      }
-    }
-  } else if (a.mode == TVP_EPI_ARGMAX) {
-    __shared__ float bv[4];
-    __shared__ int32_t bi[4];
-    for (int row = 0; row < M; ++row) {
-      float best = -INFINITY;
-      int32_t besti = 0x7FFFFFFF;
-      for (int cc = tid; cc < nc; cc += 256) {
-        const int col = c0 + cc;
-        const int32_t r = a.rowmap[col];
-        if (r < 0) continue;
-        const float v = red(row, col);
-        if (a.logits) a.logits[row * a.ldl + r] = v;
-        if (v > best || (v == best && r < besti)) { best = v; besti = r; }
-      }
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(best, off);
-        const int32_t oi = __shfl_xor(besti, off);
-        if (ov > best || (ov == best && oi < besti)) { best = ov; besti = oi; }
-      }
-      if (lane == 0) { bv[wave] = best; bi[wave] = besti; }
-      __syncthreads();
-      if (tid == 0) {
-        for (int w = 1; w < 4; ++w)
-          if (bv[w] > best || (bv[w] == best && bi[w] < besti)) { best = bv[w]; besti = bi[w]; }
-        a.amax_v[(int64_t)g * M + row] = best;
-        a.amax_i[(int64_t)g * M + row] = besti;
-      }
-      __syncthreads();
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t old = atomicAdd(a.cnt2, 1u);
-      s_last = (old == (uint32_t)a.groups - 1u) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (tid == 0) *a.cnt2 = 0u;
-    for (int row = wave; row < M; row += 4) {
-      float best = -INFINITY;
-      int32_t besti = 0x7FFFFFFF;
-      for (int gg = lane; gg < a.groups; gg += 64) {
-        const float v = a.amax_v[(int64_t)gg * M + row];
-        const int32_t i = a.amax_i[(int64_t)gg * M + row];
-        if (v > best || (v == best && i < besti)) { best = v; besti = i; }
-      }
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(best, off);
-        const int32_t oi = __shfl_xor(besti, off);
-        if (ov > best || (ov == best && oi < besti)) { best = ov; besti = oi; }
-      }
-      if (lane == 0) a.argmax[row] = besti;
-    }
+  const int bucket = g & (kArgmaxBuckets - 1);
+  switch (a.mode) {
+    case TVP_EPI_F32: epilogue<TVP_EPI_F32>(a, c0, nc, M, tid, 256, bucket, red); break;
+    case TVP_EPI_BF16: epilogue<TVP_EPI_BF16>(a, c0, nc, M, tid, 256, bucket, red); break;
+    case TVP_EPI_RESID: epilogue<TVP_EPI_RESID>(a, c0, nc, M, tid, 256, bucket, red); break;
+    case TVP_EPI_SWIGLU: epilogue<TVP_EPI_SWIGLU>(a, c0, nc, M, tid, 256, bucket, red); break;
+    case TVP_EPI_QKV: epilogue<TVP_EPI_QKV>(a, c0, nc, M, tid, 256, bucket, red); break;
+    default: epilogue<TVP_EPI_ARGMAX>(a, c0, nc, M, tid, 256, bucket, red); break;
   }
 }
 
 struct GemmPlan {
-  int MT, RB, TPW, TG, groups, splits, kbs;
-  size_t off_av, off_ai, off_part, scratch_bytes;
+  bool skinny;
+  int MT, RB, TPW, RD, KW, TG, groups, splits, kbs, ntasks, grid;
+  size_t scratch_bytes;
 };
+
+// Work decomposition.  Skinny (m <= 32): one workgroup per TPW tiles whose KW
+// wavefronts split K (kbs <= 63 blocks each, so a wave's escape offsets fit
+// one VGPR).  Wide (m > 32, or K too long for 8 waves of 63 blocks):
+// workgroups of 4 tiles sharing X through LDS, split K over workgroups.
+constexpr int kWideTargetGroups = 1024;
 
 static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w) {
   GemmPlan p{};
+  const int64_t n_pad = (int64_t)w->n_tiles * 32;
+  const int nkb = w->n_kb;
   p.MT = m <= 16 ? 16 : 32;
   p.RB = (int)ceil_div(m, p.MT);
-  p.TPW = (p.RB == 1 && w->n_tiles >= 768) ? 2 : 1;
-  p.TG = 4 * p.TPW;
-  p.groups = (int)ceil_div(w->n_tiles, p.TG);
-  const int target = 1024;  // workgroups per launch, about 4 per CU
-  int s = (int)((target + p.groups / 2) / p.groups);
-  s = s < 1 ? 1 : s;
-  const int smax = (int)ceil_div(w->n_kb, 2);
-  if (s > smax) s = smax < 1 ? 1 : smax;
-  int kbs = (int)ceil_div(w->n_kb, s);
-  kbs += kbs & 1;
-  p.kbs = kbs;
-  p.splits = kbs > 0 ? (int)ceil_div(w->n_kb, kbs) : 1;
-  if (p.splits < 1) p.splits = 1;
-  const int64_t n_pad = (int64_t)w->n_tiles * 32;
-  size_t off = 0;
-  p.off_av = off;
-  off = align_up(off + (size_t)p.groups * m * 4, 256);
-  p.off_ai = off;
-  off = align_up(off + (size_t)p.groups * m * 4, 256);
-  p.off_part = off;
-  off = align_up(off + (size_t)p.splits * m * n_pad * 4, 256);
-  p.scratch_bytes = off;
+  p.skinny = m <= 32 && nkb <= 8 * 63;
+  if (p.skinny) {
+    p.TPW = w->n_tiles >= 1024 ? 2 : 1;
+    p.RD = p.TPW == 2 ? 2 : 3;
+    p.TG = p.TPW;
+    p.groups = (int)ceil_div(w->n_tiles, p.TPW);
+    p.KW = p.groups >= 512 ? 4 : 8;
+    if (nkb > 4 * 63) p.KW = 8;
+    p.KW = std::max(1, std::min(p.KW, nkb));
+    p.kbs = nkb > 0 ? (int)ceil_div(nkb, p.KW) : 0;
+    p.splits = 1;
+    p.ntasks = p.groups;
+    p.grid = p.groups;
+  } else {
+    p.TPW = 1;
+    p.RD = 0;
+    p.KW = 4;
+    p.TG = 4;
+    p.groups = (int)ceil_div(w->n_tiles, p.TG);
+    int s = (int)((kWideTargetGroups + p.groups / 2) / p.groups);
+    s = std::max(s, 1);
+    const int smax = std::max((int)ceil_div(nkb, 2), 1);
+    s = std::min(s, smax);
+    int kbs = nkb > 0 ? (int)ceil_div(nkb, s) : 0;
+    kbs += kbs & 1;
+    p.kbs = kbs;
+    p.splits = kbs > 0 ? (int)ceil_div(nkb, kbs) : 1;
+    p.ntasks = p.groups * p.splits;
+    p.grid = p.ntasks;
+  }
+  p.scratch_bytes = p.skinny ? 256 : align_up((size_t)p.splits * m * n_pad * 4, 256);
   return p;
 }
 
-template <int MT, int RB, int TPW>
-static void launch(const GemmArgs& a, hipStream_t stream) {
-  w12_gemm_kernel<MT, RB, TPW><<<dim3((unsigned)(a.groups * a.splits)), dim3(256), 0, stream>>>(a);
+template <int MT, int TPW, int RD>
+static void launch_skinny(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.grid), block((unsigned)(p.KW * 64));
+  const size_t lds = (size_t)p.KW * TPW * 4096;
+  switch (a.mode) {
+    case TVP_EPI_F32: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_F32><<<grid, block, lds, stream>>>(a); break;
+    case TVP_EPI_BF16: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_BF16><<<grid, block, lds, stream>>>(a); break;
+    case TVP_EPI_RESID: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_RESID><<<grid, block, lds, stream>>>(a); break;
+    case TVP_EPI_SWIGLU: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_SWIGLU><<<grid, block, lds, stream>>>(a); break;
+    case TVP_EPI_QKV: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_QKV><<<grid, block, lds, stream>>>(a); break;
+    default: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_ARGMAX><<<grid, block, lds, stream>>>(a); break;
+  }
+}
+
+template <int RB>
+static void launch_wide(const GemmArgs& a, int grid, hipStream_t stream) {
+  w12_wide_kernel<32, RB, 1><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(a);
 }
 
 static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  if (p.MT == 16) {
-    if (p.TPW == 2) launch<16, 1, 2>(a, stream);
-    else launch<16, 1, 1>(a, stream);
-  } else {
-    switch (p.RB) {
-      case 1:
-        if (p.TPW == 2) launch<32, 1, 2>(a, stream);
-        else launch<32, 1, 1>(a, stream);
-        break;
-      case 2: launch<32, 2, 1>(a, stream); break;
-      case 3: launch<32, 3, 1>(a, stream); break;
-      case 4: launch<32, 4, 1>(a, stream); break;
-      case 5: launch<32, 5, 1>(a, stream); break;
-      case 6: launch<32, 6, 1>(a, stream); break;
-      default: return TVP_ERR_SHAPE;
+  if (p.grid > 0) {
+    if (p.skinny) {
+      if (p.MT == 16) {
+        if (p.TPW == 2) launch_skinny<16, 2, 2>(a, p, stream);
+        else launch_skinny<16, 1, 3>(a, p, stream);
+      } else {
+        if (p.TPW == 2) launch_skinny<32, 2, 2>(a, p, stream);
+        else launch_skinny<32, 1, 3>(a, p, stream);
+      }
+    } else {
+      switch (p.RB) {
+        case 2: launch_wide<2>(a, p.grid, stream); break;
+        case 3: launch_wide<3>(a, p.grid, stream); break;
+        case 4: launch_wide<4>(a, p.grid, stream); break;
+        case 5: launch_wide<5>(a, p.grid, stream); break;
+        case 6: launch_wide<6>(a, p.grid, stream); break;
+        default: return TVP_ERR_SHAPE;
+      }
     }
+    TVP_LAUNCH_CHECK();
   }
-  TVP_LAUNCH_CHECK();
+  if (a.mode == TVP_EPI_ARGMAX) {
+    argmax_finalize_kernel<<<1, 256, 0, stream>>>(a.keys, a.m, a.argmax);
+    TVP_LAUNCH_CHECK();
+  }
   return TVP_OK;
 }
 
@@ -490,9 +761,9 @@ void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* 
 }
 
 int gemm_run(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
-             const tvp_gemm_epilogue* epi, uint32_t* cnt, uint32_t* cnt2, void* scratch,
+             const tvp_gemm_epilogue* epi, uint32_t* cnt, unsigned long long* keys, void* scratch,
              size_t scratch_bytes, hipStream_t stream) {
-  if (!w || !epi || !w->blob || !cnt || !cnt2) return TVP_ERR_ARG;
+  if (!w || !epi || !w->blob || !cnt || !keys) return TVP_ERR_ARG;
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
   if (w->k_in > 0 && (!x || ldx < w->k_in)) return TVP_ERR_ARG;
   if (w->k_in > 0 && (((uintptr_t)x) % 16 != 0 || ldx % 8 != 0)) return TVP_ERR_ARG;
@@ -515,12 +786,10 @@ int gemm_run(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
   a.groups = p.groups;
   a.splits = p.splits;
   a.kbs = p.kbs;
-  uint8_t* sb = (uint8_t*)scratch;
+  a.ntasks = p.ntasks;
   a.cnt = cnt;
-  a.cnt2 = cnt2;
-  a.amax_v = (float*)(sb + p.off_av);
-  a.amax_i = (int32_t*)(sb + p.off_ai);
-  a.part = (float*)(sb + p.off_part);
+  a.keys = keys;
+  a.part = (float*)scratch;
   a.mode = epi->mode;
   a.y = epi->y;
   a.ldy = epi->ldy;
@@ -563,6 +832,7 @@ int gemm_run(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
     default:
       return TVP_ERR_ARG;
   }
+  if ((size_t)p.groups > kGemmMaxGroups) return TVP_ERR_SHAPE;
   return dispatch(p, a, stream);
 }
 
@@ -570,17 +840,15 @@ int gemm_run(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
 
 using namespace tvp;
 
-// Standalone GEMM workspace: a fixed counter region (so that calls on tensors
-// of different shapes sharing one workspace never see another call's scratch
-// where their counters live), then the scratch for partial sums.
-constexpr size_t kGemmMaxGroups = 65536;
-constexpr size_t kGemmCntBytes = kGemmMaxGroups * 4;
-
-static size_t gemm_ws_layout(int64_t m, const tvp_w12_packed* w, size_t* off_cnt2, size_t* off_scr,
+// Standalone GEMM workspace: a fixed zero region (completion counters, then
+// the argmax buckets) so that calls on tensors of different shapes sharing
+// one workspace never find another call's scratch where their counters live;
+// then the scratch for partial sums.
+static size_t gemm_ws_layout(int64_t m, const tvp_w12_packed* w, size_t* off_keys, size_t* off_scr,
                              size_t* scr_bytes, int* groups) {
   gemm_requirements(m, w, groups, scr_bytes);
-  *off_cnt2 = kGemmCntBytes;
-  *off_scr = kGemmCntBytes + 256;
+  *off_keys = kGemmMaxGroups * 4;
+  *off_scr = kGemmZeroBytes;
   return *off_scr + *scr_bytes;
 }
 
@@ -597,14 +865,14 @@ int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed*
                 const tvp_gemm_epilogue* epi, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!w || !epi) return TVP_ERR_ARG;
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
-  size_t off_cnt2, off_scr, scr_bytes;
+  size_t off_keys, off_scr, scr_bytes;
   int groups;
-  const size_t need = gemm_ws_layout(m, w, &off_cnt2, &off_scr, &scr_bytes, &groups);
+  const size_t need = gemm_ws_layout(m, w, &off_keys, &off_scr, &scr_bytes, &groups);
   if ((size_t)groups > kGemmMaxGroups) return TVP_ERR_SHAPE;
   if (!ws || ws_bytes < need) return TVP_ERR_WORKSPACE;
   uint8_t* b = (uint8_t*)ws;
-  return gemm_run(x, m, ldx, w, epi, (uint32_t*)b, (uint32_t*)(b + off_cnt2), b + off_scr, scr_bytes,
-                  stream);
+  return gemm_run(x, m, ldx, w, epi, (uint32_t*)b, (unsigned long long*)(b + off_keys), b + off_scr,
+                  scr_bytes, stream);
 }
 
 int w12_gemm(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w, void* y,
