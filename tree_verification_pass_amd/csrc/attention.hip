@@ -71,7 +71,14 @@ struct AttnArgs {
   float* pl;
   int row_blocks;  // merge: 16-row blocks per (request, kv head)
   uint16_t* out;
+  int out_packed;  // out in the packed activation layout (<= 32 nodes) instead of [node][hq * D]
 };
+
+// Output element (global node, column `col` of the node's hq * D row).
+template <int D>
+__device__ inline int64_t attn_out_index(const AttnArgs& a, int node, int col) {
+  return a.out_packed ? xpack_index(node, col) : (int64_t)node * a.hq * D + col;
+}
 
 template <int D, int NT>
 __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
       kpre[it] = make_uint4(0, 0, 0, 0);
       vpre[it] = make_uint4(0, 0, 0, 0);
       if (idx < KC * CH) {
-        const int kk = sub + idx / CH, c = idx % CH;
+        const int kk = sub + idx % KC, c = idx / KC;
         if (kk < k1) {
           kpre[it] = *(const uint4*)(kbase + (int64_t)kk * D + 8 * c);
           vpre[it] = *(const uint4*)(vbase + (int64_t)kk * D + 8 * c);
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
     for (int it = 0; it < PER; ++it) {
       const int idx = tid + it * nthr;
       if (idx >= KC * CH) continue;
-      const int key = idx / CH, c = idx % CH;
+      const int key = idx % KC, c = idx / KC;
       ks[key * CH + (c ^ (key % CH))] = kpre[it];
       const uint4 vv = vpre[it];
       const uint32_t hv[8] = {vv.x & 0xFFFFu, vv.x >> 16, vv.y & 0xFFFFu, vv.y >> 16,
@@ -234,11 +241,13 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
   if (nsplit == 1) {
     if (row_ok) {
       const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-      uint16_t* op = a.out + ((int64_t)(nb + node) * a.hq + kh * a.G + gq) * D;
+      const int c0 = (kh * a.G + gq) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) op[db * 32 + 8 * (v >> 2) + 4 * h + (v & 3)] = (uint16_t)f32_to_bf16(o[db][v] * inv);
+        for (int v = 0; v < 16; ++v)
+          a.out[attn_out_index<D>(a, nb + node, c0 + db * 32 + 8 * (v >> 2) + 4 * h + (v & 3))] =
+              (uint16_t)f32_to_bf16(o[db][v] * inv);
     }
     return;
   }
@@ -264,7 +273,7 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
 // (request, kv head, 16 query rows).
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
-  __shared__ float wts[16 * 32];
+  __shared__ float wts[16 * 64];
   const int rb = blockIdx.x % a.row_blocks;
   const int kh = (blockIdx.x / a.row_blocks) % a.hkv;
   const int r = blockIdx.x / (a.row_blocks * a.hkv);
@@ -284,11 +293,11 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
     for (int sp = 0; sp < nsplit; ++sp) {
       const int64_t pr = hb + (int64_t)sp * a.rows_total + rr;
       const float w = exp2f(a.pm[pr] - bse);
-      wts[tid * 32 + sp] = w;
+      wts[tid * 64 + sp] = w;
       den += a.pl[pr] * w;
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) wts[tid * 32 + sp] *= inv;
+    for (int sp = 0; sp < nsplit; ++sp) wts[tid * 64 + sp] *= inv;
   }
   __syncthreads();
   for (int q4 = tid; q4 < nr * (D / 4); q4 += 256) {
@@ -297,14 +306,15 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
     float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int sp = 0; sp < nsplit; ++sp) {
       const float4 v = *(const float4*)&a.po[(hb + (int64_t)sp * a.rows_total + rr) * D + dd];
-      const float w = wts[lr * 32 + sp];
+      const float w = wts[lr * 64 + sp];
       acc4.x += v.x * w;
       acc4.y += v.y * w;
       acc4.z += v.z * w;
       acc4.w += v.w * w;
     }
     const int g2 = rr / n, nd = rr % n;
-    uint16_t* op = a.out + ((int64_t)(nb + nd) * a.hq + kh * a.G + g2) * D + dd;
+    // four consecutive columns stay within one 8-column group of the packed layout
+    uint16_t* op = a.out + attn_out_index<D>(a, nb + nd, (kh * a.G + g2) * D + dd);
     op[0] = (uint16_t)f32_to_bf16(acc4.x);
     op[1] = (uint16_t)f32_to_bf16(acc4.y);
     op[2] = (uint16_t)f32_to_bf16(acc4.z);
@@ -321,8 +331,8 @@ struct AttnPlan {
 // n_total: nodes of all requests.
 static AttnPlan attn_plan(int hkv, int G, int d, int r_max, int n_total, int max_keys) {
   AttnPlan p{};
-  p.kr = 512;
-  while (max_keys > 32 * p.kr) p.kr *= 2;  // at most 32 splits (merge weights live in LDS)
+  p.kr = 128;
+  while (max_keys > 64 * p.kr) p.kr *= 2;  // at most 64 splits (merge weights live in LDS)
   p.max_splits = max_keys > 0 ? (max_keys + p.kr - 1) / p.kr : 1;
   p.rows_total = G * n_total;
   p.nthreads = r_max <= 128 ? 256 : 512;
@@ -345,12 +355,12 @@ int launch_tree_prep(const int32_t* parents, const ReqInfo& ri, int32_t s_req, u
   return TVP_OK;
 }
 
-// attn_cnt: n_req * hkv counters, zero on entry, left zero.
 int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int64_t s_stride,
                           const ReqInfo& ri, int32_t s_req, const uint64_t* anc, int hq, int hkv, int d,
-                          int r_max, int max_keys, uint16_t* out, uint32_t* attn_cnt, void* scratch,
+                          int r_max, int max_keys, uint16_t* out, int out_packed, void* scratch,
                           size_t scratch_bytes, hipStream_t stream) {
   if (r_max > 256 || r_max < 1) return TVP_ERR_SHAPE;
+  if (out_packed && ri.node_ptr[ri.n_req] > 32) return TVP_ERR_SHAPE;
   const int n_req = ri.n_req;
   const AttnPlan p = attn_plan(hkv, hq / hkv, d, r_max, ri.node_ptr[n_req], max_keys);
   if (scratch_bytes < p.bytes) return TVP_ERR_WORKSPACE;
@@ -374,8 +384,8 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
   a.po = (float*)(sb + p.off_po);
   a.pm = (float*)(sb + p.off_pm);
   a.pl = (float*)(sb + p.off_pl);
-  (void)attn_cnt;
   a.out = out;
+  a.out_packed = out_packed;
   a.row_blocks = (r_max + 15) / 16;
   const dim3 grid((unsigned)(n_req * hkv * p.max_splits));
   const dim3 mgrid((unsigned)(n_req * hkv * a.row_blocks));
@@ -403,7 +413,7 @@ size_t attention_scratch_bytes(int hkv, int G, int d, int r_max, int n_total, in
 using namespace tvp;
 
 // Standalone layout of the tree_attention workspace:
-//   [0, 256)        attention counters (hkv <= 64), zero on entry, left zero
+//   [0, 256)        reserved
 //   [256, ...)      anc u64 [64], pos/slot i32 [64]
 //   then            attention partials
 static size_t ta_layout(int32_t n, int32_t hq, int32_t hkv, int32_t d, int32_t max_keys, size_t* off_part) {
@@ -439,7 +449,6 @@ int tree_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v
   const size_t need = ta_layout(n, hq, hkv, d, ctx_len + n, &offp);
   if (!ws || ws_bytes < need) return TVP_ERR_WORKSPACE;
   uint8_t* w = (uint8_t*)ws;
-  uint32_t* cnt = (uint32_t*)w;
   uint64_t* anc = (uint64_t*)(w + 256);
   int32_t* pos = (int32_t*)(w + 256 + 64 * 8);
   int32_t* slot = pos + 64;
@@ -451,7 +460,7 @@ int tree_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v
   int st = launch_tree_prep(parents, ri, 0, anc, pos, slot, status, stream);
   if (st != TVP_OK) return st;
   return launch_tree_attention(q, k_cache, v_cache, s_stride, ri, 0, anc, hq, hkv, d, (hq / hkv) * n,
-                               ctx_len + n, out, cnt, w + offp, ws_bytes - offp, stream);
+                               ctx_len + n, out, 0, w + offp, ws_bytes - offp, stream);
 }
 
 }  // extern "C"

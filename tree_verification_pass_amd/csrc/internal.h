@@ -13,10 +13,22 @@ constexpr size_t kGemmZeroBytes = 256 * 1024;
 static_assert(kGemmMaxGroups * 4 + kGemmKeyBytes <= kGemmZeroBytes, "zero region");
 
 // W12 GEMM with caller-provided counters (`cnt`, groups entries), argmax
-// buckets (`keys`) and scratch for partial sums.
-int gemm_run(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
-             const tvp_gemm_epilogue* epi, uint32_t* cnt, unsigned long long* keys, void* scratch,
+// buckets (`keys`) and scratch.  Activations come row-major in `x` or, for
+// m <= 32, already in the packed layout in `xp` (then `x` is unused).
+// `y_packed`: the SwiGLU epilogue writes its output packed (m <= 32).
+int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
+             const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, unsigned long long* keys, void* scratch,
              size_t scratch_bytes, hipStream_t stream);
+
+// Packed activation layout for up to 32 rows: 16-byte groups of 8 columns,
+// [k / 8][row (32)][k % 8].  One MFMA A-fragment load of a wavefront is then
+// 1 KB contiguous instead of 32 rows of 16 bytes.  Columns are padded to a
+// multiple of 64; rows >= m and padding columns are never used.
+__host__ __device__ inline int64_t xpack_index(int row, int64_t k) { return (k >> 3) * 256 + row * 8 + (k & 7); }
+inline int64_t xpack_elems(int64_t k_in) { return ((k_in + 63) / 64) * 2048; }
+
+// Whether gemm_run takes the skinny path (and so accepts packed input) for m rows.
+bool gemm_is_skinny(int64_t m, const tvp_w12_packed* w);
 // Counter entries and scratch bytes gemm_run needs for m rows.
 void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes);
 
@@ -24,7 +36,7 @@ int launch_tree_prep(const int32_t* parents, const ReqInfo& ri, int32_t s_req, u
                      int32_t* pos, int32_t* slot, int32_t* status, hipStream_t stream);
 int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int64_t s_stride,
                           const ReqInfo& ri, int32_t s_req, const uint64_t* anc, int hq, int hkv, int d,
-                          int r_max, int max_keys, uint16_t* out, uint32_t* attn_cnt, void* scratch,
+                          int r_max, int max_keys, uint16_t* out, int out_packed, void* scratch,
                           size_t scratch_bytes, hipStream_t stream);
 size_t attention_scratch_bytes(int hkv, int G, int d, int r_max, int n_total, int max_keys);
 

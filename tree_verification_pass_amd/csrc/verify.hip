@@ -36,15 +36,17 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 
 // y = bf16(x * (mean(x^2) + eps)^-1/2 * g), fp32 with a fixed reduction order.
 // One workgroup per row; rows of 8-element chunks (16-byte loads) when the
-// row length and pitches allow it, element by element otherwise.
+// row length and pitches allow it, element by element otherwise.  With
+// `packed` (at most 32 rows) y is written in the GEMM's packed activation
+// layout and ldy is unused.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x, int ldx,
                                                       const uint16_t* __restrict__ g, int hidden,
-                                                      float eps, uint16_t* __restrict__ y, int ldy) {
+                                                      float eps, uint16_t* __restrict__ y, int ldy, int packed) {
   __shared__ float ws[4];
   const int i = blockIdx.x, tid = threadIdx.x;
   const uint16_t* xr = x + (int64_t)i * ldx;
   uint16_t* yr = y + (int64_t)i * ldy;
-  const bool vec = (hidden % 8) == 0 && (ldx % 8) == 0 && (ldy % 8) == 0;
+  const bool vec = (hidden % 8) == 0 && (ldx % 8) == 0 && (packed || (ldy % 8) == 0);
   float ss = 0.0f;
   if (vec) {
     const int nc = hidden / 8;
@@ -81,11 +83,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
         const uint32_t hi = f32_to_bf16(bf16_to_f32(w[e] >> 16) * r * bf16_to_f32(gw[e] >> 16));
         o[e] = lo | (hi << 16);
       }
-      *(uint4*)(yr + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+      *(uint4*)(packed ? y + xpack_index(i, 8 * c) : yr + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   } else {
     for (int k = tid; k < hidden; k += 256)
-      yr[k] = (uint16_t)f32_to_bf16(bf16_to_f32(xr[k]) * r * bf16_to_f32(g[k]));
+      (packed ? y[xpack_index(i, k)] : yr[k]) = (uint16_t)f32_to_bf16(bf16_to_f32(xr[k]) * r * bf16_to_f32(g[k]));
   }
 }
 
@@ -190,8 +192,9 @@ struct tvp_plan {
   std::vector<tvp_layer> layers;
   int32_t max_nodes;
   int ld_h, ld_q, ld_u;
+  bool pack_ok;  // every GEMM takes the skinny path at <= 32 rows
   // workspace layout
-  size_t off_gcnt, off_gkeys, off_acnt, zero_end;
+  size_t off_gcnt, off_gkeys, zero_end;
   size_t off_h, off_a, off_q, off_o, off_u;
   size_t off_anc, off_pos, off_slot, off_tstat, off_bad;
   size_t off_gscr, gscr_bytes;
@@ -242,6 +245,7 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   p->ld_h = (int)align_up(H, 8);
   p->ld_q = (int)align_up((size_t)hq * hd, 8);
   p->ld_u = (int)align_up(F, 8);
+  const int mn = max_nodes;
   // counters and scratch over every GEMM at every row count up to max_nodes
   int gmax = 1;
   size_t gscr = 256;
@@ -255,31 +259,35 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
     }
   };
   need(d->lm_head);
+  p->pack_ok = gemm_is_skinny(32, &d->lm_head);
   for (int l = 0; l < d->n_layers; ++l) {
     need(p->layers[l].wqkv);
     need(p->layers[l].wo);
     need(p->layers[l].wgu);
     need(p->layers[l].wdown);
+    p->pack_ok = p->pack_ok && gemm_is_skinny(32, &p->layers[l].wqkv) && gemm_is_skinny(32, &p->layers[l].wo) &&
+                 gemm_is_skinny(32, &p->layers[l].wgu) && gemm_is_skinny(32, &p->layers[l].wdown);
   }
-  const int mn = max_nodes;
+  // activation buffers hold either layout: row-major [mn][ld] or packed
+  auto act_bytes = [&](int ld, int64_t k) {
+    return std::max((size_t)mn * ld * 2, (size_t)xpack_elems(k) * 2);
+  };
   size_t off = 0;
   p->off_gcnt = off;
   off = align_up(off + (size_t)gmax * 4, 256);
   p->off_gkeys = off;
   off = align_up(off + kGemmKeyBytes, 256);
-  p->off_acnt = off;
-  off = align_up(off + (size_t)kMaxReq * hkv * 4, 256);
   p->zero_end = off;
   p->off_h = off;
   off = align_up(off + (size_t)mn * p->ld_h * 2, 256);
   p->off_a = off;
-  off = align_up(off + (size_t)mn * p->ld_h * 2, 256);
+  off = align_up(off + act_bytes(p->ld_h, H), 256);
   p->off_q = off;
   off = align_up(off + (size_t)mn * p->ld_q * 2, 256);
   p->off_o = off;
-  off = align_up(off + (size_t)mn * p->ld_q * 2, 256);
+  off = align_up(off + act_bytes(p->ld_q, (int64_t)hq * hd), 256);
   p->off_u = off;
-  off = align_up(off + (size_t)mn * p->ld_u * 2, 256);
+  off = align_up(off + act_bytes(p->ld_u, F), 256);
   p->off_anc = off;
   off = align_up(off + (size_t)mn * 8, 256);
   p->off_pos = off;
@@ -315,6 +323,8 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   const int hq = d.n_heads, hkv = d.n_kv_heads, hd = d.head_dim, H = d.hidden, F = d.ffn;
   const int G = hq / hkv;
   const int n_total = ri.node_ptr[ri.n_req];
+  // up to 32 nodes: GEMM inputs (a, o, u) are produced in the packed layout
+  const int pk = (n_total <= 32 && p->pack_ok) ? 1 : 0;
   int max_n = 0, max_keys = 0;
   for (int r = 0; r < ri.n_req; ++r) {
     const int n = ri.node_ptr[r + 1] - ri.node_ptr[r];
@@ -324,7 +334,6 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   uint8_t* w = (uint8_t*)ws;
   uint32_t* gcnt = (uint32_t*)(w + p->off_gcnt);
   unsigned long long* gkeys = (unsigned long long*)(w + p->off_gkeys);
-  uint32_t* acnt = (uint32_t*)(w + p->off_acnt);
   uint16_t* h = (uint16_t*)(w + p->off_h);
   uint16_t* a = (uint16_t*)(w + p->off_a);
   uint16_t* q = (uint16_t*)(w + p->off_q);
@@ -344,7 +353,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   TVP_LAUNCH_CHECK();
   for (int l = 0; l < d.n_layers; ++l) {
     const tvp_layer& L = p->layers[l];
-    rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, L.attn_norm, H, d.norm_eps, a, p->ld_h);
+    rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, L.attn_norm, H, d.norm_eps, a, p->ld_h, pk);
     TVP_LAUNCH_CHECK();
     tvp_gemm_epilogue e{};
     e.mode = TVP_EPI_QKV;
@@ -356,9 +365,11 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     e.v_cache = L.v_cache;
     e.s_stride = d.s_max;
     e.rope_theta = d.rope_theta;
-    if ((st = gemm_run(a, n_total, p->ld_h, &L.wqkv, &e, gcnt, gkeys, gscr, p->gscr_bytes, stream))) return st;
+    if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wqkv, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes,
+                       stream)))
+      return st;
     if ((st = launch_tree_attention(q, L.k_cache, L.v_cache, d.s_max, ri, s_req, anc, hq, hkv, hd, G * max_n,
-                                    max_keys, o, acnt, ascr, p->ascr_bytes, stream)))
+                                    max_keys, o, pk, ascr, p->ascr_bytes, stream)))
       return st;
     e = tvp_gemm_epilogue{};
     e.mode = TVP_EPI_RESID;
@@ -366,30 +377,38 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     e.ldy = p->ld_h;
     e.resid = h;
     e.ldr = p->ld_h;
-    if ((st = gemm_run(o, n_total, p->ld_q, &L.wo, &e, gcnt, gkeys, gscr, p->gscr_bytes, stream))) return st;
-    rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, L.ffn_norm, H, d.norm_eps, a, p->ld_h);
+    if ((st = gemm_run(o, pk ? o : nullptr, n_total, p->ld_q, &L.wo, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes,
+                       stream)))
+      return st;
+    rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, L.ffn_norm, H, d.norm_eps, a, p->ld_h, pk);
     TVP_LAUNCH_CHECK();
     e = tvp_gemm_epilogue{};
     e.mode = TVP_EPI_SWIGLU;
     e.y = u;
     e.ldy = p->ld_u;
-    if ((st = gemm_run(a, n_total, p->ld_h, &L.wgu, &e, gcnt, gkeys, gscr, p->gscr_bytes, stream))) return st;
+    if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wgu, &e, pk, gcnt, gkeys, gscr, p->gscr_bytes,
+                       stream)))
+      return st;
     e = tvp_gemm_epilogue{};
     e.mode = TVP_EPI_RESID;
     e.y = h;
     e.ldy = p->ld_h;
     e.resid = h;
     e.ldr = p->ld_h;
-    if ((st = gemm_run(u, n_total, p->ld_u, &L.wdown, &e, gcnt, gkeys, gscr, p->gscr_bytes, stream))) return st;
+    if ((st = gemm_run(u, pk ? u : nullptr, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes,
+                       stream)))
+      return st;
   }
-  rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, d.final_norm, H, d.norm_eps, a, p->ld_h);
+  rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, d.final_norm, H, d.norm_eps, a, p->ld_h, pk);
   TVP_LAUNCH_CHECK();
   tvp_gemm_epilogue e{};
   e.mode = TVP_EPI_ARGMAX;
   e.argmax = out->argmax;
   e.logits = out->logits;
   e.ldl = d.vocab;
-  if ((st = gemm_run(a, n_total, p->ld_h, &d.lm_head, &e, gcnt, gkeys, gscr, p->gscr_bytes, stream))) return st;
+  if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &d.lm_head, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes,
+                     stream)))
+    return st;
   accept_kernel<<<dim3(ri.n_req), dim3(64), 0, stream>>>(out->argmax, tokens, parents, ri, bad, out->path,
                                                          out->n_accepted, out->bonus, out->status);
   TVP_LAUNCH_CHECK();

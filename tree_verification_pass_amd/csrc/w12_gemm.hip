@@ -29,7 +29,8 @@
 namespace tvp {
 
 struct GemmArgs {
-  const uint16_t* x;
+  const uint16_t* x;   // row-major activations (wide kernel)
+  const uint16_t* xp;  // packed activations (skinny kernel): element (row, k) at (k/8)*256 + row*8 + k%8
   int64_t ldx;
   int m, k_in;
   const uint8_t* rec;
@@ -57,9 +58,25 @@ struct GemmArgs {
   int32_t* argmax;
   float* logits;
   int64_t ldl;
+  int y_packed;  // SWIGLU: write y in the packed activation layout (rows <= 32)
 };
 
 constexpr int kArgmaxBuckets = 64;
+
+// Row-major x [m][ldx] -> packed (rows >= m and columns >= k_in are zero).
+__global__ __launch_bounds__(256) void pack_x_kernel(const uint16_t* __restrict__ x, int64_t ldx, int m,
+                                                     int k_in, int nchunks, uint16_t* __restrict__ xp) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over nchunks * 32
+  if (idx >= (int64_t)nchunks * 32) return;
+  const int row = (int)(idx & 31);
+  const int64_t c = idx >> 5;
+  const int64_t k = c * 8;
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = (row < m && k + e < k_in) ? x[row * ldx + k + e] : 0u;
+  *(uint4*)(xp + c * 256 + row * 8) =
+      make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
 
 __device__ inline uint32_t rotl32(uint32_t x, int r) { return r == 0 ? x : (x << r) | (x >> (32 - r)); }
 
@@ -126,7 +143,9 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
       const int32_t r = a.rowmap[col];
       if (r < 0) continue;
       const float gv = V(row, col), uv = V(row, col + 16);
-      ((uint16_t*)a.y)[row * a.ldy + r] = (uint16_t)f32_to_bf16(silu_f32(gv) * uv);
+      const uint16_t o = (uint16_t)f32_to_bf16(silu_f32(gv) * uv);
+      if (a.y_packed) ((uint16_t*)a.y)[xpack_index(row, r)] = o;
+      else ((uint16_t*)a.y)[row * a.ldy + r] = o;
     }
   } else if constexpr (MODE == TVP_EPI_QKV) {
     const int d = a.d, tph = d / 32;
@@ -245,10 +264,11 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < NACC; ++v) acc[t][ch][v] = 0.0f;
 
+  // activation fragments from the packed layout: rows past m hold zeros or
+  // garbage and only feed output rows that are never stored
   const int xrow = MT == 32 ? (lane & 31) : (lane & 15);
   const int xsub = MT == 32 ? 8 * (lane >> 5) : 8 * (lane >> 4);
-  const bool xrow_ok = xrow < a.m;
-  const uint16_t* xr = a.x + (int64_t)min(xrow, a.m - 1) * a.ldx;
+  const uint16_t* xr = a.xp + xrow * 8;
   // the last block of a ragged K range is handled on its own, with guards
   const bool ragged_tail = nblk > 0 && kb1 == a.n_kb && (a.k_in & 63) != 0;
   const int nfast = nblk - (ragged_tail ? 1 : 0);
@@ -283,8 +303,7 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int64_t k = 64LL * j + (MT == 32 ? 16 : 32) * ks + xsub;
-      // rows past m repeat row m-1; their outputs are never stored
-      A[slot][ks] = *(const uint4*)(xr + k);
+      A[slot][ks] = *(const uint4*)(xr + (k >> 3) * 256);
     }
   };
   auto issue_tail = [&](int i, int slot) {
@@ -295,7 +314,7 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
       const int64_t k = 64LL * j + (MT == 32 ? 16 : 32) * ks + xsub;
       uint32_t h[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = (xrow_ok && k + e < a.k_in) ? xr[k + e] : 0u;
+      for (int e = 0; e < 8; ++e) h[e] = (k + e < a.k_in) ? xr[(k >> 3) * 256 + e] : 0u;
       A[slot][ks] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
     }
   };
@@ -665,6 +684,24 @@ struct GemmPlan {
 // one VGPR).  Wide (m > 32, or K too long for 8 waves of 63 blocks):
 // workgroups of 4 tiles sharing X through LDS, split K over workgroups.
 constexpr int kWideTargetGroups = 1024;
+#ifndef TVP_TPW2_MIN_TILES
+#define TVP_TPW2_MIN_TILES 1024  // tiles from which a workgroup takes two tiles
+#endif
+#ifndef TVP_KW_FEW
+#define TVP_KW_FEW 4  // waves per workgroup when workgroups are few
+#endif
+#ifndef TVP_KW_MANY
+#define TVP_KW_MANY 4  // ... and when they are many
+#endif
+#ifndef TVP_KW_SWITCH
+#define TVP_KW_SWITCH 512  // workgroup count that separates few from many
+#endif
+#ifndef TVP_RD1
+#define TVP_RD1 3  // register-ring depth, one tile per workgroup
+#endif
+#ifndef TVP_RD2
+#define TVP_RD2 2  // register-ring depth, two tiles per workgroup
+#endif
 
 static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w) {
   GemmPlan p{};
@@ -674,11 +711,11 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w) {
   p.RB = (int)ceil_div(m, p.MT);
   p.skinny = m <= 32 && nkb <= 8 * 63;
   if (p.skinny) {
-    p.TPW = w->n_tiles >= 1024 ? 2 : 1;
-    p.RD = p.TPW == 2 ? 2 : 3;
+    p.TPW = w->n_tiles >= TVP_TPW2_MIN_TILES ? 2 : 1;
+    p.RD = p.TPW == 2 ? TVP_RD2 : TVP_RD1;
     p.TG = p.TPW;
     p.groups = (int)ceil_div(w->n_tiles, p.TPW);
-    p.KW = p.groups >= 512 ? 4 : 8;
+    p.KW = p.groups >= TVP_KW_SWITCH ? TVP_KW_MANY : TVP_KW_FEW;
     if (nkb > 4 * 63) p.KW = 8;
     p.KW = std::max(1, std::min(p.KW, nkb));
     p.kbs = nkb > 0 ? (int)ceil_div(nkb, p.KW) : 0;
@@ -702,7 +739,9 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w) {
     p.ntasks = p.groups * p.splits;
     p.grid = p.ntasks;
   }
-  p.scratch_bytes = p.skinny ? 256 : align_up((size_t)p.splits * m * n_pad * 4, 256);
+  // skinny: room to pack row-major activations; wide: split-K partial sums
+  p.scratch_bytes = p.skinny ? align_up((size_t)std::max(nkb, 1) * 4096, 256)
+                             : align_up((size_t)p.splits * m * n_pad * 4, 256);
   return p;
 }
 
@@ -729,11 +768,11 @@ static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   if (p.grid > 0) {
     if (p.skinny) {
       if (p.MT == 16) {
-        if (p.TPW == 2) launch_skinny<16, 2, 2>(a, p, stream);
-        else launch_skinny<16, 1, 3>(a, p, stream);
+        if (p.TPW == 2) launch_skinny<16, 2, TVP_RD2>(a, p, stream);
+        else launch_skinny<16, 1, TVP_RD1>(a, p, stream);
       } else {
-        if (p.TPW == 2) launch_skinny<32, 2, 2>(a, p, stream);
-        else launch_skinny<32, 1, 3>(a, p, stream);
+        if (p.TPW == 2) launch_skinny<32, 2, TVP_RD2>(a, p, stream);
+        else launch_skinny<32, 1, TVP_RD1>(a, p, stream);
       }
     } else {
       switch (p.RB) {
@@ -754,24 +793,41 @@ static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   return TVP_OK;
 }
 
+bool gemm_is_skinny(int64_t m, const tvp_w12_packed* w) { return make_plan(m, w).skinny; }
+
 void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes) {
   const GemmPlan p = make_plan(m, w);
   *groups = p.groups;
   *scratch_bytes = p.scratch_bytes;
 }
 
-int gemm_run(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
-             const tvp_gemm_epilogue* epi, uint32_t* cnt, unsigned long long* keys, void* scratch,
+int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
+             const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, unsigned long long* keys, void* scratch,
              size_t scratch_bytes, hipStream_t stream) {
   if (!w || !epi || !w->blob || !cnt || !keys) return TVP_ERR_ARG;
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
-  if (w->k_in > 0 && (!x || ldx < w->k_in)) return TVP_ERR_ARG;
-  if (w->k_in > 0 && (((uintptr_t)x) % 16 != 0 || ldx % 8 != 0)) return TVP_ERR_ARG;
   const GemmPlan p = make_plan(m, w);
+  if (xp) {
+    if (!p.skinny || ((uintptr_t)xp) % 16 != 0) return TVP_ERR_ARG;
+  } else if (w->k_in > 0) {
+    if (!x || ldx < w->k_in) return TVP_ERR_ARG;
+    if (((uintptr_t)x) % 16 != 0 || ldx % 8 != 0) return TVP_ERR_ARG;
+  }
+  if (y_packed && (m > 32 || epi->mode != TVP_EPI_SWIGLU)) return TVP_ERR_ARG;
   if (!scratch || scratch_bytes < p.scratch_bytes) return TVP_ERR_WORKSPACE;
   GemmArgs a{};
   const uint8_t* blob = (const uint8_t*)w->blob;
+  if (p.skinny && !xp) {  // pack the row-major activations into the scratch
+    uint16_t* dst = (uint16_t*)scratch;
+    const int nchunks = std::max(w->n_kb, 1) * 8;
+    pack_x_kernel<<<dim3((unsigned)ceil_div((int64_t)nchunks * 32, 256)), dim3(256), 0, stream>>>(
+        x, ldx, (int)m, (int)w->k_in, nchunks, dst);
+    TVP_LAUNCH_CHECK();
+    xp = dst;
+  }
   a.x = x;
+  a.xp = xp;
+  a.y_packed = y_packed;
   a.ldx = ldx;
   a.m = (int)m;
   a.k_in = (int)w->k_in;
@@ -871,8 +927,8 @@ int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed*
   if ((size_t)groups > kGemmMaxGroups) return TVP_ERR_SHAPE;
   if (!ws || ws_bytes < need) return TVP_ERR_WORKSPACE;
   uint8_t* b = (uint8_t*)ws;
-  return gemm_run(x, m, ldx, w, epi, (uint32_t*)b, (unsigned long long*)(b + off_keys), b + off_scr,
-                  scr_bytes, stream);
+  return gemm_run(x, nullptr, m, ldx, w, epi, 0, (uint32_t*)b, (unsigned long long*)(b + off_keys),
+                  b + off_scr, scr_bytes, stream);
 }
 
 int w12_gemm(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w, void* y,
