@@ -111,16 +111,19 @@ def time_gateup(dm, cfg, iters: int):
     dev = torch.device("cuda:0")
     n, H, F = cfg.n_nodes, cfg.hidden, cfg.ffn
     x = torch.randn(n, H, device=dev).to(torch.bfloat16)
-    u = torch.empty(n, F, dtype=torch.bfloat16, device=dev)
-    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=u.data_ptr(), ldy=F)
+    # the launch configuration of the verification pass: packed activations in and out
+    xp = tvp.w12_pack_x(x)
+    u = torch.empty(tvp.w12_packed_x_elems(F), dtype=torch.bfloat16, device=dev)
+    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=u.data_ptr(), y_packed=1)
     layers = dm.layers
     for i in range(len(layers)):
-        tvp.w12_gemm_ex(x, layers[i].wgu, epi)
+        tvp.w12_gemm_px(xp, n, layers[i].wgu, epi)
     torch.cuda.synchronize()
+    # the library launches on torch's current stream, where these events are recorded
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for i in range(iters):
-        tvp.w12_gemm_ex(x, layers[i % len(layers)].wgu, epi)
+        tvp.w12_gemm_px(xp, n, layers[i % len(layers)].wgu, epi)
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / iters
@@ -169,6 +172,37 @@ def cpu_baseline(dm, cfg, seed: int, tree):
                        f"weights ({cfg.streamed_params() / w_layer:.2f}x) to a whole step of {est:.1f} s")}
 
 
+def rocprof_summary(out_dir: str, top: int = 24) -> None:
+    """Prints the short text summary of a rocprofv3 csv output folder: the
+    per-kernel duration table of ``--kernel-trace --stats`` runs and, for
+    ``--pmc`` runs, each kernel's counters summed over their instances and
+    averaged over its dispatches."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    for path in sorted(glob.glob(os.path.join(out_dir, "**", "*_kernel_stats.csv"), recursive=True)):
+        rows = list(csv.DictReader(open(path)))
+        print(f"kernel stats ({os.path.basename(path)}): calls, total us, avg us, min us, max us, %, name")
+        for r in rows[:top]:
+            print(f"{int(r['Calls']):7d} {float(r['TotalDurationNs']) / 1e3:12.1f} {float(r['AverageNs']) / 1e3:9.2f} "
+                  f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}  "
+                  f"{r['Name'][:110]}")
+    for path in sorted(glob.glob(os.path.join(out_dir, "**", "*_counter_collection.csv"), recursive=True)):
+        per = defaultdict(float)
+        names = {}
+        for r in csv.DictReader(open(path)):
+            key = (r["Kernel_Name"], r["Counter_Name"], r["Dispatch_Id"])
+            per[key] += float(r["Counter_Value"])
+            names[key[:2]] = r["Grid_Size"]
+        agg = defaultdict(list)
+        for (kn, cn, _), v in per.items():
+            agg[(kn, cn)].append(v)
+        print(f"counters ({os.path.basename(path)}): dispatches, mean per dispatch, min, max, counter, kernel")
+        for (kn, cn), vals in sorted(agg.items(), key=lambda kv: -sum(kv[1]))[:top]:
+            print(f"{len(vals):7d} {sum(vals) / len(vals):14.1f} {min(vals):14.1f} {max(vals):14.1f}  {cn}  {kn[:100]}")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,13 +213,31 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--gemm-iters", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run three plain device copies of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--rocprof-summary", metavar="DIR", default="",
+                    help="only print the summary of a rocprofv3 csv output folder (no GPU use)")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
+        return 0
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: the verification pass runs on one GPU "
               f"(one GPU's weights and KV cache, no collectives); run with --gpus 1", flush=True)
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        # an elementwise kernel that reads nb bytes and writes nb bytes
+        nb = args.copy_calibration << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"bench: negated-copied {nb} bytes 3 times")
+        return 0
 
     import tree_verification_pass_amd as tvp
     from synth.configs import CONFIGS

@@ -172,10 +172,25 @@ typedef struct tvp_gemm_epilogue {
   int32_t* argmax;         /* ARGMAX: device int32 [m] */
   float* logits;           /* ARGMAX: optional device fp32 [m][ldl] (NULL = none) */
   int64_t ldl;
+  int32_t x_packed;        /* x is in the packed activation layout (ldx unused) */
+  int32_t y_packed;        /* SWIGLU: y is written in the packed layout (ldy unused) */
 } tvp_gemm_epilogue;
 
+/* x_packed and y_packed need m <= 32 and every k_in <= 32256 (the
+ * single-pass path); otherwise TVP_ERR_ARG. */
 int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
                 const tvp_gemm_epilogue* epi, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Packed activation layout, the GEMM's input format for up to 32 rows (and
+ * what verify_step produces internally): bf16 element (row, k) lives at
+ * (k/8)*256 + row*8 + k%8, so a wavefront's MFMA A-fragment of 32 rows x 8
+ * columns is 512 contiguous bytes.  k is padded to a multiple of 64:
+ * w12_packed_x_elems(k_in) elements.  w12_pack_x converts row-major
+ * x (device bf16 [m][ldx], ldx >= k_in) into xp (device, 16-byte aligned,
+ * caller-owned), zero-filling rows m..31 and the padding columns.
+ * 1 <= m <= 32, k_in >= 0; TVP_ERR_SHAPE / TVP_ERR_ARG otherwise. */
+int64_t w12_packed_x_elems(int64_t k_in);
+int w12_pack_x(const uint16_t* x, int64_t m, int64_t ldx, int64_t k_in, uint16_t* xp, hipStream_t stream);
 
 /* ------------------------------------------------------- tree attention
  * Attention of n draft-tree nodes over a committed context and their own

@@ -54,3 +54,11 @@ def test_pack_size_layout_host_only():
         tvp.w12_pack_size(100, 70000, 0)
     with pytest.raises(tvp.TvpError):
         tvp.w12_pack_size(2 * 1000, 512, 0, tvp.TVP_CHAN_GATEUP, 999)
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_packed_activation_size_host_only():
+    import tree_verification_pass_amd as tvp
+    # 32 row slots x k padded to a multiple of 64
+    for k, want in ((0, 0), (1, 2048), (64, 2048), (65, 4096), (5120, 80 * 2048), (17408, 272 * 2048)):
+        assert tvp.w12_packed_x_elems(k) == want

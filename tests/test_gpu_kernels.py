@@ -301,6 +301,56 @@ def test_accept_path_exact(tvp, cuda):
         assert int(st.item()) == tvp.TVP_ERR_TREE and int(na.item()) == 0
 
 
+def _packed_layout_host(x_bits: np.ndarray, k_pad: int) -> np.ndarray:
+    """The packed activation layout written out element by element: (row, k)
+    at (k // 8) * 256 + row * 8 + k % 8, 32 row slots, zeros elsewhere."""
+    m, k_in = x_bits.shape
+    out = np.zeros(k_pad * 32, np.uint16)
+    for r in range(m):
+        for k in range(k_in):
+            out[(k // 8) * 256 + r * 8 + k % 8] = x_bits[r, k]
+    return out
+
+
+@pytest.mark.parametrize("m,k_in", [(1, 1000), (13, 1000), (17, 64), (32, 200)])
+def test_packed_activation_layout(tvp, cuda, m, k_in):
+    """w12_pack_x against the layout written out on the host, then the GEMM on
+    packed input equals the GEMM on row-major input bit for bit (and the
+    oracle within the GEMM bound), including the packed SwiGLU output."""
+    print(f"[packed x] m={m} k_in={k_in}", flush=True)
+    k_pad = -(-k_in // 64) * 64
+    assert tvp.w12_packed_x_elems(k_in) == k_pad * 32
+    x = _x(m, k_in, 300 + m, cuda)
+    xp = tvp.w12_pack_x(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u16(xp), _packed_layout_host(_u16(x), k_pad))
+    w_bits = bf16_bits_numpy(gen_linear_bf16(make_generator(9), 96, k_in, TINY_RECIPE))
+    pw = _packed(tvp, w_bits, cuda)
+    y_row = tvp.w12_gemm(x, pw, out_fp32=True)
+    y_pk = torch.zeros_like(y_row)
+    tvp.w12_gemm_px(xp, m, pw, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_F32, y=y_pk.data_ptr(), ldy=96))
+    torch.cuda.synchronize()
+    assert torch.equal(y_row, y_pk)
+    _check_gemm(y_pk.cpu().numpy().astype(np.float64), _u16(x), w_bits)
+    # SwiGLU written packed, read back through the host layout
+    F = 80
+    w_gu = bf16_bits_numpy(gen_linear_bf16(make_generator(10), 2 * F, k_in, TINY_RECIPE))
+    pgu = _packed(tvp, w_gu, cuda, tvp.TVP_CHAN_GATEUP, F)
+    u_row = torch.zeros(m, F, dtype=torch.bfloat16, device=cuda)
+    tvp.w12_gemm_ex(x, pgu, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=u_row.data_ptr(), ldy=F))
+    u_pk = torch.full((tvp.w12_packed_x_elems(F),), 7.0, dtype=torch.bfloat16, device=cuda)
+    tvp.w12_gemm_px(xp, m, pgu, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=u_pk.data_ptr(), y_packed=1))
+    torch.cuda.synchronize()
+    got = _u16(u_pk)
+    want = _u16(u_row)
+    for r in range(m):
+        for k in range(F):
+            assert got[(k // 8) * 256 + r * 8 + k % 8] == want[r, k], (r, k)
+    gu = from_bits(_u16(x)) @ from_bits(w_gu).T
+    ref = round_bf16(om.silu(gu[:, :F]) * gu[:, F:])
+    assert np.all(np.abs(from_bits(want) - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+
+
 def test_host_validation_launches_nothing(tvp, cuda):
     pw = _packed(tvp, bf16_bits_numpy(gen_linear_bf16(make_generator(1), 64, 64, TINY_RECIPE)), cuda)
     with pytest.raises(tvp.TvpError) as e:
@@ -312,4 +362,16 @@ def test_host_validation_launches_nothing(tvp, cuda):
     with pytest.raises(tvp.TvpError) as e:  # SwiGLU needs the gate/up channel map
         y = torch.zeros(4, 64, dtype=torch.bfloat16, device=cuda)
         tvp.w12_gemm_ex(_x(4, 64, 1, cuda), pw, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=y.data_ptr(), ldy=64))
+    assert e.value.status == tvp.TVP_ERR_ARG
+    # packed layouts: at most 32 rows, packed output only for SwiGLU
+    with pytest.raises(tvp.TvpError) as e:
+        tvp.w12_pack_x(_x(33, 64, 1, cuda))
+    assert e.value.status == tvp.TVP_ERR_SHAPE
+    xp = tvp.w12_pack_x(_x(4, 64, 1, cuda))
+    y = torch.zeros(33, 64, dtype=torch.float32, device=cuda)
+    with pytest.raises(tvp.TvpError) as e:
+        tvp.w12_gemm_px(xp, 33, pw, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_F32, y=y.data_ptr(), ldy=64))
+    assert e.value.status == tvp.TVP_ERR_ARG
+    with pytest.raises(tvp.TvpError) as e:
+        tvp.w12_gemm_px(xp, 4, pw, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_F32, y=y.data_ptr(), ldy=64, y_packed=1))
     assert e.value.status == tvp.TVP_ERR_ARG

@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtvp.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tree_verification_pass_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python tree_verification_pass_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ----------------------------------------------------------------- constants
@@ -56,7 +56,8 @@ class TvpW12Packed(ctypes.Structure):
 class TvpGemmEpilogue(ctypes.Structure):
     _fields_ = [("mode", c_i32), ("y", c_vp), ("ldy", c_i64), ("resid", c_vp), ("ldr", c_i64),
                 ("pos", c_vp), ("slot", c_vp), ("k_cache", c_vp), ("v_cache", c_vp), ("s_stride", c_i64),
-                ("rope_theta", ctypes.c_double), ("argmax", c_vp), ("logits", c_vp), ("ldl", c_i64)]
+                ("rope_theta", ctypes.c_double), ("argmax", c_vp), ("logits", c_vp), ("ldl", c_i64),
+                ("x_packed", c_i32), ("y_packed", c_i32)]
 
 
 class TvpLayer(ctypes.Structure):
@@ -101,6 +102,8 @@ _lib_w12_gemm = _sig("w12_gemm", ctypes.c_int,
 _lib_w12_gemm_ex = _sig("w12_gemm_ex", ctypes.c_int,
                         [c_vp, c_i64, c_i64, ctypes.POINTER(TvpW12Packed), ctypes.POINTER(TvpGemmEpilogue),
                          c_vp, c_sz, c_vp])
+_lib_w12_packed_x_elems = _sig("w12_packed_x_elems", c_i64, [c_i64])
+_lib_w12_pack_x = _sig("w12_pack_x", ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp])
 _lib_tree_attention_workspace = _sig("tree_attention_workspace", c_sz, [c_i32, c_i32, c_i32, c_i32])
 _lib_tree_attention = _sig("tree_attention", ctypes.c_int,
                            [c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
@@ -118,6 +121,7 @@ _lib_verify_step_batched = _sig("verify_step_batched", ctypes.c_int,
 
 EXPORTED = ("tvp_status_string", "w12_encode_count", "w12_encode", "w12_decode", "w12_pack_size",
             "w12_pack_workspace", "w12_pack", "w12_gemm_workspace", "w12_gemm", "w12_gemm_ex",
+            "w12_packed_x_elems", "w12_pack_x",
             "tree_attention_workspace", "tree_attention", "accept_path", "tvp_plan_create",
             "tvp_plan_destroy", "verify_step_workspace", "verify_step", "verify_step_batched")
 
@@ -295,6 +299,31 @@ def w12_gemm_ex(x: torch.Tensor, w: PackedW12, epi: TvpGemmEpilogue) -> None:
     ws = _ws_gemm.get(need, x.device)
     _check(_lib_w12_gemm_ex(_ptr(x), m, x.stride(0), ctypes.byref(w.desc), ctypes.byref(epi), _ptr(ws),
                             ws.numel(), _stream(x.device)), "w12_gemm_ex")
+
+
+def w12_packed_x_elems(k_in: int) -> int:
+    return int(_lib_w12_packed_x_elems(int(k_in)))
+
+
+def w12_pack_x(x: torch.Tensor, k_in: int | None = None) -> torch.Tensor:
+    """Row-major bf16 ``x [m, >= k_in]`` (m <= 32) -> the GEMM's packed
+    activation layout, a flat bf16 tensor of ``w12_packed_x_elems(k_in)``."""
+    _dev_check(x)
+    m = x.shape[0]
+    k_in = x.shape[1] if k_in is None else int(k_in)
+    xp = torch.empty(max(w12_packed_x_elems(k_in), 8), dtype=torch.bfloat16, device=x.device)
+    _check(_lib_w12_pack_x(_ptr(x), m, x.stride(0), k_in, _ptr(xp), _stream(x.device)), "w12_pack_x")
+    return xp
+
+
+def w12_gemm_px(xp: torch.Tensor, m: int, w: PackedW12, epi: TvpGemmEpilogue) -> None:
+    """The GEMM on packed activations (``epi.x_packed`` is set here)."""
+    _dev_check(xp)
+    epi.x_packed = 1
+    need = w12_gemm_workspace(m, w)
+    ws = _ws_gemm.get(need, xp.device)
+    _check(_lib_w12_gemm_ex(_ptr(xp), m, 0, ctypes.byref(w.desc), ctypes.byref(epi), _ptr(ws), ws.numel(),
+                            _stream(xp.device)), "w12_gemm_ex")
 
 
 # --------------------------------------------------------------- attention

@@ -1,6 +1,7 @@
 """Builds ``libtvp.so`` (the C-ABI library) from ``csrc/*.hip`` for gfx950 with hipcc.
 
-Usage: ``python -m tree_verification_pass_amd.build`` (or ``build()`` from Python).
+Usage: ``python tree_verification_pass_amd/build.py`` (or ``build()`` from Python; run
+by path, since importing the package needs the library).
 Objects are compiled in parallel into ``_build/`` next to this file and linked
 in-tree, so the library travels with the source tree.
 """

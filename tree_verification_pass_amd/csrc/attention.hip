@@ -268,49 +268,81 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge of the key splits, in split order (a separate launch: the kernel
-// boundary makes every split's partials visible).  One workgroup per
-// (request, kv head, 16 query rows).
+// Merge of the key splits (a separate launch: the kernel boundary makes every
+// split's partials visible).  One workgroup per (request, kv head, 16 query
+// rows); each row's split weights are formed by 16 lanes with a fixed
+// shuffle-tree order, then every output element sums its splits in split
+// order, so the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
-  __shared__ float wts[16 * 64];
+  __shared__ float wts[16 * 64];  // [row][split], normalised merge weights
   const int rb = blockIdx.x % a.row_blocks;
   const int kh = (blockIdx.x / a.row_blocks) % a.hkv;
   const int r = blockIdx.x / (a.row_blocks * a.hkv);
   const int L = a.ri.ctx_len[r], nb = a.ri.node_ptr[r], n = a.ri.node_ptr[r + 1] - nb;
   const int R = a.G * n;
-  const int nsplit = (L + n + a.kr - 1) / a.kr;
+  const int nsplit = (L + n + a.kr - 1) / a.kr;  // <= 64
   if (nsplit <= 1 || rb * 16 >= R) return;
   const int tid = threadIdx.x;
   const int64_t hb = (int64_t)kh * a.max_splits * a.rows_total + (int64_t)a.G * nb;
   const int r0 = rb * 16, nr = min(16, R - r0);
-  if (tid < nr) {
-    const int rr = r0 + tid;
-    float mx = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, a.pm[hb + (int64_t)sp * a.rows_total + rr]);
-    const float bse = mx == -INFINITY ? 0.0f : mx;
-    float den = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const int64_t pr = hb + (int64_t)sp * a.rows_total + rr;
-      const float w = exp2f(a.pm[pr] - bse);
-      wts[tid * 64 + sp] = w;
-      den += a.pl[pr] * w;
+  {
+    const int lr = tid >> 4, s0 = tid & 15;  // 16 lanes per row, 4 rows per wavefront
+    const bool rok = lr < nr;
+    float pm[4], pl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sp = s0 + 16 * j;
+      const bool ok = rok && sp < nsplit;
+      const int64_t pr = hb + (int64_t)sp * a.rows_total + r0 + lr;
+      pm[j] = ok ? a.pm[pr] : -INFINITY;
+      pl[j] = ok ? a.pl[pr] : 0.0f;
     }
+    float mx = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float bse = mx == -INFINITY ? 0.0f : mx;
+    float w[4], den = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = pm[j] == -INFINITY ? 0.0f : exp2f(pm[j] - bse);
+      den += pl[j] * w[j];
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) den += __shfl_xor(den, off);
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) wts[tid * 64 + sp] *= inv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (rok) wts[lr * 64 + s0 + 16 * j] = w[j] * inv;
   }
   __syncthreads();
   for (int q4 = tid; q4 < nr * (D / 4); q4 += 256) {
     const int lr = q4 / (D / 4), dd = (q4 % (D / 4)) * 4;
     const int rr = r0 + lr;
+    const float* src = a.po + (hb + rr) * D + dd;
+    const int64_t sstride = (int64_t)a.rows_total * D;
     float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float4 v = *(const float4*)&a.po[(hb + (int64_t)sp * a.rows_total + rr) * D + dd];
-      const float w = wts[lr * 64 + sp];
-      acc4.x += v.x * w;
-      acc4.y += v.y * w;
-      acc4.z += v.z * w;
-      acc4.w += v.w * w;
+    int sp = 0;
+    for (; sp + 4 <= nsplit; sp += 4) {  // four independent loads in flight
+      float4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = *(const float4*)(src + (sp + j) * sstride);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float wj = wts[lr * 64 + sp + j];
+        acc4.x += v[j].x * wj;
+        acc4.y += v[j].y * wj;
+        acc4.z += v[j].z * wj;
+        acc4.w += v[j].w * wj;
+      }
+    }
+    for (; sp < nsplit; ++sp) {
+      const float4 v = *(const float4*)(src + sp * sstride);
+      const float wj = wts[lr * 64 + sp];
+      acc4.x += v.x * wj;
+      acc4.y += v.y * wj;
+      acc4.z += v.z * wj;
+      acc4.w += v.w * wj;
     }
     const int g2 = rr / n, nd = rr % n;
     // four consecutive columns stay within one 8-column group of the packed layout
@@ -322,6 +354,10 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
   }
 }
 
+#ifndef TVP_ATTN_KR
+#define TVP_ATTN_KR 128  // keys per split (doubled while more than 64 splits would be needed)
+#endif
+
 struct AttnPlan {
   int kr, max_splits, rows_total, nthreads;
   size_t off_po, off_pm, off_pl, bytes;
@@ -331,7 +367,7 @@ struct AttnPlan {
 // n_total: nodes of all requests.
 static AttnPlan attn_plan(int hkv, int G, int d, int r_max, int n_total, int max_keys) {
   AttnPlan p{};
-  p.kr = 128;
+  p.kr = TVP_ATTN_KR;
   while (max_keys > 64 * p.kr) p.kr *= 2;  // at most 64 splits (merge weights live in LDS)
   p.max_splits = max_keys > 0 ? (max_keys + p.kr - 1) / p.kr : 1;
   p.rows_total = G * n_total;

@@ -813,7 +813,7 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
     if (!x || ldx < w->k_in) return TVP_ERR_ARG;
     if (((uintptr_t)x) % 16 != 0 || ldx % 8 != 0) return TVP_ERR_ARG;
   }
-  if (y_packed && (m > 32 || epi->mode != TVP_EPI_SWIGLU)) return TVP_ERR_ARG;
+  if (y_packed && (!p.skinny || epi->mode != TVP_EPI_SWIGLU)) return TVP_ERR_ARG;
   if (!scratch || scratch_bytes < p.scratch_bytes) return TVP_ERR_WORKSPACE;
   GemmArgs a{};
   const uint8_t* blob = (const uint8_t*)w->blob;
@@ -870,7 +870,7 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
       break;
     case TVP_EPI_SWIGLU:
       if (w->chan_map != TVP_CHAN_GATEUP) return TVP_ERR_ARG;
-      if (!epi->y || epi->ldy < w->map_a) return TVP_ERR_ARG;
+      if (!epi->y || (!y_packed && epi->ldy < w->map_a)) return TVP_ERR_ARG;  // packed: ldy unused
       break;
     case TVP_EPI_QKV:
       if (w->chan_map != TVP_CHAN_QKV) return TVP_ERR_ARG;
@@ -927,8 +927,24 @@ int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed*
   if ((size_t)groups > kGemmMaxGroups) return TVP_ERR_SHAPE;
   if (!ws || ws_bytes < need) return TVP_ERR_WORKSPACE;
   uint8_t* b = (uint8_t*)ws;
-  return gemm_run(x, nullptr, m, ldx, w, epi, 0, (uint32_t*)b, (unsigned long long*)(b + off_keys),
-                  b + off_scr, scr_bytes, stream);
+  if (epi->x_packed && !x) return TVP_ERR_ARG;
+  return gemm_run(epi->x_packed ? nullptr : x, epi->x_packed ? x : nullptr, m, ldx, w, epi, epi->y_packed,
+                  (uint32_t*)b, (unsigned long long*)(b + off_keys), b + off_scr, scr_bytes, stream);
+}
+
+int64_t w12_packed_x_elems(int64_t k_in) { return k_in < 0 ? 0 : xpack_elems(k_in); }
+
+int w12_pack_x(const uint16_t* x, int64_t m, int64_t ldx, int64_t k_in, uint16_t* xp, hipStream_t stream) {
+  if (m < 1 || m > 32 || k_in < 0 || k_in > (1LL << 30)) return TVP_ERR_SHAPE;
+  if (!xp || ((uintptr_t)xp) % 16 != 0) return TVP_ERR_ARG;
+  if (k_in > 0 && (!x || ldx < k_in)) return TVP_ERR_ARG;
+  const int64_t nchunks = xpack_elems(k_in) / 256;
+  const int64_t threads = nchunks * 32;
+  if (threads == 0) return TVP_OK;
+  pack_x_kernel<<<dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, stream>>>(x, ldx, (int)m, (int)k_in,
+                                                                                  (int)nchunks, xp);
+  TVP_LAUNCH_CHECK();
+  return TVP_OK;
 }
 
 int w12_gemm(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w, void* y,
