@@ -35,6 +35,44 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+# HBM traffic of the gate/up launch measured with rocprofv3 --pmc (FETCH_SIZE,
+# WRITE_SIZE), recorded with a hash of the kernel's sources: the figure is
+# reported only while the sources are unchanged.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "w12_skinny_gateup_27b_pmc.md")
+KERNEL_SOURCES = ["tree_verification_pass_amd/csrc/w12_gemm.hip", "tree_verification_pass_amd/csrc/common.h",
+                  "tree_verification_pass_amd/csrc/internal.h", "include/tvp.h"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per launch from the committed counter summary, if it was taken on
+    the current sources; else None."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def w12_algorithmic_bytes(n_out: int, k_in: int, n_esc: int) -> int:
     """Bytes of the canonical W12 format: planes, base, escape pointers, 4 per escape."""
     return n_out * k_in + n_out * ((k_in + 1) // 2) + n_out + 4 * (n_out + 1) + 4 * n_esc
@@ -217,9 +255,14 @@ def main() -> int:
                     help="only run three plain device copies of MIB MiB (calibrates HBM byte counters)")
     ap.add_argument("--rocprof-summary", metavar="DIR", default="",
                     help="only print the summary of a rocprofv3 csv output folder (no GPU use)")
+    ap.add_argument("--source-hash", action="store_true",
+                    help="only print the hash of the GEMM kernel's sources (recorded with counter summaries)")
     args = ap.parse_args()
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary)
+        return 0
+    if args.source_hash:
+        print(kernel_source_hash())
         return 0
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: the verification pass runs on one GPU "
@@ -310,7 +353,7 @@ def main() -> int:
                               "0.05% outliers x1000)", "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": "w12_skinny_kernel<32,2,2,SWIGLU> (fused gate/up, 34816x5120)", "bound": "hbm",
                      "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "us_per_launch": round(g_ms * 1000.0, 2), "bytes_per_launch": int(g_bytes)},
         "cpu_baseline": cpu,
     }

@@ -16,9 +16,16 @@ static_assert(kGemmMaxGroups * 4 + kGemmKeyBytes <= kGemmZeroBytes, "zero region
 // buckets (`keys`) and scratch.  Activations come row-major in `x` or, for
 // m <= 32, already in the packed layout in `xp` (then `x` is unused).
 // `y_packed`: the SwiGLU epilogue writes its output packed (m <= 32).
+// `ksplit` > 1 (skinny path, epilogue kEpiPartial only) also splits K over
+// workgroups.
 int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
              const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, unsigned long long* keys, void* scratch,
-             size_t scratch_bytes, hipStream_t stream);
+             size_t scratch_bytes, hipStream_t stream, int ksplit = 1);
+
+// Internal epilogue (not part of the ABI): each K slice's fp32 partial result
+// goes to y = P[slice][m][ldy] (canonical columns); the consumer sums the
+// slices in slice order.  Needs the plain channel map and the skinny path.
+constexpr int kEpiPartial = 16;
 
 // Packed activation layout for up to 32 rows: 16-byte groups of 8 columns,
 // [k / 8][row (32)][k % 8].  One MFMA A-fragment load of a wavefront is then
@@ -29,6 +36,8 @@ inline int64_t xpack_elems(int64_t k_in) { return ((k_in + 63) / 64) * 2048; }
 
 // Whether gemm_run takes the skinny path (and so accepts packed input) for m rows.
 bool gemm_is_skinny(int64_t m, const tvp_w12_packed* w);
+// Number of K slices gemm_run uses for `ksplit` (clamped so none is empty).
+int gemm_ksplits(int64_t m, const tvp_w12_packed* w, int ksplit);
 // Counter entries and scratch bytes gemm_run needs for m rows.
 void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes);
 

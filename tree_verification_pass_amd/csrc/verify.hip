@@ -20,6 +20,13 @@ namespace tvp {
 
 constexpr int kMaxLayers = 120;
 
+#ifndef TVP_KSPLIT_O
+#define TVP_KSPLIT_O 2  // K slices of the O projection (packed path)
+#endif
+#ifndef TVP_KSPLIT_DOWN
+#define TVP_KSPLIT_DOWN 4  // K slices of the down projection (packed path)
+#endif
+
 // ------------------------------------------------------------ small kernels
 
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
@@ -34,34 +41,73 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   for (int k = threadIdx.x; k < hidden; k += 256) h[(int64_t)i * ldh + k] = src[k];
 }
 
-// y = bf16(x * (mean(x^2) + eps)^-1/2 * g), fp32 with a fixed reduction order.
-// One workgroup per row; rows of 8-element chunks (16-byte loads) when the
-// row length and pitches allow it, element by element otherwise.  With
-// `packed` (at most 32 rows) y is written in the GEMM's packed activation
-// layout and ldy is unused.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x, int ldx,
-                                                      const uint16_t* __restrict__ g, int hidden,
-                                                      float eps, uint16_t* __restrict__ y, int ldy, int packed) {
+// Residual update fused with the next RMSNorm, one workgroup per row:
+//   h <- bf16(h + (P[0] + P[1] + ... + P[S-1]))   (K-slice partial sums of the
+//        preceding projection, added in slice order; nothing when S == 0)
+//   y <- bf16(h * (mean(h^2) + eps)^-1/2 * g)       (fp32, fixed reduction order)
+// y is the next GEMM's input, row-major or (packed != 0, at most 32 rows) in
+// the packed activation layout.  Rows of 8-element chunks (16-byte accesses)
+// when the row length and pitches allow it, element by element otherwise;
+// up to CPT chunks per thread stay in registers between the two passes.
+template <int CPT>
+__global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict__ P, int S, int64_t pstride,
+                                                         int ldp, uint16_t* __restrict__ h, int ldh,
+                                                         const uint16_t* __restrict__ g, int hidden, float eps,
+                                                         uint16_t* __restrict__ y, int ldy, int packed) {
   __shared__ float ws[4];
   const int i = blockIdx.x, tid = threadIdx.x;
-  const uint16_t* xr = x + (int64_t)i * ldx;
+  uint16_t* hr = h + (int64_t)i * ldh;
+  const float* pr = P + (int64_t)i * ldp;
   uint16_t* yr = y + (int64_t)i * ldy;
-  const bool vec = (hidden % 8) == 0 && (ldx % 8) == 0 && (packed || (ldy % 8) == 0);
+  const bool vec = (hidden % 8) == 0 && (ldh % 8) == 0 && (S == 0 || (ldp % 4) == 0) && (packed || (ldy % 8) == 0);
   float ss = 0.0f;
-  if (vec) {
-    const int nc = hidden / 8;
-    for (int c = tid; c < nc; c += 256) {
-      const uint4 v = *(const uint4*)(xr + 8 * c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t keep[CPT][4];  // the first CPT chunks of this thread (fully unrolled, so registers)
+  // pass 1 on chunk c: residual update (written back) and sum of squares
+  auto pass1 = [&](int c, uint32_t (&w)[4]) {
+    const uint4 v = *(const uint4*)(hr + 8 * c);
+    w[0] = v.x, w[1] = v.y, w[2] = v.z, w[3] = v.w;
+    if (S > 0) {
+      float acc[8];
+      for (int sl = 0; sl < S; ++sl) {
+        const float4 p0 = *(const float4*)(pr + sl * pstride + 8 * c);
+        const float4 p1 = *(const float4*)(pr + sl * pstride + 8 * c + 4);
+        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = sl == 0 ? pv[e] : acc[e] + pv[e];
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float a0 = bf16_to_f32(w[e] & 0xFFFFu), a1 = bf16_to_f32(w[e] >> 16);
-        ss += a0 * a0 + a1 * a1;
+        const uint32_t lo = f32_to_bf16(bf16_to_f32(w[e] & 0xFFFFu) + acc[2 * e]);
+        const uint32_t hi = f32_to_bf16(bf16_to_f32(w[e] >> 16) + acc[2 * e + 1]);
+        w[e] = lo | (hi << 16);
       }
+      *(uint4*)(hr + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a0 = bf16_to_f32(w[e] & 0xFFFFu), a1 = bf16_to_f32(w[e] >> 16);
+      ss += a0 * a0 + a1 * a1;
+    }
+  };
+  const int nc = vec ? hidden / 8 : 0;
+  if (vec) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+      if (tid + 256 * j < nc) pass1(tid + 256 * j, keep[j]);
+    for (int c = tid + 256 * CPT; c < nc; c += 256) {
+      uint32_t w[4];
+      pass1(c, w);
     }
   } else {
     for (int k = tid; k < hidden; k += 256) {
-      const float v = bf16_to_f32(xr[k]);
+      float v = bf16_to_f32(hr[k]);
+      if (S > 0) {
+        float acc = 0.0f;
+        for (int sl = 0; sl < S; ++sl) acc = sl == 0 ? pr[sl * pstride + k] : acc + pr[sl * pstride + k];
+        const uint32_t hb = f32_to_bf16(v + acc);
+        hr[k] = (uint16_t)hb;
+        v = bf16_to_f32(hb);
+      }
       ss += v * v;
     }
   }
@@ -70,25 +116,39 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
   __syncthreads();
   const float tot = (ws[0] + ws[1]) + (ws[2] + ws[3]);
   const float r = 1.0f / sqrtf(tot / (float)hidden + eps);
-  if (vec) {
-    const int nc = hidden / 8;
-    for (int c = tid; c < nc; c += 256) {
-      const uint4 v = *(const uint4*)(xr + 8 * c);
-      const uint4 gv = *(const uint4*)(g + 8 * c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
-      uint32_t o[4];
+  // pass 2 on chunk c (w: its updated values)
+  auto pass2 = [&](int c, const uint32_t (&w)[4]) {
+    const uint4 gv = *(const uint4*)(g + 8 * c);
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint32_t o[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = f32_to_bf16(bf16_to_f32(w[e] & 0xFFFFu) * r * bf16_to_f32(gw[e] & 0xFFFFu));
-        const uint32_t hi = f32_to_bf16(bf16_to_f32(w[e] >> 16) * r * bf16_to_f32(gw[e] >> 16));
-        o[e] = lo | (hi << 16);
-      }
-      *(uint4*)(packed ? y + xpack_index(i, 8 * c) : yr + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = f32_to_bf16(bf16_to_f32(w[e] & 0xFFFFu) * r * bf16_to_f32(gw[e] & 0xFFFFu));
+      const uint32_t hi = f32_to_bf16(bf16_to_f32(w[e] >> 16) * r * bf16_to_f32(gw[e] >> 16));
+      o[e] = lo | (hi << 16);
+    }
+    *(uint4*)(packed ? y + xpack_index(i, 8 * c) : yr + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+  };
+  if (vec) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+      if (tid + 256 * j < nc) pass2(tid + 256 * j, keep[j]);
+    for (int c = tid + 256 * CPT; c < nc; c += 256) {  // re-read this thread's own pass-1 result
+      const uint4 v = *(const uint4*)(hr + 8 * c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      pass2(c, w);
     }
   } else {
     for (int k = tid; k < hidden; k += 256)
-      (packed ? y[xpack_index(i, k)] : yr[k]) = (uint16_t)f32_to_bf16(bf16_to_f32(xr[k]) * r * bf16_to_f32(g[k]));
+      (packed ? y[xpack_index(i, k)] : yr[k]) = (uint16_t)f32_to_bf16(bf16_to_f32(hr[k]) * r * bf16_to_f32(g[k]));
   }
+}
+
+// RMSNorm alone (no residual update): S = 0 of the fused kernel.
+static void launch_norm(const float* P, int S, int64_t pstride, int ldp, uint16_t* h, int ldh, const uint16_t* g,
+                        int hidden, float eps, uint16_t* y, int ldy, int packed, int rows, hipStream_t stream) {
+  resid_norm_kernel<4><<<dim3(rows), dim3(256), 0, stream>>>(P, S, pstride, ldp, h, ldh, g, hidden, eps, y, ldy,
+                                                             packed);
 }
 
 // One workgroup per request; the walk is sequential over nodes (parents[i] < i).
@@ -198,6 +258,8 @@ struct tvp_plan {
   size_t off_h, off_a, off_q, off_o, off_u;
   size_t off_anc, off_pos, off_slot, off_tstat, off_bad;
   size_t off_gscr, gscr_bytes;
+  size_t off_part;  // K-slice partial sums of the O and down projections (packed path)
+  int ks_o, ks_down;  // their K slices at 32 rows
   size_t off_ascr, ascr_bytes;
   size_t bytes;
 };
@@ -298,6 +360,20 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   off = align_up(off + (size_t)kMaxReq * 4, 256);
   p->off_bad = off;
   off = align_up(off + (size_t)mn * 4, 256);
+  // O and down projections in the packed path: K split over workgroups, the
+  // slices' partial sums reduced by the fused residual + RMSNorm kernel
+  p->ks_o = 1;
+  p->ks_down = 1;
+  if (p->pack_ok) {
+    p->ks_o = TVP_KSPLIT_O;
+    p->ks_down = TVP_KSPLIT_DOWN;
+    for (int l = 0; l < d->n_layers; ++l) {
+      p->ks_o = std::min(p->ks_o, gemm_ksplits(32, &p->layers[l].wo, TVP_KSPLIT_O));
+      p->ks_down = std::min(p->ks_down, gemm_ksplits(32, &p->layers[l].wdown, TVP_KSPLIT_DOWN));
+    }
+  }
+  p->off_part = off;
+  off = align_up(off + (size_t)std::max(p->ks_o, p->ks_down) * 32 * H * 4, 256);
   p->off_gscr = off;
   p->gscr_bytes = gscr;
   off = align_up(off + gscr, 256);
@@ -351,10 +427,15 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   if ((st = launch_tree_prep(parents, ri, s_req, anc, pos, slot, tstat, stream))) return st;
   embed_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(tokens, d.embed, H, d.vocab, h, p->ld_h, bad);
   TVP_LAUNCH_CHECK();
+  float* part = (float*)(w + p->off_part);
+  const int64_t pstride = (int64_t)n_total * H;  // one K slice of partial sums [n_total][H]
+  // the first layer's attention norm; later norms are fused with the residual update
+  launch_norm(part, 0, pstride, H, h, p->ld_h, p->layers[0].attn_norm, H, d.norm_eps, a, p->ld_h, pk, n_total,
+              stream);
+  TVP_LAUNCH_CHECK();
   for (int l = 0; l < d.n_layers; ++l) {
     const tvp_layer& L = p->layers[l];
-    rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, L.attn_norm, H, d.norm_eps, a, p->ld_h, pk);
-    TVP_LAUNCH_CHECK();
+    const uint16_t* next_norm = l + 1 < d.n_layers ? p->layers[l + 1].attn_norm : d.final_norm;
     tvp_gemm_epilogue e{};
     e.mode = TVP_EPI_QKV;
     e.y = q;
@@ -371,16 +452,27 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     if ((st = launch_tree_attention(q, L.k_cache, L.v_cache, d.s_max, ri, s_req, anc, hq, hkv, hd, G * max_n,
                                     max_keys, o, pk, ascr, p->ascr_bytes, stream)))
       return st;
+    // O projection + residual, then the FFN norm
     e = tvp_gemm_epilogue{};
-    e.mode = TVP_EPI_RESID;
-    e.y = h;
-    e.ldy = p->ld_h;
-    e.resid = h;
-    e.ldr = p->ld_h;
-    if ((st = gemm_run(o, pk ? o : nullptr, n_total, p->ld_q, &L.wo, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes,
-                       stream)))
-      return st;
-    rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, L.ffn_norm, H, d.norm_eps, a, p->ld_h, pk);
+    if (pk) {
+      e.mode = kEpiPartial;
+      e.y = part;
+      e.ldy = H;
+      if ((st = gemm_run(o, o, n_total, p->ld_q, &L.wo, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes, stream,
+                         p->ks_o)))
+        return st;
+      launch_norm(part, p->ks_o, pstride, H, h, p->ld_h, L.ffn_norm, H, d.norm_eps, a, p->ld_h, 1, n_total,
+                  stream);
+    } else {
+      e.mode = TVP_EPI_RESID;
+      e.y = h;
+      e.ldy = p->ld_h;
+      e.resid = h;
+      e.ldr = p->ld_h;
+      if ((st = gemm_run(o, nullptr, n_total, p->ld_q, &L.wo, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes, stream)))
+        return st;
+      launch_norm(part, 0, pstride, H, h, p->ld_h, L.ffn_norm, H, d.norm_eps, a, p->ld_h, 0, n_total, stream);
+    }
     TVP_LAUNCH_CHECK();
     e = tvp_gemm_epilogue{};
     e.mode = TVP_EPI_SWIGLU;
@@ -389,18 +481,30 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wgu, &e, pk, gcnt, gkeys, gscr, p->gscr_bytes,
                        stream)))
       return st;
+    // down projection + residual, then the next layer's attention norm (or the final norm)
     e = tvp_gemm_epilogue{};
-    e.mode = TVP_EPI_RESID;
-    e.y = h;
-    e.ldy = p->ld_h;
-    e.resid = h;
-    e.ldr = p->ld_h;
-    if ((st = gemm_run(u, pk ? u : nullptr, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes,
-                       stream)))
-      return st;
+    if (pk) {
+      e.mode = kEpiPartial;
+      e.y = part;
+      e.ldy = H;
+      if ((st = gemm_run(u, u, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes, stream,
+                         p->ks_down)))
+        return st;
+      launch_norm(part, p->ks_down, pstride, H, h, p->ld_h, next_norm, H, d.norm_eps, a, p->ld_h, 1, n_total,
+                  stream);
+    } else {
+      e.mode = TVP_EPI_RESID;
+      e.y = h;
+      e.ldy = p->ld_h;
+      e.resid = h;
+      e.ldr = p->ld_h;
+      if ((st = gemm_run(u, nullptr, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes,
+                         stream)))
+        return st;
+      launch_norm(part, 0, pstride, H, h, p->ld_h, next_norm, H, d.norm_eps, a, p->ld_h, 0, n_total, stream);
+    }
+    TVP_LAUNCH_CHECK();
   }
-  rmsnorm_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(h, p->ld_h, d.final_norm, H, d.norm_eps, a, p->ld_h, pk);
-  TVP_LAUNCH_CHECK();
   tvp_gemm_epilogue e{};
   e.mode = TVP_EPI_ARGMAX;
   e.argmax = out->argmax;

@@ -40,6 +40,7 @@ struct GemmArgs {
   const int32_t* rowmap;
   int n_tiles, n_kb, n_pad;
   int groups, splits, kbs, ntasks;
+  int kps;  // skinny: K blocks per K slice (slices = splits)
   float* part;
   uint32_t* cnt;
   unsigned long long* keys;  // ARGMAX: [m][64] packed (value, -id) maxima, zero on entry
@@ -119,8 +120,15 @@ __device__ inline unsigned long long argmax_key(float v, int32_t id) {
 // (thread index `tid`), reading fp32 results through V(row, col).
 template <int MODE, typename Get>
 __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int tid, int nthr, int bucket,
-                                Get V) {
-  if constexpr (MODE == TVP_EPI_F32 || MODE == TVP_EPI_BF16 || MODE == TVP_EPI_RESID) {
+                                Get V, int slice = 0) {
+  if constexpr (MODE == kEpiPartial) {
+    float* P = (float*)a.y + (int64_t)slice * M * a.ldy;
+    for (int idx = tid; idx < M * nc; idx += nthr) {
+      const int row = idx / nc, col = c0 + idx % nc;
+      const int32_t r = a.rowmap[col];
+      if (r >= 0) P[row * a.ldy + r] = V(row, col);
+    }
+  } else if constexpr (MODE == TVP_EPI_F32 || MODE == TVP_EPI_BF16 || MODE == TVP_EPI_RESID) {
     for (int idx = tid; idx < M * nc; idx += nthr) {
       const int row = idx / nc, col = c0 + idx % nc;
       const int32_t r = a.rowmap[col];
@@ -238,10 +246,11 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KW = blockDim.x >> 6;
-  const int grp = blockIdx.x;
+  const int grp = blockIdx.x % a.groups, slice = blockIdx.x / a.groups;
   const int t0 = grp * TPW;
-  const int kb0 = wave * a.kbs;
-  const int kb1 = min(a.n_kb, kb0 + a.kbs);
+  const int ks1 = min(a.n_kb, (slice + 1) * a.kps);  // this workgroup's K slice ends here
+  const int kb0 = slice * a.kps + wave * a.kbs;
+  const int kb1 = min(ks1, kb0 + a.kbs);
   const int nblk = kb1 > kb0 ? kb1 - kb0 : 0;  // <= 63
 
   // Tiles past the end are computed on a clamped tile and dropped at the end,
@@ -431,7 +440,8 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
                    float v = 0.0f;
                    for (int w = 0; w < KW; ++w) v += P[(w * M + row) * NC + c];
                    return v;
-                 });
+                 },
+                 slice);
 }
 
 template <int ROWS>
@@ -675,7 +685,7 @@ __global__ __launch_bounds__(256) void w12_wide_kernel(GemmArgs a) {
 
 struct GemmPlan {
   bool skinny;
-  int MT, RB, TPW, RD, KW, TG, groups, splits, kbs, ntasks, grid;
+  int MT, RB, TPW, RD, KW, TG, groups, splits, kbs, kps, ntasks, grid;
   size_t scratch_bytes;
 };
 
@@ -703,7 +713,7 @@ constexpr int kWideTargetGroups = 1024;
 #define TVP_RD2 2  // register-ring depth, two tiles per workgroup
 #endif
 
-static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w) {
+static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1) {
   GemmPlan p{};
   const int64_t n_pad = (int64_t)w->n_tiles * 32;
   const int nkb = w->n_kb;
@@ -715,13 +725,16 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w) {
     p.RD = p.TPW == 2 ? TVP_RD2 : TVP_RD1;
     p.TG = p.TPW;
     p.groups = (int)ceil_div(w->n_tiles, p.TPW);
-    p.KW = p.groups >= TVP_KW_SWITCH ? TVP_KW_MANY : TVP_KW_FEW;
-    if (nkb > 4 * 63) p.KW = 8;
-    p.KW = std::max(1, std::min(p.KW, nkb));
-    p.kbs = nkb > 0 ? (int)ceil_div(nkb, p.KW) : 0;
-    p.splits = 1;
-    p.ntasks = p.groups;
-    p.grid = p.groups;
+    // K slices over workgroups (partial-sum epilogue only), none empty
+    int sl = std::max(1, std::min(ksplit, std::max(nkb, 1)));
+    p.kps = nkb > 0 ? (int)ceil_div(nkb, sl) : 0;
+    p.splits = p.kps > 0 ? (int)ceil_div(nkb, p.kps) : 1;
+    p.KW = p.groups * p.splits >= TVP_KW_SWITCH ? TVP_KW_MANY : TVP_KW_FEW;
+    if (p.kps > 4 * 63) p.KW = 8;
+    p.KW = std::max(1, std::min(p.KW, p.kps));
+    p.kbs = p.kps > 0 ? (int)ceil_div(p.kps, p.KW) : 0;
+    p.ntasks = p.groups * p.splits;
+    p.grid = p.ntasks;
   } else {
     p.TPW = 1;
     p.RD = 0;
@@ -755,6 +768,7 @@ static void launch_skinny(const GemmArgs& a, const GemmPlan& p, hipStream_t stre
     case TVP_EPI_RESID: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_RESID><<<grid, block, lds, stream>>>(a); break;
     case TVP_EPI_SWIGLU: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_SWIGLU><<<grid, block, lds, stream>>>(a); break;
     case TVP_EPI_QKV: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_QKV><<<grid, block, lds, stream>>>(a); break;
+    case kEpiPartial: w12_skinny_kernel<MT, TPW, RD, kEpiPartial><<<grid, block, lds, stream>>>(a); break;
     default: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_ARGMAX><<<grid, block, lds, stream>>>(a); break;
   }
 }
@@ -795,6 +809,11 @@ static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
 
 bool gemm_is_skinny(int64_t m, const tvp_w12_packed* w) { return make_plan(m, w).skinny; }
 
+int gemm_ksplits(int64_t m, const tvp_w12_packed* w, int ksplit) {
+  const GemmPlan p = make_plan(m, w, ksplit);
+  return p.skinny ? p.splits : 1;
+}
+
 void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes) {
   const GemmPlan p = make_plan(m, w);
   *groups = p.groups;
@@ -803,10 +822,11 @@ void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* 
 
 int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
              const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, unsigned long long* keys, void* scratch,
-             size_t scratch_bytes, hipStream_t stream) {
+             size_t scratch_bytes, hipStream_t stream, int ksplit) {
   if (!w || !epi || !w->blob || !cnt || !keys) return TVP_ERR_ARG;
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
-  const GemmPlan p = make_plan(m, w);
+  if (ksplit > 1 && epi->mode != kEpiPartial) return TVP_ERR_ARG;
+  const GemmPlan p = make_plan(m, w, ksplit);
   if (xp) {
     if (!p.skinny || ((uintptr_t)xp) % 16 != 0) return TVP_ERR_ARG;
   } else if (w->k_in > 0) {
@@ -842,6 +862,7 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
   a.groups = p.groups;
   a.splits = p.splits;
   a.kbs = p.kbs;
+  a.kps = p.kps;
   a.ntasks = p.ntasks;
   a.cnt = cnt;
   a.keys = keys;
@@ -885,6 +906,9 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
       if (!epi->argmax) return TVP_ERR_ARG;
       if (epi->logits && epi->ldl < w->n_out) return TVP_ERR_ARG;
       break;
+    case kEpiPartial:
+      if (!p.skinny || w->chan_map != TVP_CHAN_PLAIN || !epi->y || epi->ldy < w->n_out) return TVP_ERR_ARG;
+      break;
     default:
       return TVP_ERR_ARG;
   }
@@ -926,6 +950,7 @@ int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed*
   const size_t need = gemm_ws_layout(m, w, &off_keys, &off_scr, &scr_bytes, &groups);
   if ((size_t)groups > kGemmMaxGroups) return TVP_ERR_SHAPE;
   if (!ws || ws_bytes < need) return TVP_ERR_WORKSPACE;
+  if (epi->mode < TVP_EPI_F32 || epi->mode > TVP_EPI_ARGMAX) return TVP_ERR_ARG;
   uint8_t* b = (uint8_t*)ws;
   if (epi->x_packed && !x) return TVP_ERR_ARG;
   return gemm_run(epi->x_packed ? nullptr : x, epi->x_packed ? x : nullptr, m, ldx, w, epi, epi->y_packed,
