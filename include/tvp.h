@@ -97,7 +97,10 @@ int w12_decode(const tvp_w12* t, uint16_t* out, hipStream_t stream);
  * The GEMM streams W12 from a tiled copy of the same records: tiles of 32
  * channels x 64 k, each 3072 contiguous bytes laid out in the order the
  * 64 lanes of a wavefront load and decode them, plus per-tile-block escape
- * lists.  It decodes to exactly the same bf16 values as the canonical layout
+ * lists.  Tile blocks are stored k-block-major (block j of tile t at
+ * (j * n_tiles + t) * 3072 bytes), so workgroups that stream the same k range
+ * of neighbouring tiles at the same time read neighbouring memory.
+ * It decodes to exactly the same bf16 values as the canonical layout
  * (checked by w12_gemm parity).  `chan_map` chooses which canonical row lands
  * in each packed channel, so fused epilogues find their operands in one tile:
  *   TVP_CHAN_PLAIN   packed channel p = row p

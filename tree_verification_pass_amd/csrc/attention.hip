@@ -8,14 +8,20 @@
 //
 // Design: per (request, kv head, key split) one workgroup of up to 8
 // wavefronts; wavefront w owns 32 query rows (row = gq * n + i for query head
-// kv_head*G + gq and node i).  Keys are staged 64 at a time through LDS (K
-// row-major, V transposed, both XOR-swizzled), scores are computed as
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so each lane owns one query row,
-// masked with the node's 64-bit ancestor mask, folded into an online softmax,
-// and P V is accumulated with the same MFMA (P as a sum of two bf16 pieces).  Splits
-// write (max, sum, O) partials; the last split of each (request, kv head)
-// merges them in split order, so the result is deterministic.
+// kv_head*G + gq and node i).  Keys are staged 64 at a time through LDS with
+// fully coalesced 16-byte loads (K and V both row-major there, XOR-swizzled
+// per row).  Scores are computed as S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 so each lane owns one query row, masked with the
+// node's 64-bit ancestor mask and folded into an online softmax; P V is
+// accumulated with the same MFMA, its V^T operand read straight from the
+// row-major V tile with the LDS transpose read (ds_read_b64_tr_b16), and P
+// applied as a sum of two bf16 pieces.  Splits write (max, sum, O) partials
+// in the accumulator's own register layout (one coalesced 256-byte store per
+// accumulator register); a separate merge launch sums them in split order,
+// so the result is deterministic.
 #include <math.h>
+
+#include <algorithm>
 
 #include "internal.h"
 
@@ -56,6 +62,12 @@ __global__ __launch_bounds__(64) void tree_prep_kernel(const int32_t* __restrict
   if (i == 0) status[r] = all_ok ? TVP_OK : TVP_ERR_TREE;
 }
 
+// Partial rows of request r start at prow[r]: its G * n rows rounded up to a
+// multiple of 32, so every wavefront's 32-row block is its own.
+struct PartRows {
+  int32_t prow[kMaxReq + 1];
+};
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* kc;
@@ -69,7 +81,8 @@ struct AttnArgs {
   float* po;
   float* pm;
   float* pl;
-  int row_blocks;  // merge: 16-row blocks per (request, kv head)
+  int row_blocks;  // merge: 32-row blocks per (request, kv head)
+  PartRows pr;
   uint16_t* out;
   int out_packed;  // out in the packed activation layout (<= 32 nodes) instead of [node][hq * D]
 };
@@ -80,13 +93,23 @@ __device__ inline int64_t attn_out_index(const AttnArgs& a, int node, int col) {
   return a.out_packed ? xpack_index(node, col) : (int64_t)node * a.hq * D + col;
 }
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+// Swizzle of V rows in LDS (16-byte chunk index XOR): the transpose reads of
+// one MFMA operand touch 8 rows x 64 bytes and spread evenly over the banks.
+template <int D>
+__device__ inline int v_swz(int key) {
+  return D == 128 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2);
+}
+
 template <int D, int NT>
 __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
   constexpr int KC = 64;        // keys per LDS stage
-  constexpr int CH = D / 8;     // 16-byte chunks per K row
+  constexpr int CH = D / 8;     // 16-byte chunks per row
   constexpr int NDB = D / 32;   // d blocks of the P V product
-  __shared__ uint4 ks[KC * CH];              // K [key][chunk ^ (key % CH)]
-  __shared__ uint2 vt[D * (KC / 4)];         // V^T [d][4-key chunk ^ (d % 16)]
+  __shared__ uint4 ks[KC * CH];  // K [key][chunk ^ (key % CH)]
+  __shared__ uint4 vs[KC * CH];  // V [key][chunk ^ v_swz(key)]
 
   const int split = blockIdx.x % a.max_splits;
   const int kh = (blockIdx.x / a.max_splits) % a.hkv;
@@ -97,7 +120,6 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
   if (split >= nsplit) return;
   const int k0 = split * a.kr, k1 = min(T, k0 + a.kr);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
-  constexpr int nthr = NT;
   const int row = wave * 32 + (lane & 31);
   const bool row_ok = row < R;
   const int gq = row_ok ? row / n : 0, node = row_ok ? row % n : 0;
@@ -122,43 +144,39 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[db][v] = 0.0f;
 
-  // K/V of the next 64 keys are fetched into registers while the current
-  // ones are used (nthr is 256 or 512, so at most PER chunks per thread).
+  // K/V of the next 64 keys are fetched into registers while the current ones
+  // are used; CH consecutive lanes read one 2*D-byte row.
   constexpr int PER = KC * CH / NT;
   uint4 kpre[PER], vpre[PER];
   auto fetch = [&](int sub) {
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-      const int idx = tid + it * nthr;
+      const int idx = tid + it * NT;
+      const int kk = sub + idx / CH, c = idx % CH;
       kpre[it] = make_uint4(0, 0, 0, 0);
       vpre[it] = make_uint4(0, 0, 0, 0);
-      if (idx < KC * CH) {
-        const int kk = sub + idx % KC, c = idx / KC;
-        if (kk < k1) {
-          kpre[it] = *(const uint4*)(kbase + (int64_t)kk * D + 8 * c);
-          vpre[it] = *(const uint4*)(vbase + (int64_t)kk * D + 8 * c);
-        }
+      if (kk < k1) {
+        kpre[it] = *(const uint4*)(kbase + (int64_t)kk * D + 8 * c);
+        vpre[it] = *(const uint4*)(vbase + (int64_t)kk * D + 8 * c);
       }
     }
   };
   auto stash = [&]() {
-    uint16_t* vts = (uint16_t*)vt;
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-      const int idx = tid + it * nthr;
-      if (idx >= KC * CH) continue;
-      const int key = idx % KC, c = idx / KC;
+      const int idx = tid + it * NT;
+      const int key = idx / CH, c = idx % CH;
       ks[key * CH + (c ^ (key % CH))] = kpre[it];
-      const uint4 vv = vpre[it];
-      const uint32_t hv[8] = {vv.x & 0xFFFFu, vv.x >> 16, vv.y & 0xFFFFu, vv.y >> 16,
-                              vv.z & 0xFFFFu, vv.z >> 16, vv.w & 0xFFFFu, vv.w >> 16};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dd = 8 * c + e;
-        vts[(dd * (KC / 4) + ((key >> 2) ^ (dd & 15))) * 4 + (key & 3)] = (uint16_t)hv[e];
-      }
+      vs[key * CH + (c ^ v_swz<D>(key))] = vpre[it];
     }
   };
+  // transpose-read geometry: in each 16-lane group, source lane s points at
+  // key row (s / 4) and 4 d-columns (s % 4) * 4; lane i then receives
+  // V[key0 + 0..3][d0 + i]
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_key = 4 * h + (s16 >> 2);
+  const int tr_d = 16 * (g16 & 1) + 4 * (s16 & 3);
+  const char* vs_bytes = (const char*)vs;
 
   fetch(k0);
   for (int sub = k0; sub < k1; sub += KC) {
@@ -183,39 +201,50 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
           sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, sc, 0, 0, 0);
         }
       }
+      // raw scores; the 1/sqrt(d) scale (in log2 units) is applied inside the
+      // exponent.  Blocks of context keys only need no mask.
       float mloc = -INFINITY;
+      const int kb0 = sub + kb * 32;
+      if (kb0 + 32 <= min(L, k1)) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = sub + kb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        bool vis = row_ok && key < k1;
-        if (vis && key >= L) vis = (anc >> (key - L)) & 1ull;
-        const float x = vis ? sc[v] * a.scale_log2 : -INFINITY;
-        sc[v] = x;
-        mloc = fmaxf(mloc, x);
+        for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sc[v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kb0 + 8 * (v >> 2) + 4 * h + (v & 3);
+          bool vis = row_ok && key < k1;
+          if (vis && key >= L) vis = (anc >> (key - L)) & 1ull;
+          sc[v] = vis ? sc[v] : -INFINITY;
+          mloc = fmaxf(mloc, sc[v]);
+        }
       }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
       const float m_new = fmaxf(m_run, mloc);
       const float base = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = exp2f(m_run - base);
+      const float nbs = -base * a.scale_log2;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - base) * a.scale_log2);
       // P is split into two bf16 pieces (hi = bf16(p), lo = bf16(p - hi)) so the
       // P V product on bf16 MFMA keeps 16 significant bits of every weight.
       float lsum = 0.0f;
       uint32_t pk[8], pl[8];
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
-        const float p0 = exp2f(sc[v] - base), p1 = exp2f(sc[v + 1] - base);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[v], a.scale_log2, nbs));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[v + 1], a.scale_log2, nbs));
         lsum += p0 + p1;
-        const uint32_t h0 = f32_to_bf16(p0), h1 = f32_to_bf16(p1);
-        pk[v / 2] = h0 | (h1 << 16);
-        pl[v / 2] = f32_to_bf16(p0 - bf16_to_f32(h0)) | (f32_to_bf16(p1 - bf16_to_f32(h1)) << 16);
+        const uint32_t hk = pack_bf16x2(p0, p1);
+        pk[v / 2] = hk;
+        pl[v / 2] = pack_bf16x2(p0 - __uint_as_float(hk << 16), p1 - __uint_as_float(hk & 0xFFFF0000u));
       }
       lsum += __shfl_xor(lsum, 32);
       l_run = l_run * alpha + lsum;
       m_run = m_new;
+      if (__ballot(alpha != 1.0f)) {  // the running max moved for some row: rescale
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      }
 
       // O^T[d][row] += V^T[d][key] P^T[key][row]; MFMA q of this key block
       // covers keys kb*32 + 16 q + 8 (i/4) + 4 h + i%4 for k-index 8 h + i.
@@ -223,16 +252,20 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
       for (int q = 0; q < 2; ++q) {
         const bf16x8_t B = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]));
         const bf16x8_t Bl = __builtin_bit_cast(bf16x8_t, make_uint4(pl[4 * q], pl[4 * q + 1], pl[4 * q + 2], pl[4 * q + 3]));
-        const int c8 = 8 * kb + 4 * q + h;
+        const int r1 = kb * 32 + 16 * q + tr_key, r2 = r1 + 8;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int dd = db * 32 + (lane & 31);
-          const uint2 lo = vt[dd * (KC / 4) + (c8 ^ (dd & 15))];
-          const uint2 hi = vt[dd * (KC / 4) + ((c8 + 2) ^ (dd & 15))];
-          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          const int d = 32 * db + tr_d;  // 4 columns, 8 bytes inside one 16-byte chunk
+          const int off1 = (r1 * CH + ((d >> 3) ^ v_swz<D>(r1))) * 16 + (d & 7) * 2;
+          const int off2 = (r2 * CH + ((d >> 3) ^ v_swz<D>(r2))) * 16 + (d & 7) * 2;
+          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vs_bytes + off1));
+          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vs_bytes + off2));
+          const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, o[db], 0, 0, 0);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bl, o[db], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);  // keeps the operand reads of the two halves apart (register pressure)
       }
     }
   }
@@ -251,112 +284,112 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
     }
     return;
   }
-  // partial rows: [kv head][split][G * global node], request r's rows start at G * nb
-  const int64_t pbase = ((int64_t)kh * a.max_splits + split) * a.rows_total + (int64_t)a.G * nb;
-  if (row_ok) {
+  if (wave * 32 >= R) return;
+  // partial rows: [kv head][split][padded rows]; this wavefront's 32-row block
+  // is stored in the accumulator layout: element (db, v) of lane l at
+  // block * D + (db * 16 + v) * 64 + l
+  const int64_t pbase = ((int64_t)kh * a.max_splits + split) * a.rows_total + a.pr.prow[r] + wave * 32;
+  float* pob = a.po + pbase * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int dd = db * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        a.po[(pbase + row) * D + dd] = o[db][v];
-      }
-    if (h == 0) {
-      a.pm[pbase + row] = m_run;
-      a.pl[pbase + row] = l_run;
-    }
+    for (int v = 0; v < 16; ++v) pob[(db * 16 + v) * 64 + lane] = o[db][v];
+  if (h == 0) {  // the running max is a raw score (unscaled)
+    a.pm[pbase + (lane & 31)] = m_run;
+    a.pl[pbase + (lane & 31)] = l_run;
   }
 }
 
 // Merge of the key splits (a separate launch: the kernel boundary makes every
-// split's partials visible).  One workgroup per (request, kv head, 16 query
-// rows); each row's split weights are formed by 16 lanes with a fixed
-// shuffle-tree order, then every output element sums its splits in split
-// order, so the result is deterministic.
+// split's partials visible).  One workgroup per (request, kv head, 32-row
+// block, quarter of the block's D*32 elements).  Each row's split weights
+// come from 8 lanes with a fixed shuffle-tree order; every output element
+// sums its splits in split order, so the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
-  __shared__ float wts[16 * 64];  // [row][split], normalised merge weights
-  const int rb = blockIdx.x % a.row_blocks;
-  const int kh = (blockIdx.x / a.row_blocks) % a.hkv;
-  const int r = blockIdx.x / (a.row_blocks * a.hkv);
+  __shared__ float wts[32 * 64];  // [row][split], normalised merge weights
+  const int qt = blockIdx.x & 3;
+  const int rb = (blockIdx.x >> 2) % a.row_blocks;
+  const int kh = ((blockIdx.x >> 2) / a.row_blocks) % a.hkv;
+  const int r = (blockIdx.x >> 2) / (a.row_blocks * a.hkv);
   const int L = a.ri.ctx_len[r], nb = a.ri.node_ptr[r], n = a.ri.node_ptr[r + 1] - nb;
   const int R = a.G * n;
   const int nsplit = (L + n + a.kr - 1) / a.kr;  // <= 64
-  if (nsplit <= 1 || rb * 16 >= R) return;
+  if (nsplit <= 1 || rb * 32 >= R) return;
   const int tid = threadIdx.x;
-  const int64_t hb = (int64_t)kh * a.max_splits * a.rows_total + (int64_t)a.G * nb;
-  const int r0 = rb * 16, nr = min(16, R - r0);
+  // row block base of split 0; split sp adds sp * rows_total
+  const int64_t hb = (int64_t)kh * a.max_splits * a.rows_total + a.pr.prow[r] + rb * 32;
   {
-    const int lr = tid >> 4, s0 = tid & 15;  // 16 lanes per row, 4 rows per wavefront
-    const bool rok = lr < nr;
-    float pm[4], pl[4];
+    const int lr = tid >> 3, s0 = tid & 7;  // 8 lanes per row
+    float pm[8], pl[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int sp = s0 + 16 * j;
-      const bool ok = rok && sp < nsplit;
-      const int64_t pr = hb + (int64_t)sp * a.rows_total + r0 + lr;
+    for (int j = 0; j < 8; ++j) {
+      const int sp = s0 + 8 * j;
+      const bool ok = sp < nsplit;
+      const int64_t pr = hb + (int64_t)sp * a.rows_total + lr;
       pm[j] = ok ? a.pm[pr] : -INFINITY;
       pl[j] = ok ? a.pl[pr] : 0.0f;
     }
-    float mx = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
+    float mx = pm[0];
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, pm[j]);
+#pragma unroll
+    for (int off = 4; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     const float bse = mx == -INFINITY ? 0.0f : mx;
-    float w[4], den = 0.0f;
+    float w[8], den = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w[j] = pm[j] == -INFINITY ? 0.0f : exp2f(pm[j] - bse);
+    for (int j = 0; j < 8; ++j) {
+      w[j] = pm[j] == -INFINITY ? 0.0f : exp2f((pm[j] - bse) * a.scale_log2);  // maxima are raw scores
       den += pl[j] * w[j];
     }
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) den += __shfl_xor(den, off);
+    for (int off = 4; off > 0; off >>= 1) den += __shfl_xor(den, off);
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (rok) wts[lr * 64 + s0 + 16 * j] = w[j] * inv;
+    for (int j = 0; j < 8; ++j) wts[lr * 64 + s0 + 8 * j] = w[j] * inv;
   }
   __syncthreads();
-  for (int q4 = tid; q4 < nr * (D / 4); q4 += 256) {
-    const int lr = q4 / (D / 4), dd = (q4 % (D / 4)) * 4;
-    const int rr = r0 + lr;
-    const float* src = a.po + (hb + rr) * D + dd;
-    const int64_t sstride = (int64_t)a.rows_total * D;
-    float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    int sp = 0;
-    for (; sp + 4 <= nsplit; sp += 4) {  // four independent loads in flight
-      float4 v[4];
+  const int64_t sstride = (int64_t)a.rows_total * D;
+  const float* src = a.po + hb * D;
+  constexpr int NE = D / 32;  // elements per thread
+  int pe[NE];
+  float acc[NE];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = *(const float4*)(src + (sp + j) * sstride);
+  for (int i = 0; i < NE; ++i) {
+    pe[i] = qt * (8 * D) + i * 256 + tid;  // element of the block in accumulator layout
+    acc[i] = 0.0f;
+  }
+  int sp = 0;
+  for (; sp + 4 <= nsplit; sp += 4) {  // 4 * NE independent loads in flight
+    float v[4][NE];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float wj = wts[lr * 64 + sp + j];
-        acc4.x += v[j].x * wj;
-        acc4.y += v[j].y * wj;
-        acc4.z += v[j].z * wj;
-        acc4.w += v[j].w * wj;
-      }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < NE; ++i) v[j][i] = src[(sp + j) * sstride + pe[i]];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < NE; ++i) acc[i] += v[j][i] * wts[(pe[i] & 31) * 64 + sp + j];
+  }
+  for (; sp < nsplit; ++sp)
+#pragma unroll
+    for (int i = 0; i < NE; ++i) acc[i] += src[sp * sstride + pe[i]] * wts[(pe[i] & 31) * 64 + sp];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int ln = pe[i] & 63, dv = pe[i] >> 6;  // lane, db * 16 + v
+    const int rr = rb * 32 + (ln & 31);
+    if (rr < R) {
+      const int db = dv >> 4, v = dv & 15;
+      const int dd = db * 32 + 8 * (v >> 2) + 4 * (ln >> 5) + (v & 3);
+      const int g2 = rr / n, nd = rr % n;
+      a.out[attn_out_index<D>(a, nb + nd, (kh * a.G + g2) * D + dd)] = (uint16_t)f32_to_bf16(acc[i]);
     }
-    for (; sp < nsplit; ++sp) {
-      const float4 v = *(const float4*)(src + sp * sstride);
-      const float wj = wts[lr * 64 + sp];
-      acc4.x += v.x * wj;
-      acc4.y += v.y * wj;
-      acc4.z += v.z * wj;
-      acc4.w += v.w * wj;
-    }
-    const int g2 = rr / n, nd = rr % n;
-    // four consecutive columns stay within one 8-column group of the packed layout
-    uint16_t* op = a.out + attn_out_index<D>(a, nb + nd, (kh * a.G + g2) * D + dd);
-    op[0] = (uint16_t)f32_to_bf16(acc4.x);
-    op[1] = (uint16_t)f32_to_bf16(acc4.y);
-    op[2] = (uint16_t)f32_to_bf16(acc4.z);
-    op[3] = (uint16_t)f32_to_bf16(acc4.w);
   }
 }
 
-#ifndef TVP_ATTN_KR
-#define TVP_ATTN_KR 128  // keys per split (doubled while more than 64 splits would be needed)
-#endif
+// Key splits are sized so that one launch has about this many workgroups
+// (one per compute unit: a workgroup fills a CU's register file).
+constexpr int kAttnTargetGroups = 256;
 
 struct AttnPlan {
   int kr, max_splits, rows_total, nthreads;
@@ -364,13 +397,15 @@ struct AttnPlan {
 };
 
 // max_keys: largest ctx_len + n over the requests; r_max: largest G * n;
-// n_total: nodes of all requests.
-static AttnPlan attn_plan(int hkv, int G, int d, int r_max, int n_total, int max_keys) {
+// rows_total: partial rows over all requests (each request's G * n rounded
+// up to a multiple of 32).  Splits are multiples of the 64-key stage.
+static AttnPlan attn_plan(int hkv, int d, int r_max, int rows_total, int max_keys, int n_req) {
   AttnPlan p{};
-  p.kr = TVP_ATTN_KR;
+  const int target = std::max(1, kAttnTargetGroups / std::max(1, n_req * hkv));
+  p.kr = 64 * (int)ceil_div(std::max(max_keys, 1), 64LL * target);
   while (max_keys > 64 * p.kr) p.kr *= 2;  // at most 64 splits (merge weights live in LDS)
   p.max_splits = max_keys > 0 ? (max_keys + p.kr - 1) / p.kr : 1;
-  p.rows_total = G * n_total;
+  p.rows_total = rows_total;
   p.nthreads = r_max <= 128 ? 256 : 512;
   const size_t rows = (size_t)hkv * p.max_splits * p.rows_total;
   size_t off = 0;
@@ -398,9 +433,13 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
   if (r_max > 256 || r_max < 1) return TVP_ERR_SHAPE;
   if (out_packed && ri.node_ptr[ri.n_req] > 32) return TVP_ERR_SHAPE;
   const int n_req = ri.n_req;
-  const AttnPlan p = attn_plan(hkv, hq / hkv, d, r_max, ri.node_ptr[n_req], max_keys);
-  if (scratch_bytes < p.bytes) return TVP_ERR_WORKSPACE;
+  const int G = hq / hkv;
   AttnArgs a{};
+  a.pr.prow[0] = 0;
+  for (int i = 0; i < n_req; ++i)
+    a.pr.prow[i + 1] = a.pr.prow[i] + (int)align_up((size_t)G * (ri.node_ptr[i + 1] - ri.node_ptr[i]), 32);
+  const AttnPlan p = attn_plan(hkv, d, r_max, a.pr.prow[n_req], max_keys, n_req);
+  if (scratch_bytes < p.bytes) return TVP_ERR_WORKSPACE;
   a.q = q;
   a.kc = kc;
   a.vc = vc;
@@ -422,9 +461,9 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
   a.pl = (float*)(sb + p.off_pl);
   a.out = out;
   a.out_packed = out_packed;
-  a.row_blocks = (r_max + 15) / 16;
+  a.row_blocks = (r_max + 31) / 32;
   const dim3 grid((unsigned)(n_req * hkv * p.max_splits));
-  const dim3 mgrid((unsigned)(n_req * hkv * a.row_blocks));
+  const dim3 mgrid((unsigned)(n_req * hkv * a.row_blocks * 4));
   if (d == 128) {
     if (p.nthreads == 256) tree_attn_kernel<128, 256><<<grid, dim3(256), 0, stream>>>(a);
     else tree_attn_kernel<128, 512><<<grid, dim3(512), 0, stream>>>(a);
@@ -441,7 +480,12 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
 }
 
 size_t attention_scratch_bytes(int hkv, int G, int d, int r_max, int n_total, int max_keys) {
-  return attn_plan(hkv, G, d, r_max, n_total, max_keys).bytes;
+  // every request's rows are padded to a multiple of 32; the split count
+  // depends on the number of requests
+  size_t best = 0;
+  for (int nr = 1; nr <= std::min(kMaxReq, std::max(n_total, 1)); ++nr)
+    best = std::max(best, attn_plan(hkv, d, r_max, G * n_total + 31 * nr, max_keys, nr).bytes);
+  return best;
 }
 
 }  // namespace tvp

@@ -28,6 +28,9 @@ constexpr int kTileN = 32;      // channels per packed tile
 constexpr int kBlockK = 64;     // k per packed block
 constexpr int kBlockBytes = 3072;  // 32 x 64 x 12 bits
 
+// Record block (tile t, k-block j) of a packed weight, k-block-major.
+__host__ __device__ inline int64_t rec_block(int64_t t, int64_t j, int64_t n_tiles) { return j * n_tiles + t; }
+
 constexpr int kMaxReq = 64;      // requests per batched pass
 
 // Per-request bookkeeping passed by value to the batched kernels.
@@ -49,6 +52,16 @@ __device__ inline uint32_t f32_to_bf16(float f) {
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x0040u) & 0xFFFFu;
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.  Same result as f32_to_bf16 for every
+// non-NaN input.
+typedef __bf16 bf16x2_vec_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_vec_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_vec_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_vec_t));
 }
 
 // 16-byte streaming load (non-temporal hint: the weight stream is read once).

@@ -255,7 +255,8 @@ __global__ __launch_bounds__(64) void pack_write_kernel(const uint8_t* __restric
     }
     D[8 + s] = hn;
   }
-  uint4* blk = (uint4*)(rec_out + unit * (int64_t)kBlockBytes);
+  const int64_t n_tiles = (int64_t)gridDim.x / n_kb;  // one workgroup per (tile, k-block)
+  uint4* blk = (uint4*)(rec_out + rec_block(t, j, n_tiles) * (int64_t)kBlockBytes);
 #pragma unroll
   for (int s = 0; s < 3; ++s) blk[s * 64 + l] = make_uint4(D[4 * s], D[4 * s + 1], D[4 * s + 2], D[4 * s + 3]);
 

@@ -263,7 +263,6 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
     tt[t] = min(t0 + t, a.n_tiles - 1);
     ewin[t] = a.escoff[(int64_t)tt[t] * a.n_kb + min(kb0 + min(lane, nblk), a.n_kb)];
     b2v[t] = a.b2[tt[t] * 32 + (lane & 31)];
-    asm volatile("" ::"v"(ewin[t]), "v"(b2v[t]));  // complete these loads before the ring starts
   }
   accv acc[TPW][NCH];
 #pragma unroll
@@ -286,15 +285,16 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
   uint4 A[RD][KS];
   uint32_t E[RD][TPW];
 
-  auto issue_recs = [&](int i, int slot) {
+  auto issue_rec_only = [&](int i, int slot) {
     const int j = kb0 + i;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const int64_t un = (int64_t)tt[t] * a.n_kb + j;
-      const uint4* blk = (const uint4*)(a.rec + un * kBlockBytes);
+      const uint4* blk = (const uint4*)(a.rec + rec_block(tt[t], j, a.n_tiles) * kBlockBytes);
 #pragma unroll
       for (int q = 0; q < 3; ++q) R[slot][t][q] = load_nt(blk + q * 64 + lane);
     }
+  };
+  auto issue_esc = [&](int i, int slot) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const uint32_t eo = __builtin_amdgcn_readlane(ewin[t], i);
@@ -304,16 +304,23 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
       E[slot][t] = a.esc[(uint32_t)lane < ec ? eo + lane : eo];
     }
   };
+  auto issue_recs = [&](int i, int slot) {
+    issue_rec_only(i, slot);
+    issue_esc(i, slot);
+  };
   // full blocks: every activation load is in range
-  auto issue_fast = [&](int i, int slot) {
-    i = min(i, nfast - 1);  // past the end: re-read the last block (cached), result unused
-    issue_recs(i, slot);
+  auto issue_act_fast = [&](int i, int slot) {
     const int j = kb0 + i;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int64_t k = 64LL * j + (MT == 32 ? 16 : 32) * ks + xsub;
       A[slot][ks] = *(const uint4*)(xr + (k >> 3) * 256);
     }
+  };
+  auto issue_fast = [&](int i, int slot) {
+    i = min(i, nfast - 1);  // past the end: re-read the last block (cached), result unused
+    issue_recs(i, slot);
+    issue_act_fast(i, slot);
   };
   auto issue_tail = [&](int i, int slot) {
     issue_recs(i, slot);
@@ -374,25 +381,36 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
     lds_order();
   };
 
-  // Tasks where some tile block has more escapes than lanes take a simple
-  // unpipelined loop; all others stream through the register ring, whose
-  // body then holds no loop with loads of its own.
-  uint32_t mx = 0;
+  // The first blocks' records and activations need no escape offsets: they
+  // are issued before the wait for the offsets, so that wait overlaps them
+  // (all on one straight path, so the wait counts stay exact).
+  if (nfast > 0) {
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const uint32_t nxt = __shfl_down(ewin[t], 1);
-    const uint32_t c = lane < nblk ? nxt - ewin[t] : 0u;
-    mx = c > mx ? c : mx;
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t o = __shfl_xor(mx, off);
-    mx = o > mx ? o : mx;
-  }
-  const bool slow = __builtin_amdgcn_readfirstlane(mx) > 64u;
-  if (!slow) {
-    if (nfast > 0) {
+    for (int p = 0; p < RD - 1; ++p) {
+      issue_rec_only(min(p, nfast - 1), p);
+      issue_act_fast(min(p, nfast - 1), p);
+    }
 #pragma unroll
-      for (int p = 0; p < RD - 1; ++p) issue_fast(p, p);
+    for (int t = 0; t < TPW; ++t) asm volatile("" ::"v"(ewin[t]), "v"(b2v[t]));  // offsets and bases arrived
+
+    // Tasks where some tile block has more escapes than lanes take a simple
+    // unpipelined loop; all others stream through the register ring, whose
+    // body then holds no loop with loads of its own.
+    uint32_t mx = 0;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const uint32_t nxt = __shfl_down(ewin[t], 1);
+      const uint32_t c = lane < nblk ? nxt - ewin[t] : 0u;
+      mx = c > mx ? c : mx;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t o = __shfl_xor(mx, off);
+      mx = o > mx ? o : mx;
+    }
+    const bool slow = __builtin_amdgcn_readfirstlane(mx) > 64u;
+    if (!slow) {
+#pragma unroll
+      for (int p = 0; p < RD - 1; ++p) issue_esc(min(p, nfast - 1), p);
       for (int i0 = 0; i0 < nfast; i0 += RD) {
 #pragma unroll
         for (int r = 0; r < RD; ++r) {
@@ -400,13 +418,15 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
           if (i0 + r < nfast) process(i0 + r, r, std::false_type{});
         }
       }
-    }
-  } else {
-    for (int i = 0; i < nfast; ++i) {
-      issue_fast(i, 0);
-      process(i, 0, std::true_type{});
+    } else {
+      for (int i = 0; i < nfast; ++i) {
+        issue_fast(i, 0);
+        process(i, 0, std::true_type{});
+      }
     }
   }
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) asm volatile("" ::"v"(ewin[t]), "v"(b2v[t]));
   if (ragged_tail) {
     issue_tail(nblk - 1, 0);
     process(nblk - 1, 0, std::true_type{});
@@ -510,8 +530,8 @@ __global__ __launch_bounds__(256) void w12_wide_kernel(GemmArgs a) {
     for (int u = 0; u < 2; ++u) {
       e[u] = 0;
       if (st < nsteps && unit_ok(st, u)) {
-        const int64_t un = (int64_t)unit_tile(u) * a.n_kb + unit_blk(st, u);
-        const uint4* blk = (const uint4*)(a.rec + un * kBlockBytes);
+        const uint4* blk =
+            (const uint4*)(a.rec + rec_block(unit_tile(u), unit_blk(st, u), a.n_tiles) * kBlockBytes);
 #pragma unroll
         for (int i = 0; i < 3; ++i) r[u][i] = load_nt(blk + i * 64 + lane);
         if ((uint32_t)lane < c[u]) e[u] = a.esc[o[u] + lane];
