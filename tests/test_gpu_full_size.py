@@ -1,0 +1,78 @@
+"""The verification pass at the 27B-like shapes, in the launch configuration
+bench.py times: hidden 5120, 40 query / 8 KV heads of 128, SwiGLU 17408, the
+full 151936-token LM head, a 4096-token context and a 32-node best-first
+tree -- one decoder layer (the oracle's fp64 cost of all 64 would not fit a
+test).  Logits are compared on every row within 2e-3 max-abs-rel, greedy
+tokens on decidable rows, acceptance where determined; the pass is bitwise
+reproducible."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import model as om
+from oracle.accept import accept as oaccept
+from oracle.bf16 import from_bits
+from synth import best_first_topology
+from synth.configs import CONFIGS, gen_kv_context, gen_model
+from synth.trees import assign_tokens_by_depth
+from synth.weights import bf16_bits_numpy
+from tests.gpu_util import to_i32
+from tests.helpers import oracle_topk_fn
+from tests.parity import acceptance_ok, check_logits
+
+pytestmark = pytest.mark.gpu
+
+
+class _Rows:
+    """Embedding rows converted on demand (the full fp64 table would be 6 GB)."""
+
+    def __init__(self, bits: np.ndarray):
+        self.bits = bits
+
+    def __getitem__(self, idx):
+        return from_bits(self.bits[idx])
+
+
+def test_verify_step_27b_shapes_one_layer(cuda):
+    import tree_verification_pass_amd as tvp
+    from tree_verification_pass_amd.model import DeviceModel, Dims
+
+    cfg = dataclasses.replace(CONFIGS["27b"], n_layers=1)
+    L, s_max, n = cfg.ctx_len, cfg.ctx_len + 64, cfg.n_nodes
+    print(f"[full size] 1 layer, ctx {L}, {n} nodes, vocab {cfg.vocab}", flush=True)
+    m = gen_model(cfg, 5, cuda, "random")
+    kc, vc = gen_kv_context(cfg, 5, 0, L, s_max, device=cuda)
+    dm = DeviceModel(Dims.of(cfg), m.embed, m.final_norm, m.lm_head, lambda l: m.layers[l],
+                     lambda l: (kc, vc), s_max=s_max, max_nodes=n)
+    layer_bits = {k: bf16_bits_numpy(v) for k, v in m.layers[0].items()}
+    orc = om.OracleModel(om.Dims.of(cfg), _Rows(bf16_bits_numpy(m.embed)),
+                         [{k: from_bits(v) for k, v in layer_bits.items()}],
+                         from_bits(bf16_bits_numpy(m.final_norm)), from_bits(bf16_bits_numpy(m.lm_head)))
+    cache = om.KVCache.from_bits([bf16_bits_numpy(kc)], [bf16_bits_numpy(vc)])
+    rng = np.random.default_rng(6)
+    parents, rank, _ = best_first_topology(rng, n)
+    # draft tokens from the oracle's own top-4 at each parent, level by level
+    tokens = assign_tokens_by_depth(rng, parents, rank, int(rng.integers(cfg.vocab)), cfg.vocab,
+                                    oracle_topk_fn(orc, cache, L), 0.7)
+    print("  oracle forward", flush=True)
+    ref = om.verify(orc, cache, L, tokens, parents)
+    print("  gpu pass", flush=True)
+    res = tvp.verify_step(dm.plan, L, to_i32(tokens), to_i32(parents), commit=False, want_logits=True)
+    res2 = tvp.verify_step(dm.plan, L, to_i32(tokens), to_i32(parents), commit=False, want_logits=True)
+    torch.cuda.synchronize()
+    g = res.logits.cpu().numpy().astype(np.float64)
+    chk = check_logits(g, ref["logits"], tol=2e-3)
+    print(f"  logits max_abs_rel={chk['max_abs_rel']:.2e} undecidable={chk['undecidable_frac']:.3f} "
+          f"accepted={int(res.n_accepted.item())} (oracle {ref['n_accepted']})", flush=True)
+    assert chk["logits_ok"], chk["max_abs_rel"]
+    assert chk["argmax_ok"], chk["bad_argmax_rows"]
+    am = res.argmax.cpu().numpy()
+    assert np.array_equal(am, np.argmax(res.logits.cpu().numpy(), axis=1))
+    p_own, a_own, b_own = oaccept(am, tokens, parents)
+    assert int(res.n_accepted.item()) == a_own and int(res.bonus.item()) == b_own
+    assert res.path.cpu().numpy()[: a_own + 1].tolist() == p_own
+    assert acceptance_ok(am, ref["argmax"], tokens, parents, chk["decidable"])
+    assert torch.equal(res.logits, res2.logits)

@@ -5,22 +5,21 @@
 
 namespace tvp {
 
-// Zero region of a GEMM: completion counters (kGemmMaxGroups entries), then
-// argmax buckets (192 rows x 64 u64).  Zero on entry, left zero by every call.
+// Zero region of a GEMM: completion counters (kGemmMaxGroups entries).
+// Zero on entry, left zero by every call.
 constexpr size_t kGemmMaxGroups = 32768;
-constexpr size_t kGemmKeyBytes = 192 * 64 * 8;
 constexpr size_t kGemmZeroBytes = 256 * 1024;
-static_assert(kGemmMaxGroups * 4 + kGemmKeyBytes <= kGemmZeroBytes, "zero region");
+static_assert(kGemmMaxGroups * 4 <= kGemmZeroBytes, "zero region");
 
-// W12 GEMM with caller-provided counters (`cnt`, groups entries), argmax
-// buckets (`keys`) and scratch.  Activations come row-major in `x` or, for
+// W12 GEMM with caller-provided counters (`cnt`, groups entries) and scratch
+// (which also holds the argmax key slots).  Activations come row-major in `x` or, for
 // m <= 32, already in the packed layout in `xp` (then `x` is unused).
 // `y_packed`: the SwiGLU epilogue writes its output packed (m <= 32).
 // `ksplit` > 1 (skinny path, epilogue kEpiPartial only) also splits K over
 // workgroups.
 int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
-             const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, unsigned long long* keys, void* scratch,
-             size_t scratch_bytes, hipStream_t stream, int ksplit = 1);
+             const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, void* scratch, size_t scratch_bytes,
+             hipStream_t stream, int ksplit = 1);
 
 // Internal epilogue (not part of the ABI): each K slice's fp32 partial result
 // goes to y = P[slice][m][ldy] (canonical columns); the consumer sums the
@@ -38,8 +37,8 @@ inline int64_t xpack_elems(int64_t k_in) { return ((k_in + 63) / 64) * 2048; }
 bool gemm_is_skinny(int64_t m, const tvp_w12_packed* w);
 // Number of K slices gemm_run uses for `ksplit` (clamped so none is empty).
 int gemm_ksplits(int64_t m, const tvp_w12_packed* w, int ksplit);
-// Counter entries and scratch bytes gemm_run needs for m rows.
-void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes);
+// Counter entries and scratch bytes gemm_run needs for m rows (and `ksplit`).
+void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes, int ksplit = 1);
 
 int launch_tree_prep(const int32_t* parents, const ReqInfo& ri, int32_t s_req, uint64_t* anc,
                      int32_t* pos, int32_t* slot, int32_t* status, hipStream_t stream);

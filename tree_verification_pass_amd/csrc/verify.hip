@@ -20,11 +20,8 @@ namespace tvp {
 
 constexpr int kMaxLayers = 120;
 
-#ifndef TVP_KSPLIT_O
-#define TVP_KSPLIT_O 2  // K slices of the O projection (packed path)
-#endif
-#ifndef TVP_KSPLIT_DOWN
-#define TVP_KSPLIT_DOWN 4  // K slices of the down projection (packed path)
+#ifndef TVP_KSPLIT_MAX
+#define TVP_KSPLIT_MAX 16  // most K slices of the O and down projections (packed path)
 #endif
 
 // ------------------------------------------------------------ small kernels
@@ -68,13 +65,24 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict
     w[0] = v.x, w[1] = v.y, w[2] = v.z, w[3] = v.w;
     if (S > 0) {
       float acc[8];
-      for (int sl = 0; sl < S; ++sl) {
-        const float4 p0 = *(const float4*)(pr + sl * pstride + 8 * c);
-        const float4 p1 = *(const float4*)(pr + sl * pstride + 8 * c + 4);
+      auto add_slice = [&](int sl, const float4& p0, const float4& p1) {
         const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = sl == 0 ? pv[e] : acc[e] + pv[e];
+      };
+      int sl = 0;
+      for (; sl + 4 <= S; sl += 4) {  // 8 independent loads in flight, added in slice order
+        float4 q0[4], q1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          q0[j] = *(const float4*)(pr + (sl + j) * pstride + 8 * c);
+          q1[j] = *(const float4*)(pr + (sl + j) * pstride + 8 * c + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) add_slice(sl + j, q0[j], q1[j]);
       }
+      for (; sl < S; ++sl)
+        add_slice(sl, *(const float4*)(pr + sl * pstride + 8 * c), *(const float4*)(pr + sl * pstride + 8 * c + 4));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t lo = f32_to_bf16(bf16_to_f32(w[e] & 0xFFFFu) + acc[2 * e]);
@@ -254,7 +262,7 @@ struct tvp_plan {
   int ld_h, ld_q, ld_u;
   bool pack_ok;  // every GEMM takes the skinny path at <= 32 rows
   // workspace layout
-  size_t off_gcnt, off_gkeys, zero_end;
+  size_t off_gcnt, zero_end;
   size_t off_h, off_a, off_q, off_o, off_u;
   size_t off_anc, off_pos, off_slot, off_tstat, off_bad;
   size_t off_gscr, gscr_bytes;
@@ -311,22 +319,27 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   // counters and scratch over every GEMM at every row count up to max_nodes
   int gmax = 1;
   size_t gscr = 256;
-  auto need = [&](const tvp_w12_packed& w) {
+  auto need = [&](const tvp_w12_packed& w, bool sliced) {
     for (int m = 1; m <= max_nodes; ++m) {
       int g;
       size_t b;
       gemm_requirements(m, &w, &g, &b);
       gmax = std::max(gmax, g);
       gscr = std::max(gscr, b);
+      if (sliced && m <= 32) {  // the O and down projections' K-sliced launches
+        gemm_requirements(m, &w, &g, &b, TVP_KSPLIT_MAX);
+        gmax = std::max(gmax, g);
+        gscr = std::max(gscr, b);
+      }
     }
   };
-  need(d->lm_head);
+  need(d->lm_head, false);
   p->pack_ok = gemm_is_skinny(32, &d->lm_head);
   for (int l = 0; l < d->n_layers; ++l) {
-    need(p->layers[l].wqkv);
-    need(p->layers[l].wo);
-    need(p->layers[l].wgu);
-    need(p->layers[l].wdown);
+    need(p->layers[l].wqkv, false);
+    need(p->layers[l].wo, true);
+    need(p->layers[l].wgu, false);
+    need(p->layers[l].wdown, true);
     p->pack_ok = p->pack_ok && gemm_is_skinny(32, &p->layers[l].wqkv) && gemm_is_skinny(32, &p->layers[l].wo) &&
                  gemm_is_skinny(32, &p->layers[l].wgu) && gemm_is_skinny(32, &p->layers[l].wdown);
   }
@@ -337,8 +350,6 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   size_t off = 0;
   p->off_gcnt = off;
   off = align_up(off + (size_t)gmax * 4, 256);
-  p->off_gkeys = off;
-  off = align_up(off + kGemmKeyBytes, 256);
   p->zero_end = off;
   p->off_h = off;
   off = align_up(off + (size_t)mn * p->ld_h * 2, 256);
@@ -364,12 +375,10 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   // slices' partial sums reduced by the fused residual + RMSNorm kernel
   p->ks_o = 1;
   p->ks_down = 1;
-  if (p->pack_ok) {
-    p->ks_o = TVP_KSPLIT_O;
-    p->ks_down = TVP_KSPLIT_DOWN;
+  if (p->pack_ok) {  // the largest slice counts any layer uses (they size the partial buffer)
     for (int l = 0; l < d->n_layers; ++l) {
-      p->ks_o = std::min(p->ks_o, gemm_ksplits(32, &p->layers[l].wo, TVP_KSPLIT_O));
-      p->ks_down = std::min(p->ks_down, gemm_ksplits(32, &p->layers[l].wdown, TVP_KSPLIT_DOWN));
+      p->ks_o = std::max(p->ks_o, gemm_ksplits(32, &p->layers[l].wo, TVP_KSPLIT_MAX));
+      p->ks_down = std::max(p->ks_down, gemm_ksplits(32, &p->layers[l].wdown, TVP_KSPLIT_MAX));
     }
   }
   p->off_part = off;
@@ -409,7 +418,6 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   }
   uint8_t* w = (uint8_t*)ws;
   uint32_t* gcnt = (uint32_t*)(w + p->off_gcnt);
-  unsigned long long* gkeys = (unsigned long long*)(w + p->off_gkeys);
   uint16_t* h = (uint16_t*)(w + p->off_h);
   uint16_t* a = (uint16_t*)(w + p->off_a);
   uint16_t* q = (uint16_t*)(w + p->off_q);
@@ -446,7 +454,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     e.v_cache = L.v_cache;
     e.s_stride = d.s_max;
     e.rope_theta = d.rope_theta;
-    if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wqkv, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes,
+    if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wqkv, &e, 0, gcnt, gscr, p->gscr_bytes,
                        stream)))
       return st;
     if ((st = launch_tree_attention(q, L.k_cache, L.v_cache, d.s_max, ri, s_req, anc, hq, hkv, hd, G * max_n,
@@ -458,18 +466,18 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
       e.mode = kEpiPartial;
       e.y = part;
       e.ldy = H;
-      if ((st = gemm_run(o, o, n_total, p->ld_q, &L.wo, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes, stream,
-                         p->ks_o)))
+      if ((st = gemm_run(o, o, n_total, p->ld_q, &L.wo, &e, 0, gcnt, gscr, p->gscr_bytes, stream,
+                         TVP_KSPLIT_MAX)))
         return st;
-      launch_norm(part, p->ks_o, pstride, H, h, p->ld_h, L.ffn_norm, H, d.norm_eps, a, p->ld_h, 1, n_total,
-                  stream);
+      launch_norm(part, gemm_ksplits(n_total, &L.wo, TVP_KSPLIT_MAX), pstride, H, h, p->ld_h, L.ffn_norm, H,
+                  d.norm_eps, a, p->ld_h, 1, n_total, stream);
     } else {
       e.mode = TVP_EPI_RESID;
       e.y = h;
       e.ldy = p->ld_h;
       e.resid = h;
       e.ldr = p->ld_h;
-      if ((st = gemm_run(o, nullptr, n_total, p->ld_q, &L.wo, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes, stream)))
+      if ((st = gemm_run(o, nullptr, n_total, p->ld_q, &L.wo, &e, 0, gcnt, gscr, p->gscr_bytes, stream)))
         return st;
       launch_norm(part, 0, pstride, H, h, p->ld_h, L.ffn_norm, H, d.norm_eps, a, p->ld_h, 0, n_total, stream);
     }
@@ -478,7 +486,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     e.mode = TVP_EPI_SWIGLU;
     e.y = u;
     e.ldy = p->ld_u;
-    if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wgu, &e, pk, gcnt, gkeys, gscr, p->gscr_bytes,
+    if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wgu, &e, pk, gcnt, gscr, p->gscr_bytes,
                        stream)))
       return st;
     // down projection + residual, then the next layer's attention norm (or the final norm)
@@ -487,18 +495,18 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
       e.mode = kEpiPartial;
       e.y = part;
       e.ldy = H;
-      if ((st = gemm_run(u, u, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes, stream,
-                         p->ks_down)))
+      if ((st = gemm_run(u, u, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gscr, p->gscr_bytes, stream,
+                         TVP_KSPLIT_MAX)))
         return st;
-      launch_norm(part, p->ks_down, pstride, H, h, p->ld_h, next_norm, H, d.norm_eps, a, p->ld_h, 1, n_total,
-                  stream);
+      launch_norm(part, gemm_ksplits(n_total, &L.wdown, TVP_KSPLIT_MAX), pstride, H, h, p->ld_h, next_norm, H,
+                  d.norm_eps, a, p->ld_h, 1, n_total, stream);
     } else {
       e.mode = TVP_EPI_RESID;
       e.y = h;
       e.ldy = p->ld_h;
       e.resid = h;
       e.ldr = p->ld_h;
-      if ((st = gemm_run(u, nullptr, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes,
+      if ((st = gemm_run(u, nullptr, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gscr, p->gscr_bytes,
                          stream)))
         return st;
       launch_norm(part, 0, pstride, H, h, p->ld_h, next_norm, H, d.norm_eps, a, p->ld_h, 0, n_total, stream);
@@ -510,7 +518,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   e.argmax = out->argmax;
   e.logits = out->logits;
   e.ldl = d.vocab;
-  if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &d.lm_head, &e, 0, gcnt, gkeys, gscr, p->gscr_bytes,
+  if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &d.lm_head, &e, 0, gcnt, gscr, p->gscr_bytes,
                      stream)))
     return st;
   accept_kernel<<<dim3(ri.n_req), dim3(64), 0, stream>>>(out->argmax, tokens, parents, ri, bad, out->path,

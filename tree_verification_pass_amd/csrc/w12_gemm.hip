@@ -40,10 +40,16 @@ struct GemmArgs {
   const int32_t* rowmap;
   int n_tiles, n_kb, n_pad;
   int groups, splits, kbs, ntasks;
-  int kps;  // skinny: K blocks per K slice (slices = splits)
+  int kps;    // skinny: K blocks per slice of a split group
+  int kbs_split;  // skinny, partial-sum epilogue: K blocks per wavefront of a slice
+  int gfull;      // skinny: groups [0, gfull) have one workgroup each; each later
+                  // group is shared by `parts` workgroups, one per channel part
+  int parts;
   float* part;
   uint32_t* cnt;
-  unsigned long long* keys;  // ARGMAX: [m][64] packed (value, -id) maxima, zero on entry
+  unsigned long long* keys;  // ARGMAX: [slot][m] packed (value, -id) maxima, one slot per workgroup that
+                             // applies the epilogue (every slot written, no zeroing)
+  int key_slots;
   int mode;
   void* y;
   int64_t ldy;
@@ -62,7 +68,7 @@ struct GemmArgs {
   int y_packed;  // SWIGLU: write y in the packed activation layout (rows <= 32)
 };
 
-constexpr int kArgmaxBuckets = 64;
+constexpr int kArgmaxMaxRows = 192;
 
 // Row-major x [m][ldx] -> packed (rows >= m and columns >= k_in are zero).
 __global__ __launch_bounds__(256) void pack_x_kernel(const uint16_t* __restrict__ x, int64_t ldx, int m,
@@ -119,8 +125,10 @@ __device__ inline unsigned long long argmax_key(float v, int32_t id) {
 // Epilogue over packed channels [c0, c0+nc) x rows [0, M) by `nthr` threads
 // (thread index `tid`), reading fp32 results through V(row, col).
 template <int MODE, typename Get>
-__device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int tid, int nthr, int bucket,
-                                Get V, int slice = 0) {
+__device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int tid, int nthr, int key_slot,
+                                Get V, int slice = 0, uint32_t cmask = 0xFFFFFFFFu) {
+  // cmask: the channels (bit c of each 32-channel tile) this workgroup owns
+  auto owned = [&](int col) { return (cmask >> (col & 31)) & 1u; };
   if constexpr (MODE == kEpiPartial) {
     float* P = (float*)a.y + (int64_t)slice * M * a.ldy;
     for (int idx = tid; idx < M * nc; idx += nthr) {
@@ -132,7 +140,7 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
     for (int idx = tid; idx < M * nc; idx += nthr) {
       const int row = idx / nc, col = c0 + idx % nc;
       const int32_t r = a.rowmap[col];
-      if (r < 0) continue;
+      if (r < 0 || !owned(col)) continue;
       const float v = V(row, col);
       if constexpr (MODE == TVP_EPI_F32) {
         ((float*)a.y)[row * a.ldy + r] = v;
@@ -149,7 +157,7 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
       const int row = idx / half, p = idx % half;
       const int col = c0 + (p / 16) * 32 + (p % 16);
       const int32_t r = a.rowmap[col];
-      if (r < 0) continue;
+      if (r < 0 || !owned(col)) continue;
       const float gv = V(row, col), uv = V(row, col + 16);
       const uint16_t o = (uint16_t)f32_to_bf16(silu_f32(gv) * uv);
       if (a.y_packed) ((uint16_t*)a.y)[xpack_index(row, r)] = o;
@@ -161,7 +169,7 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
     for (int idx = tid; idx < M * nc; idx += nthr) {
       const int row = idx / nc, col = c0 + idx % nc;
       const int t = col / 32, c = col % 32;
-      if (t >= a.n_tiles) continue;
+      if (t >= a.n_tiles || !owned(col)) continue;
       if (t < rot_tiles) {
         if (c >= 16) continue;
         const int head = t / tph, u = t % tph;
@@ -186,13 +194,14 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
         a.vc[((int64_t)kh * a.s_stride + a.slot[row]) * d + dim] = (uint16_t)f32_to_bf16(V(row, col));
       }
     }
-  } else {  // ARGMAX: per row the best (value, smallest id), merged by a 64-bit atomic max
+  } else {  // ARGMAX: per row the best (value, smallest id) of this workgroup, to its key slot
+    __shared__ unsigned long long red[8][kArgmaxMaxRows];
     for (int row = 0; row < M; ++row) {
       unsigned long long best = 0ull;
       for (int cc = tid; cc < nc; cc += nthr) {
         const int col = c0 + cc;
         const int32_t r = a.rowmap[col];
-        if (r < 0) continue;
+        if (r < 0 || !owned(col)) continue;
         const float v = V(row, col);
         if (a.logits) a.logits[row * a.ldl + r] = v;
         const unsigned long long k = argmax_key(v, r);
@@ -202,24 +211,38 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
         const unsigned long long o = __shfl_xor(best, off);
         best = o > best ? o : best;
       }
-      if ((tid & 63) == 0 && best) atomicMax(&a.keys[row * kArgmaxBuckets + bucket], best);
+      if ((tid & 63) == 0) red[tid >> 6][row] = best;
+    }
+    __syncthreads();
+    for (int row = tid; row < M; row += nthr) {
+      unsigned long long best = 0ull;
+      for (int w = 0; w < (nthr >> 6); ++w) best = red[w][row] > best ? red[w][row] : best;
+      a.keys[(int64_t)key_slot * M + row] = best;
     }
   }
 }
 
-// One workgroup: argmax[row] from the bucket maxima, then the buckets are
-// cleared for the next launch.
-__global__ __launch_bounds__(256) void argmax_finalize_kernel(unsigned long long* __restrict__ keys, int m,
-                                                              int32_t* __restrict__ argmax) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int row = wave; row < m; row += 4) {
-    unsigned long long k = keys[row * kArgmaxBuckets + lane];
-    for (int off = 32; off > 0; off >>= 1) {
-      const unsigned long long o = __shfl_xor(k, off);
-      k = o > k ? o : k;
-    }
-    if (lane == 0) argmax[row] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)) : 0;
-    keys[row * kArgmaxBuckets + lane] = 0ull;
+// One workgroup per row: argmax[row] from the key slots (max over slots, so
+// the order does not matter).
+__global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned long long* __restrict__ keys,
+                                                              int slots, int m, int32_t* __restrict__ argmax) {
+  __shared__ unsigned long long wmax[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  unsigned long long k = 0ull;
+  for (int s = tid; s < slots; s += 256) {
+    const unsigned long long v = keys[(int64_t)s * m + row];
+    k = v > k ? v : k;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned long long o = __shfl_xor(k, off);
+    k = o > k ? o : k;
+  }
+  if ((tid & 63) == 0) wmax[tid >> 6] = k;
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) k = wmax[w] > k ? wmax[w] : k;
+    k = wmax[0] > k ? wmax[0] : k;
+    argmax[row] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)) : 0;
   }
 }
 
@@ -246,11 +269,31 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KW = blockDim.x >> 6;
-  const int grp = blockIdx.x % a.groups, slice = blockIdx.x / a.groups;
+  // Workgroup -> work: with the partial-sum epilogue every group is cut into
+  // `splits` K slices; otherwise groups [0, gfull) have a workgroup each and
+  // every later group is shared by `parts` workgroups, each owning a part of
+  // the tile channels over the whole K range (no partial sums to combine).
+  const int b = blockIdx.x;
+  int grp = b, slice = 0, part = 0, w16 = 16;  // w16: channels per half-tile owned
+  if (MODE == kEpiPartial) {
+    grp = b / a.splits;
+    slice = b % a.splits;
+  } else if (b >= a.gfull) {
+    grp = a.gfull + (b - a.gfull) / a.parts;
+    part = (b - a.gfull) % a.parts;
+    w16 = 16 / a.parts;
+  }
+  const uint32_t half_mask = (w16 == 16 ? 0xFFFFu : ((1u << w16) - 1u)) << (part * w16);
+  const uint32_t cmask = half_mask | (half_mask << 16);
+  // lanes of channels this workgroup does not own read a lane it owns (same
+  // addresses, so no extra memory traffic); their results are never stored
+  const int rlane = (lane & ~15) | (part * w16 + (lane & (w16 - 1)));
   const int t0 = grp * TPW;
-  const int ks1 = min(a.n_kb, (slice + 1) * a.kps);  // this workgroup's K slice ends here
-  const int kb0 = slice * a.kps + wave * a.kbs;
-  const int kb1 = min(ks1, kb0 + a.kbs);
+  const int ks0 = MODE == kEpiPartial ? slice * a.kps : 0;
+  const int ks1 = MODE == kEpiPartial ? min(a.n_kb, ks0 + a.kps) : a.n_kb;  // this workgroup's K range
+  const int kbs = MODE == kEpiPartial ? a.kbs_split : a.kbs;
+  const int kb0 = ks0 + wave * kbs;
+  const int kb1 = min(ks1, kb0 + kbs);
   const int nblk = kb1 > kb0 ? kb1 - kb0 : 0;  // <= 63
 
   // Tiles past the end are computed on a clamped tile and dropped at the end,
@@ -291,7 +334,7 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
     for (int t = 0; t < TPW; ++t) {
       const uint4* blk = (const uint4*)(a.rec + rec_block(tt[t], j, a.n_tiles) * kBlockBytes);
 #pragma unroll
-      for (int q = 0; q < 3; ++q) R[slot][t][q] = load_nt(blk + q * 64 + lane);
+      for (int q = 0; q < 3; ++q) R[slot][t][q] = load_nt(blk + q * 64 + rlane);
     }
   };
   auto issue_esc = [&](int i, int slot) {
@@ -454,14 +497,14 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
         if (row < M) P[(wave * M + row) * NC + col] = acc[t][ch][v];
       }
   __syncthreads();
-  epilogue<MODE>(a, t0 * 32, min(NC, a.n_pad - t0 * 32), M, threadIdx.x, KW * 64, grp & (kArgmaxBuckets - 1),
-                 [&](int row, int col) {
-                   const int c = col - t0 * 32;
-                   float v = 0.0f;
-                   for (int w = 0; w < KW; ++w) v += P[(w * M + row) * NC + c];
-                   return v;
-                 },
-                 slice);
+  auto sum_waves = [&](int row, int col) {
+    const int c = col - t0 * 32;
+    float v = 0.0f;
+    for (int w = 0; w < KW; ++w) v += P[(w * M + row) * NC + c];
+    return v;
+  };
+  const int nc = min(NC, a.n_pad - t0 * 32);
+  epilogue<MODE>(a, t0 * 32, nc, M, threadIdx.x, KW * 64, blockIdx.x, sum_waves, slice, cmask);
 }
 
 template <int ROWS>
@@ -692,7 +735,7 @@ __global__ __launch_bounds__(256) void w12_wide_kernel(GemmArgs a) {
     for (int s = 0; s < a.splits; ++s) v += a.part[((int64_t)s * M + row) * a.n_pad + col];
     return v;
   };
-  const int bucket = g & (kArgmaxBuckets - 1);
+  const int bucket = g;  // key slot: one per group
   switch (a.mode) {
     case TVP_EPI_F32: epilogue<TVP_EPI_F32>(a, c0, nc, M, tid, 256, bucket, red); break;
     case TVP_EPI_BF16: epilogue<TVP_EPI_BF16>(a, c0, nc, M, tid, 256, bucket, red); break;
@@ -706,7 +749,8 @@ __global__ __launch_bounds__(256) void w12_wide_kernel(GemmArgs a) {
 struct GemmPlan {
   bool skinny;
   int MT, RB, TPW, RD, KW, TG, groups, splits, kbs, kps, ntasks, grid;
-  size_t scratch_bytes;
+  int gfull, parts, kbs_split, key_slots;
+  size_t keys_off, scratch_bytes;
 };
 
 // Work decomposition.  Skinny (m <= 32): one workgroup per TPW tiles whose KW
@@ -733,10 +777,23 @@ constexpr int kWideTargetGroups = 1024;
 #define TVP_RD2 2  // register-ring depth, two tiles per workgroup
 #endif
 
+// Compute units the skinny decomposition balances over (MI355X: 256).
+constexpr int kNumCUs = 256;
+
+// Per-CU cost, in K blocks, of `gsplit` groups cut into `s` K slices of
+// `kps` blocks (partial-sum epilogue): the busiest CU's blocks plus a fixed
+// cost per workgroup; a CU holding a single workgroup streams slower.
+static double slice_cost(int gsplit, int s, int kps) {
+  const int per_cu = (int)ceil_div((int64_t)gsplit * s, kNumCUs);
+  const double cost = (double)per_cu * kps + 2.0 * per_cu;
+  return per_cu <= 1 ? 1.5 * cost : cost;
+}
+
 static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1) {
   GemmPlan p{};
   const int64_t n_pad = (int64_t)w->n_tiles * 32;
   const int nkb = w->n_kb;
+  const bool partial = ksplit > 1;  // partial-sum epilogue: every group is cut into K slices
   p.MT = m <= 16 ? 16 : 32;
   p.RB = (int)ceil_div(m, p.MT);
   p.skinny = m <= 32 && nkb <= 8 * 63;
@@ -745,16 +802,37 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1) {
     p.RD = p.TPW == 2 ? TVP_RD2 : TVP_RD1;
     p.TG = p.TPW;
     p.groups = (int)ceil_div(w->n_tiles, p.TPW);
-    // K slices over workgroups (partial-sum epilogue only), none empty
-    int sl = std::max(1, std::min(ksplit, std::max(nkb, 1)));
-    p.kps = nkb > 0 ? (int)ceil_div(nkb, sl) : 0;
-    p.splits = p.kps > 0 ? (int)ceil_div(nkb, p.kps) : 1;
-    p.KW = p.groups * p.splits >= TVP_KW_SWITCH ? TVP_KW_MANY : TVP_KW_FEW;
-    if (p.kps > 4 * 63) p.KW = 8;
-    p.KW = std::max(1, std::min(p.KW, p.kps));
-    p.kbs = p.kps > 0 ? (int)ceil_div(p.kps, p.KW) : 0;
-    p.ntasks = p.groups * p.splits;
-    p.grid = p.ntasks;
+    p.splits = 1;
+    p.parts = 1;
+    p.kps = nkb;
+    if (partial) {
+      // K slices, summed in slice order by the consumer
+      int best_s = 1, best_kps = std::max(nkb, 1);
+      double best = 1e30;
+      for (int sl = 1; sl <= std::min(ksplit, 16) && nkb > 0; ++sl) {
+        const int kps = (int)ceil_div(nkb, sl);
+        if ((int)ceil_div(nkb, kps) != sl || (sl > 1 && kps < 2)) continue;
+        const double c = slice_cost(p.groups, sl, kps);
+        if (c < best - 1e-9) best = c, best_s = sl, best_kps = kps;
+      }
+      p.gfull = 0;
+      p.splits = best_s;
+      p.kps = nkb > 0 ? best_kps : 0;
+    } else {
+      // whole groups in multiples of the CU count; the rest shared by channel parts
+      p.gfull = p.groups >= kNumCUs ? (p.groups / kNumCUs) * kNumCUs : p.groups;
+      const int rest = p.groups - p.gfull;
+      while (rest > 0 && p.parts < 8 && rest * p.parts < kNumCUs) p.parts *= 2;
+    }
+    const int nwg = partial ? p.groups * p.splits : p.gfull + (p.groups - p.gfull) * p.parts;
+    const int krange = partial ? p.kps : nkb;
+    p.KW = nwg >= TVP_KW_SWITCH ? TVP_KW_MANY : TVP_KW_FEW;
+    if (krange > 4 * 63) p.KW = 8;
+    p.KW = std::max(1, std::min(p.KW, std::max(krange, 1)));
+    p.kbs = nkb > 0 ? (int)ceil_div(nkb, p.KW) : 0;
+    p.kbs_split = p.kps > 0 ? (int)ceil_div(p.kps, p.KW) : 0;
+    p.ntasks = nwg;
+    p.grid = nwg;
   } else {
     p.TPW = 1;
     p.RD = 0;
@@ -772,9 +850,12 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1) {
     p.ntasks = p.groups * p.splits;
     p.grid = p.ntasks;
   }
-  // skinny: room to pack row-major activations; wide: split-K partial sums
-  p.scratch_bytes = p.skinny ? align_up((size_t)std::max(nkb, 1) * 4096, 256)
-                             : align_up((size_t)p.splits * m * n_pad * 4, 256);
+  // skinny: room to pack row-major activations; wide: split-K partial sums;
+  // then the argmax key slots (one per workgroup / group)
+  p.key_slots = p.skinny ? p.grid : p.groups;
+  p.keys_off = p.skinny ? align_up((size_t)std::max(nkb, 1) * 4096, 256)
+                        : align_up((size_t)p.splits * m * n_pad * 4, 256);
+  p.scratch_bytes = p.keys_off + align_up((size_t)std::max(p.key_slots, 1) * m * 8, 256);
   return p;
 }
 
@@ -821,7 +902,7 @@ static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
     TVP_LAUNCH_CHECK();
   }
   if (a.mode == TVP_EPI_ARGMAX) {
-    argmax_finalize_kernel<<<1, 256, 0, stream>>>(a.keys, a.m, a.argmax);
+    argmax_finalize_kernel<<<dim3((unsigned)a.m), 256, 0, stream>>>(a.keys, a.key_slots, a.m, a.argmax);
     TVP_LAUNCH_CHECK();
   }
   return TVP_OK;
@@ -834,16 +915,16 @@ int gemm_ksplits(int64_t m, const tvp_w12_packed* w, int ksplit) {
   return p.skinny ? p.splits : 1;
 }
 
-void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes) {
-  const GemmPlan p = make_plan(m, w);
+void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes, int ksplit) {
+  const GemmPlan p = make_plan(m, w, ksplit);
   *groups = p.groups;
   *scratch_bytes = p.scratch_bytes;
 }
 
 int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
-             const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, unsigned long long* keys, void* scratch,
-             size_t scratch_bytes, hipStream_t stream, int ksplit) {
-  if (!w || !epi || !w->blob || !cnt || !keys) return TVP_ERR_ARG;
+             const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, void* scratch, size_t scratch_bytes,
+             hipStream_t stream, int ksplit) {
+  if (!w || !epi || !w->blob || !cnt) return TVP_ERR_ARG;
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
   if (ksplit > 1 && epi->mode != kEpiPartial) return TVP_ERR_ARG;
   const GemmPlan p = make_plan(m, w, ksplit);
@@ -883,10 +964,14 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
   a.splits = p.splits;
   a.kbs = p.kbs;
   a.kps = p.kps;
+  a.kbs_split = p.kbs_split;
+  a.gfull = p.gfull;
+  a.parts = p.parts;
   a.ntasks = p.ntasks;
   a.cnt = cnt;
-  a.keys = keys;
-  a.part = (float*)scratch;
+  a.keys = (unsigned long long*)((uint8_t*)scratch + p.keys_off);
+  a.key_slots = p.key_slots;
+  a.part = (float*)scratch;  // wide: split-K partial sums
   a.mode = epi->mode;
   a.y = epi->y;
   a.ldy = epi->ldy;
@@ -940,14 +1025,12 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
 
 using namespace tvp;
 
-// Standalone GEMM workspace: a fixed zero region (completion counters, then
-// the argmax buckets) so that calls on tensors of different shapes sharing
-// one workspace never find another call's scratch where their counters live;
-// then the scratch for partial sums.
-static size_t gemm_ws_layout(int64_t m, const tvp_w12_packed* w, size_t* off_keys, size_t* off_scr,
-                             size_t* scr_bytes, int* groups) {
+// Standalone GEMM workspace: a fixed zero region (completion counters) so
+// that calls on tensors of different shapes sharing one workspace never find
+// another call's scratch where their counters live; then the scratch.
+static size_t gemm_ws_layout(int64_t m, const tvp_w12_packed* w, size_t* off_scr, size_t* scr_bytes,
+                             int* groups) {
   gemm_requirements(m, w, groups, scr_bytes);
-  *off_keys = kGemmMaxGroups * 4;
   *off_scr = kGemmZeroBytes;
   return *off_scr + *scr_bytes;
 }
@@ -956,25 +1039,25 @@ extern "C" {
 
 size_t w12_gemm_workspace(int64_t m, const tvp_w12_packed* w) {
   if (!w || m < 1 || m > 192) return 0;
-  size_t a, b, c;
+  size_t b, c;
   int g;
-  return gemm_ws_layout(m, w, &a, &b, &c, &g);
+  return gemm_ws_layout(m, w, &b, &c, &g);
 }
 
 int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
                 const tvp_gemm_epilogue* epi, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!w || !epi) return TVP_ERR_ARG;
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
-  size_t off_keys, off_scr, scr_bytes;
+  size_t off_scr, scr_bytes;
   int groups;
-  const size_t need = gemm_ws_layout(m, w, &off_keys, &off_scr, &scr_bytes, &groups);
+  const size_t need = gemm_ws_layout(m, w, &off_scr, &scr_bytes, &groups);
   if ((size_t)groups > kGemmMaxGroups) return TVP_ERR_SHAPE;
   if (!ws || ws_bytes < need) return TVP_ERR_WORKSPACE;
   if (epi->mode < TVP_EPI_F32 || epi->mode > TVP_EPI_ARGMAX) return TVP_ERR_ARG;
   uint8_t* b = (uint8_t*)ws;
   if (epi->x_packed && !x) return TVP_ERR_ARG;
   return gemm_run(epi->x_packed ? nullptr : x, epi->x_packed ? x : nullptr, m, ldx, w, epi, epi->y_packed,
-                  (uint32_t*)b, (unsigned long long*)(b + off_keys), b + off_scr, scr_bytes, stream);
+                  (uint32_t*)b, b + off_scr, scr_bytes, stream);
 }
 
 int64_t w12_packed_x_elems(int64_t k_in) { return k_in < 0 ? 0 : xpack_elems(k_in); }
