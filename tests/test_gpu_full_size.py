@@ -2,9 +2,10 @@
 bench.py times: hidden 5120, 40 query / 8 KV heads of 128, SwiGLU 17408, the
 full 151936-token LM head, a 4096-token context and a 32-node best-first
 tree -- one decoder layer (the oracle's fp64 cost of all 64 would not fit a
-test).  Logits are compared on every row within 2e-3 max-abs-rel, greedy
-tokens on decidable rows, acceptance where determined; the pass is bitwise
-reproducible."""
+test).  Logits are compared on every row within max(2e-3, 1.5 x the
+rounding-noise envelope of fp32 evaluations of the same definition, see
+tests/fp32_reference.py), greedy tokens on decidable rows, acceptance where
+determined; the pass is bitwise reproducible."""
 
 import dataclasses
 
@@ -19,6 +20,7 @@ from synth import best_first_topology
 from synth.configs import CONFIGS, gen_kv_context, gen_model
 from synth.trees import assign_tokens_by_depth
 from synth.weights import bf16_bits_numpy
+from tests.fp32_reference import logit_tolerance, noise_envelope
 from tests.gpu_util import to_i32
 from tests.helpers import oracle_topk_fn
 from tests.parity import acceptance_ok, check_logits
@@ -64,9 +66,13 @@ def test_verify_step_27b_shapes_one_layer(cuda):
     res2 = tvp.verify_step(dm.plan, L, to_i32(tokens), to_i32(parents), commit=False, want_logits=True)
     torch.cuda.synchronize()
     g = res.logits.cpu().numpy().astype(np.float64)
-    chk = check_logits(g, ref["logits"], tol=2e-3)
-    print(f"  logits max_abs_rel={chk['max_abs_rel']:.2e} undecidable={chk['undecidable_frac']:.3f} "
-          f"accepted={int(res.n_accepted.item())} (oracle {ref['n_accepted']})", flush=True)
+    print("  rounding-noise envelope", flush=True)
+    env = noise_envelope(orc, cache, L, tokens, parents, ref["logits"], runs=2)
+    tol = logit_tolerance(env)
+    chk = check_logits(g, ref["logits"], tol=tol)
+    print(f"  logits max_abs_rel={chk['max_abs_rel']:.2e} fp32-envelope={env:.2e} tol={tol:.2e} "
+          f"undecidable={chk['undecidable_frac']:.3f} accepted={int(res.n_accepted.item())} "
+          f"(oracle {ref['n_accepted']})", flush=True)
     assert chk["logits_ok"], chk["max_abs_rel"]
     assert chk["argmax_ok"], chk["bad_argmax_rows"]
     am = res.argmax.cpu().numpy()
