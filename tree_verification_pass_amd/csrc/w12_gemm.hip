@@ -507,193 +507,6 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
   epilogue<MODE>(a, t0 * 32, nc, M, threadIdx.x, KW * 64, blockIdx.x, sum_waves, slice, cmask);
 }
 
-// ----------------------------------------------------------------------------
-// Streaming kernel (m <= 32): a workgroup of 4 wavefronts owns 4 consecutive
-// tiles (wavefront w: tile 4g + w) over one K range, and all four walk the
-// same k-blocks.  Each k-block's records (3 KB per tile) and its packed
-// activations (4 KB, shared by the four) come by direct global->LDS loads
-// into a D-deep ring, D-1 blocks ahead of the block being decoded, so the
-// stream holds no registers and its depth does not cost occupancy.  One
-// workgroup barrier per k-block makes the shared activations visible and
-// frees the ring slot the next loads reuse.  The compiler cannot see which
-// LDS bytes the direct loads write, so the ring is read with inline
-// ds_read_b128 after an explicit wait on this wavefront's own loads.
-constexpr int kStreamWaves = 4;
-constexpr int kStreamMaxRange = 320;  // k-blocks per workgroup (escape offsets kept in LDS)
-
-__device__ inline void dma16(const void* gsrc, void* lds_row) {
-  // 64 lanes x 16 bytes to lds_row + 16 * lane
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_row, 16, 0, 0);
-}
-__device__ inline void dma4(const void* gsrc, void* lds_row) {
-  // 64 lanes x 4 bytes to lds_row + 4 * lane
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_row, 4, 0, 0);
-}
-
-template <int D>
-__device__ inline void wait_vm_blocks() {
-  // this wavefront's loads of all but the newest D-2 blocks (5 loads each) are done
-  if constexpr (D == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (D == 3) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-  else if constexpr (D == 4) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-  else if constexpr (D == 5) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
-  else if constexpr (D == 6) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(25)" ::: "memory");
-}
-
-template <int D, int MODE>
-__global__ __launch_bounds__(kStreamWaves * 64) void w12_stream_kernel(GemmArgs a) {
-  constexpr int NW = kStreamWaves;
-  static_assert(D >= 2 && D <= 7, "ring depth");
-  __shared__ uint4 rrec[D][NW][3][64];  // record ring: [slot][wave][segment][lane]
-  __shared__ uint4 rx[D][256];          // activation ring: [slot][k-group (8) x row (32)]
-  __shared__ uint4 scr[NW][256];        // decode scratch per wave, then the output tiles
-  __shared__ uint32_t eoff[NW][kStreamMaxRange + 1];
-  __shared__ uint32_t resc[D][NW][64];   // escape entries ring: [slot][wave][lane]
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int b = blockIdx.x;
-  const int grp = MODE == kEpiPartial ? b / a.splits : b;
-  const int slice = MODE == kEpiPartial ? b % a.splits : 0;
-  const int ks0 = MODE == kEpiPartial ? slice * a.kps : 0;
-  const int ks1 = MODE == kEpiPartial ? min(a.n_kb, ks0 + a.kps) : a.n_kb;
-  const int nblk = max(ks1 - ks0, 0);
-  const int t = grp * NW + wave;
-  const int tt = min(t, a.n_tiles - 1);  // past the last tile: computed, never stored
-
-  for (int i = lane; i <= nblk; i += 64) eoff[wave][i] = a.escoff[(int64_t)tt * a.n_kb + ks0 + i];
-  const uint32_t b2v = a.b2[tt * 32 + (lane & 31)];
-  asm volatile("" ::"v"(b2v));  // arrived before the stream starts (the loop's waits stay exact)
-  // escape offsets of block i: read behind the compiler's back, like the ring
-  // (a visible LDS read here would make it wait for every load in flight)
-  const uint32_t eoff_base = (uint32_t)(size_t)&eoff[wave][0];
-  auto esc_range = [&](int i, uint32_t& eo, uint32_t& ec) {
-    uint2 v;
-    asm volatile("ds_read2_b32 %0, %1 offset1:1\ns_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(eoff_base + 4u * i) : "memory");
-    eo = v.x;
-    ec = v.y - v.x;
-  };
-  f32x16_t acc;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  lds_order();
-
-  const uint16_t* xbase = a.xp;
-  auto issue = [&](int i, int slot) {
-    i = min(i, max(nblk - 1, 0));  // past the end: re-read the last block, never used
-    const int j = ks0 + i;
-    const uint4* blk = (const uint4*)(a.rec + rec_block(tt, j, a.n_tiles) * kBlockBytes);
-#pragma unroll
-    for (int q = 0; q < 3; ++q) dma16(blk + q * 64 + lane, &rrec[slot][wave][q][0]);
-    dma16((const uint4*)(xbase + (int64_t)j * 2048) + wave * 64 + lane, &rx[slot][wave * 64]);
-    uint32_t eo, ec;
-    esc_range(i, eo, ec);
-    // lanes past the count read a neighbour (the blob continues past the
-    // escape list) and are never used
-    dma4(a.esc + ((uint32_t)lane < ec ? eo + lane : eo), &resc[slot][wave][0]);
-  };
-
-  const bool ragged_tail = nblk > 0 && ks1 == a.n_kb && (a.k_in & 63) != 0;
-  auto process = [&](int i, int slot) {
-    const int j = ks0 + i;
-    uint4 r[3], A[4];
-    uint32_t Ent;
-    {
-      const uint32_t rb = (uint32_t)(size_t)&rrec[slot][wave][0][lane];
-      const uint32_t xb = (uint32_t)(size_t)&rx[slot][(lane >> 5) * 32 + (lane & 31)];
-      const uint32_t eb = (uint32_t)(size_t)&resc[slot][wave][lane];
-      asm volatile(
-          "ds_read_b128 %0, %8\n"
-          "ds_read_b128 %1, %8 offset:1024\n"
-          "ds_read_b128 %2, %8 offset:2048\n"
-          "ds_read_b128 %3, %9\n"
-          "ds_read_b128 %4, %9 offset:1024\n"
-          "ds_read_b128 %5, %9 offset:2048\n"
-          "ds_read_b128 %6, %9 offset:3072\n"
-          "ds_read_b32 %7, %10\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(A[0]), "=v"(A[1]), "=v"(A[2]), "=v"(A[3]), "=v"(Ent)
-          : "v"(rb), "v"(xb), "v"(eb)
-          : "memory");
-    }
-    if (ragged_tail && i == nblk - 1) {  // columns past k_in contribute nothing
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int k = 64 * j + 16 * ks + 8 * (lane >> 5);
-        uint32_t w4[4] = {A[ks].x, A[ks].y, A[ks].z, A[ks].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (k + 2 * e >= a.k_in) w4[e] &= 0xFFFF0000u;
-          if (k + 2 * e + 1 >= a.k_in) w4[e] &= 0x0000FFFFu;
-        }
-        A[ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-      }
-    }
-    uint32_t o[16];
-    decode_block(r, b2v, o);
-#pragma unroll
-    for (int sg = 0; sg < 4; ++sg) scr[wave][64 * sg + lane] = make_uint4(o[4 * sg], o[4 * sg + 1], o[4 * sg + 2], o[4 * sg + 3]);
-    lds_order();
-    uint32_t eo, ec;
-    esc_range(i, eo, ec);
-    uint16_t* sh = (uint16_t*)&scr[wave][0];
-    if ((uint32_t)lane < ec) sh[Ent & 0x7FFu] = (uint16_t)(Ent >> 16);
-    if (ec > 64u) {  // more escapes than lanes in this tile block (rare)
-      for (uint32_t e = 64 + lane; e < ec; e += 64) {
-        const uint32_t ent = a.esc[eo + e];
-        sh[ent & 0x7FFu] = (uint16_t)(ent >> 16);
-      }
-    }
-    lds_order();
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t B = as_bf16x8(scr[wave][64 * ks + lane]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[ks]), B, acc, 0, 0, 0);
-    }
-    lds_order();
-  };
-
-  if (nblk > 0) {
-#pragma unroll
-    for (int p = 0; p < D - 1; ++p) issue(p, p);
-    for (int i0 = 0; i0 < nblk; i0 += D) {
-#pragma unroll
-      for (int r = 0; r < D; ++r) {
-        const int i = i0 + r;
-        if (i < nblk) {  // uniform across the workgroup
-          wait_vm_blocks<D>();
-          // block i is in LDS for every wave; block i-1's slot is free.  A bare
-          // barrier: the fences of __syncthreads would wait for every load in flight.
-          asm volatile("s_barrier" ::: "memory");
-          issue(i + D - 1, (r + D - 1) % D);
-          process(i, r);
-        }
-      }
-    }
-  }
-
-  // ------------------------------------------------------------- results
-  // the ring's last (unused) loads land before the LDS is reused or released
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  const int M = a.m;
-  const int NC = NW * 32;
-  __syncthreads();
-  float* P = (float*)&scr[0][0];  // [NW tiles][M][32]
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int row = (v >> 2) * 8 + 4 * (lane >> 5) + (v & 3);
-    if (row < M) P[(wave * M + row) * 32 + (lane & 31)] = acc[v];
-  }
-  __syncthreads();
-  const int c0 = grp * NC;
-  epilogue<MODE>(a, c0, min(NC, a.n_pad - c0), M, threadIdx.x, NW * 64, b,
-                 [&](int row, int col) {
-                   const int c = col - c0;
-                   return P[((c >> 5) * M + row) * 32 + (c & 31)];
-                 },
-                 slice);
-}
-
 template <int ROWS>
 struct XChunk {
   static constexpr int CB = ROWS <= 16 ? 8 : (ROWS <= 32 ? 4 : 2);  // blocks per X chunk
@@ -933,15 +746,8 @@ __global__ __launch_bounds__(256) void w12_wide_kernel(GemmArgs a) {
   }
 }
 
-#ifndef TVP_STREAM
-#define TVP_STREAM 0  // streaming kernel for m <= 32 (0: the register-ring kernel only)
-#endif
-#ifndef TVP_STREAM_D
-#define TVP_STREAM_D 3  // streaming kernel ring depth
-#endif
-
 struct GemmPlan {
-  bool skinny, stream;
+  bool skinny;
   int MT, RB, TPW, RD, KW, TG, groups, splits, kbs, kps, ntasks, grid;
   int gfull, parts, kbs_split, key_slots;
   size_t keys_off, scratch_bytes;
@@ -1018,43 +824,15 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1) {
       const int rest = p.groups - p.gfull;
       while (rest > 0 && p.parts < 8 && rest * p.parts < kNumCUs) p.parts *= 2;
     }
-    // the streaming kernel: groups of 4 tiles, whole K (or the K slices)
-    if (TVP_STREAM && nkb > 0) {
-      const int sg = (int)ceil_div(w->n_tiles, kStreamWaves);
-      int s_best = 1, kps_best = nkb;
-      if (partial) {
-        double best = 1e30;
-        for (int sl = 1; sl <= std::min(ksplit, 16); ++sl) {
-          const int kps = (int)ceil_div(nkb, sl);
-          if ((int)ceil_div(nkb, kps) != sl || (sl > 1 && kps < 2)) continue;
-          const double c = slice_cost(sg, sl, kps);
-          if (c < best - 1e-9) best = c, s_best = sl, kps_best = kps;
-        }
-      }
-      if (kps_best <= kStreamMaxRange) {
-        p.stream = true;
-        p.TPW = kStreamWaves;
-        p.groups = sg;
-        p.gfull = sg;
-        p.parts = 1;
-        p.splits = s_best;
-        p.kps = kps_best;
-        p.KW = kStreamWaves;
-        p.kbs = p.kbs_split = 0;
-        p.ntasks = p.grid = partial ? sg * s_best : sg;
-      }
-    }
     const int nwg = partial ? p.groups * p.splits : p.gfull + (p.groups - p.gfull) * p.parts;
     const int krange = partial ? p.kps : nkb;
-    if (!p.stream) {
-      p.KW = nwg >= TVP_KW_SWITCH ? TVP_KW_MANY : TVP_KW_FEW;
-      if (krange > 4 * 63) p.KW = 8;
-      p.KW = std::max(1, std::min(p.KW, std::max(krange, 1)));
-      p.kbs = nkb > 0 ? (int)ceil_div(nkb, p.KW) : 0;
-      p.kbs_split = p.kps > 0 ? (int)ceil_div(p.kps, p.KW) : 0;
-      p.ntasks = nwg;
-      p.grid = nwg;
-    }
+    p.KW = nwg >= TVP_KW_SWITCH ? TVP_KW_MANY : TVP_KW_FEW;
+    if (krange > 4 * 63) p.KW = 8;
+    p.KW = std::max(1, std::min(p.KW, std::max(krange, 1)));
+    p.kbs = nkb > 0 ? (int)ceil_div(nkb, p.KW) : 0;
+    p.kbs_split = p.kps > 0 ? (int)ceil_div(p.kps, p.KW) : 0;
+    p.ntasks = nwg;
+    p.grid = nwg;
   } else {
     p.TPW = 1;
     p.RD = 0;
@@ -1081,20 +859,6 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1) {
   return p;
 }
 
-template <int D>
-static void launch_stream(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.grid), block((unsigned)(kStreamWaves * 64));
-  switch (a.mode) {
-    case TVP_EPI_F32: w12_stream_kernel<D, TVP_EPI_F32><<<grid, block, 0, stream>>>(a); break;
-    case TVP_EPI_BF16: w12_stream_kernel<D, TVP_EPI_BF16><<<grid, block, 0, stream>>>(a); break;
-    case TVP_EPI_RESID: w12_stream_kernel<D, TVP_EPI_RESID><<<grid, block, 0, stream>>>(a); break;
-    case TVP_EPI_SWIGLU: w12_stream_kernel<D, TVP_EPI_SWIGLU><<<grid, block, 0, stream>>>(a); break;
-    case TVP_EPI_QKV: w12_stream_kernel<D, TVP_EPI_QKV><<<grid, block, 0, stream>>>(a); break;
-    case kEpiPartial: w12_stream_kernel<D, kEpiPartial><<<grid, block, 0, stream>>>(a); break;
-    default: w12_stream_kernel<D, TVP_EPI_ARGMAX><<<grid, block, 0, stream>>>(a); break;
-  }
-}
-
 template <int MT, int TPW, int RD>
 static void launch_skinny(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.grid), block((unsigned)(p.KW * 64));
@@ -1117,9 +881,7 @@ static void launch_wide(const GemmArgs& a, int grid, hipStream_t stream) {
 
 static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   if (p.grid > 0) {
-    if (p.stream) {
-      launch_stream<TVP_STREAM_D>(a, p, stream);
-    } else if (p.skinny) {
+    if (p.skinny) {
       if (p.MT == 16) {
         if (p.TPW == 2) launch_skinny<16, 2, TVP_RD2>(a, p, stream);
         else launch_skinny<16, 1, TVP_RD1>(a, p, stream);
