@@ -157,14 +157,16 @@ def time_gateup(dm, cfg, iters: int):
     for i in range(len(layers)):
         tvp.w12_gemm_px(xp, n, layers[i].wgu, epi)
     torch.cuda.synchronize()
-    # the library launches on torch's current stream, where these events are recorded
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
+    # the library launches on torch's current stream, where these events are
+    # recorded: one pair around each launch, so the figure is the kernel's own
+    # duration (the launch gaps between back-to-back calls are not counted)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for i in range(iters):
+        ev[i][0].record()
         tvp.w12_gemm_px(xp, n, layers[i % len(layers)].wgu, epi)
-    e.record()
+        ev[i][1].record()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / iters
+    ms = sum(s.elapsed_time(e) for s, e in ev) / iters
     p = layers[0].wgu
     nbytes = (sum(w12_algorithmic_bytes(L.wgu.n_out, L.wgu.k_in, int(L.wgu.desc.n_esc)) for L in layers)
               / len(layers) + n * H * 2 + n * F * 2)

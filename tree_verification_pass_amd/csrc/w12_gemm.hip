@@ -42,9 +42,6 @@ struct GemmArgs {
   int groups, splits, kbs, ntasks;
   int kps;    // skinny: K blocks per slice of a split group
   int kbs_split;  // skinny, partial-sum epilogue: K blocks per wavefront of a slice
-  int gfull;      // skinny: groups [0, gfull) have one workgroup each; each later
-                  // group is shared by `parts` workgroups, one per channel part
-  int parts;
   float* part;
   uint32_t* cnt;
   unsigned long long* keys;  // ARGMAX: [slot][m] packed (value, -id) maxima, one slot per workgroup that
@@ -126,9 +123,7 @@ __device__ inline unsigned long long argmax_key(float v, int32_t id) {
 // (thread index `tid`), reading fp32 results through V(row, col).
 template <int MODE, typename Get>
 __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int tid, int nthr, int key_slot,
-                                Get V, int slice = 0, uint32_t cmask = 0xFFFFFFFFu) {
-  // cmask: the channels (bit c of each 32-channel tile) this workgroup owns
-  auto owned = [&](int col) { return (cmask >> (col & 31)) & 1u; };
+                                Get V, int slice = 0) {
   if constexpr (MODE == kEpiPartial) {
     float* P = (float*)a.y + (int64_t)slice * M * a.ldy;
     for (int idx = tid; idx < M * nc; idx += nthr) {
@@ -140,7 +135,7 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
     for (int idx = tid; idx < M * nc; idx += nthr) {
       const int row = idx / nc, col = c0 + idx % nc;
       const int32_t r = a.rowmap[col];
-      if (r < 0 || !owned(col)) continue;
+      if (r < 0) continue;
       const float v = V(row, col);
       if constexpr (MODE == TVP_EPI_F32) {
         ((float*)a.y)[row * a.ldy + r] = v;
@@ -157,7 +152,7 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
       const int row = idx / half, p = idx % half;
       const int col = c0 + (p / 16) * 32 + (p % 16);
       const int32_t r = a.rowmap[col];
-      if (r < 0 || !owned(col)) continue;
+      if (r < 0) continue;
       const float gv = V(row, col), uv = V(row, col + 16);
       const uint16_t o = (uint16_t)f32_to_bf16(silu_f32(gv) * uv);
       if (a.y_packed) ((uint16_t*)a.y)[xpack_index(row, r)] = o;
@@ -169,7 +164,7 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
     for (int idx = tid; idx < M * nc; idx += nthr) {
       const int row = idx / nc, col = c0 + idx % nc;
       const int t = col / 32, c = col % 32;
-      if (t >= a.n_tiles || !owned(col)) continue;
+      if (t >= a.n_tiles) continue;
       if (t < rot_tiles) {
         if (c >= 16) continue;
         const int head = t / tph, u = t % tph;
@@ -201,7 +196,7 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
       for (int cc = tid; cc < nc; cc += nthr) {
         const int col = c0 + cc;
         const int32_t r = a.rowmap[col];
-        if (r < 0 || !owned(col)) continue;
+        if (r < 0) continue;
         const float v = V(row, col);
         if (a.logits) a.logits[row * a.ldl + r] = v;
         const unsigned long long k = argmax_key(v, r);
@@ -269,25 +264,11 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KW = blockDim.x >> 6;
-  // Workgroup -> work: with the partial-sum epilogue every group is cut into
-  // `splits` K slices; otherwise groups [0, gfull) have a workgroup each and
-  // every later group is shared by `parts` workgroups, each owning a part of
-  // the tile channels over the whole K range (no partial sums to combine).
+  // Workgroup -> work: one workgroup per group of TPW tiles over the whole K
+  // range, or, with the partial-sum epilogue, one per (group, K slice).
   const int b = blockIdx.x;
-  int grp = b, slice = 0, part = 0, w16 = 16;  // w16: channels per half-tile owned
-  if (MODE == kEpiPartial) {
-    grp = b / a.splits;
-    slice = b % a.splits;
-  } else if (b >= a.gfull) {
-    grp = a.gfull + (b - a.gfull) / a.parts;
-    part = (b - a.gfull) % a.parts;
-    w16 = 16 / a.parts;
-  }
-  const uint32_t half_mask = (w16 == 16 ? 0xFFFFu : ((1u << w16) - 1u)) << (part * w16);
-  const uint32_t cmask = half_mask | (half_mask << 16);
-  // lanes of channels this workgroup does not own read a lane it owns (same
-  // addresses, so no extra memory traffic); their results are never stored
-  const int rlane = (lane & ~15) | (part * w16 + (lane & (w16 - 1)));
+  const int grp = MODE == kEpiPartial ? b / a.splits : b;
+  const int slice = MODE == kEpiPartial ? b % a.splits : 0;
   const int t0 = grp * TPW;
   const int ks0 = MODE == kEpiPartial ? slice * a.kps : 0;
   const int ks1 = MODE == kEpiPartial ? min(a.n_kb, ks0 + a.kps) : a.n_kb;  // this workgroup's K range
@@ -334,7 +315,7 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
     for (int t = 0; t < TPW; ++t) {
       const uint4* blk = (const uint4*)(a.rec + rec_block(tt[t], j, a.n_tiles) * kBlockBytes);
 #pragma unroll
-      for (int q = 0; q < 3; ++q) R[slot][t][q] = load_nt(blk + q * 64 + rlane);
+      for (int q = 0; q < 3; ++q) R[slot][t][q] = load_nt(blk + q * 64 + lane);
     }
   };
   auto issue_esc = [&](int i, int slot) {
@@ -504,7 +485,7 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
     return v;
   };
   const int nc = min(NC, a.n_pad - t0 * 32);
-  epilogue<MODE>(a, t0 * 32, nc, M, threadIdx.x, KW * 64, blockIdx.x, sum_waves, slice, cmask);
+  epilogue<MODE>(a, t0 * 32, nc, M, threadIdx.x, KW * 64, blockIdx.x, sum_waves, slice);
 }
 
 template <int ROWS>
@@ -749,7 +730,7 @@ __global__ __launch_bounds__(256) void w12_wide_kernel(GemmArgs a) {
 struct GemmPlan {
   bool skinny;
   int MT, RB, TPW, RD, KW, TG, groups, splits, kbs, kps, ntasks, grid;
-  int gfull, parts, kbs_split, key_slots;
+  int kbs_split, key_slots;
   size_t keys_off, scratch_bytes;
 };
 
@@ -803,7 +784,6 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1) {
     p.TG = p.TPW;
     p.groups = (int)ceil_div(w->n_tiles, p.TPW);
     p.splits = 1;
-    p.parts = 1;
     p.kps = nkb;
     if (partial) {
       // K slices, summed in slice order by the consumer
@@ -815,16 +795,10 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1) {
         const double c = slice_cost(p.groups, sl, kps);
         if (c < best - 1e-9) best = c, best_s = sl, best_kps = kps;
       }
-      p.gfull = 0;
       p.splits = best_s;
       p.kps = nkb > 0 ? best_kps : 0;
-    } else {
-      // whole groups in multiples of the CU count; the rest shared by channel parts
-      p.gfull = p.groups >= kNumCUs ? (p.groups / kNumCUs) * kNumCUs : p.groups;
-      const int rest = p.groups - p.gfull;
-      while (rest > 0 && p.parts < 8 && rest * p.parts < kNumCUs) p.parts *= 2;
     }
-    const int nwg = partial ? p.groups * p.splits : p.gfull + (p.groups - p.gfull) * p.parts;
+    const int nwg = partial ? p.groups * p.splits : p.groups;
     const int krange = partial ? p.kps : nkb;
     p.KW = nwg >= TVP_KW_SWITCH ? TVP_KW_MANY : TVP_KW_FEW;
     if (krange > 4 * 63) p.KW = 8;
@@ -965,8 +939,6 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
   a.kbs = p.kbs;
   a.kps = p.kps;
   a.kbs_split = p.kbs_split;
-  a.gfull = p.gfull;
-  a.parts = p.parts;
   a.ntasks = p.ntasks;
   a.cnt = cnt;
   a.keys = (unsigned long long*)((uint8_t*)scratch + p.keys_off);
