@@ -43,46 +43,55 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 //        preceding projection, added in slice order; nothing when S == 0)
 //   y <- bf16(h * (mean(h^2) + eps)^-1/2 * g)       (fp32, fixed reduction order)
 // y is the next GEMM's input, row-major or (packed != 0, at most 32 rows) in
-// the packed activation layout.  Rows of 8-element chunks (16-byte accesses)
-// when the row length and pitches allow it, element by element otherwise;
-// up to CPT chunks per thread stay in registers between the two passes.
-template <int CPT>
-__global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict__ P, int S, int64_t pstride,
-                                                         int ldp, uint16_t* __restrict__ h, int ldh,
-                                                         const uint16_t* __restrict__ g, int hidden, float eps,
-                                                         uint16_t* __restrict__ y, int ldy, int packed) {
-  __shared__ float ws[4];
+// the packed activation layout.  1024 threads: a row of up to 8192 values is
+// one 8-element chunk per thread, so every load of the row (h, the slices,
+// the gains) is issued before the first is used and the kernel costs about
+// one memory round trip.  Longer rows loop; rows whose length or pitches are
+// not multiples of 8 go element by element.
+constexpr int kNormThreads = 1024;
+
+__global__ __launch_bounds__(kNormThreads) void resid_norm_kernel(const float* __restrict__ P, int S,
+                                                                  int64_t pstride, int ldp,
+                                                                  uint16_t* __restrict__ h, int ldh,
+                                                                  const uint16_t* __restrict__ g, int hidden,
+                                                                  float eps, uint16_t* __restrict__ y, int ldy,
+                                                                  int packed) {
+  constexpr int NT = kNormThreads;
+  __shared__ float ws[NT / 64];
   const int i = blockIdx.x, tid = threadIdx.x;
   uint16_t* hr = h + (int64_t)i * ldh;
   const float* pr = P + (int64_t)i * ldp;
   uint16_t* yr = y + (int64_t)i * ldy;
   const bool vec = (hidden % 8) == 0 && (ldh % 8) == 0 && (S == 0 || (ldp % 4) == 0) && (packed || (ldy % 8) == 0);
   float ss = 0.0f;
-  uint32_t keep[CPT][4];  // the first CPT chunks of this thread (fully unrolled, so registers)
   // pass 1 on chunk c: residual update (written back) and sum of squares
   auto pass1 = [&](int c, uint32_t (&w)[4]) {
     const uint4 v = *(const uint4*)(hr + 8 * c);
     w[0] = v.x, w[1] = v.y, w[2] = v.z, w[3] = v.w;
     if (S > 0) {
       float acc[8];
-      auto add_slice = [&](int sl, const float4& p0, const float4& p1) {
-        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = sl == 0 ? pv[e] : acc[e] + pv[e];
-      };
       int sl = 0;
-      for (; sl + 4 <= S; sl += 4) {  // 8 independent loads in flight, added in slice order
-        float4 q0[4], q1[4];
+      for (; sl + 8 <= S; sl += 8) {  // 16 independent loads in flight, added in slice order
+        float4 q0[8], q1[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 8; ++j) {
           q0[j] = *(const float4*)(pr + (sl + j) * pstride + 8 * c);
           q1[j] = *(const float4*)(pr + (sl + j) * pstride + 8 * c + 4);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) add_slice(sl + j, q0[j], q1[j]);
+        for (int j = 0; j < 8; ++j) {
+          const float pv[8] = {q0[j].x, q0[j].y, q0[j].z, q0[j].w, q1[j].x, q1[j].y, q1[j].z, q1[j].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = (sl + j) == 0 ? pv[e] : acc[e] + pv[e];
+        }
       }
-      for (; sl < S; ++sl)
-        add_slice(sl, *(const float4*)(pr + sl * pstride + 8 * c), *(const float4*)(pr + sl * pstride + 8 * c + 4));
+      for (; sl < S; ++sl) {
+        const float4 q0 = *(const float4*)(pr + sl * pstride + 8 * c);
+        const float4 q1 = *(const float4*)(pr + sl * pstride + 8 * c + 4);
+        const float pv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = sl == 0 ? pv[e] : acc[e] + pv[e];
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t lo = f32_to_bf16(bf16_to_f32(w[e] & 0xFFFFu) + acc[2 * e]);
@@ -98,16 +107,19 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict
     }
   };
   const int nc = vec ? hidden / 8 : 0;
+  uint32_t keep[4] = {0, 0, 0, 0};
+  uint4 gkeep = make_uint4(0, 0, 0, 0);
   if (vec) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j)
-      if (tid + 256 * j < nc) pass1(tid + 256 * j, keep[j]);
-    for (int c = tid + 256 * CPT; c < nc; c += 256) {
+    if (tid < nc) {
+      gkeep = *(const uint4*)(g + 8 * tid);  // the gains of pass 2, fetched with everything else
+      pass1(tid, keep);
+    }
+    for (int c = tid + NT; c < nc; c += NT) {
       uint32_t w[4];
       pass1(c, w);
     }
   } else {
-    for (int k = tid; k < hidden; k += 256) {
+    for (int k = tid; k < hidden; k += NT) {
       float v = bf16_to_f32(hr[k]);
       if (S > 0) {
         float acc = 0.0f;
@@ -122,11 +134,12 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   if ((tid & 63) == 0) ws[tid >> 6] = ss;
   __syncthreads();
-  const float tot = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; w += 2) tot += ws[w] + ws[w + 1];
   const float r = 1.0f / sqrtf(tot / (float)hidden + eps);
-  // pass 2 on chunk c (w: its updated values)
-  auto pass2 = [&](int c, const uint32_t (&w)[4]) {
-    const uint4 gv = *(const uint4*)(g + 8 * c);
+  // pass 2 on chunk c (w: its updated values, gv: its gains)
+  auto pass2 = [&](int c, const uint32_t (&w)[4], const uint4& gv) {
     const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
     uint32_t o[4];
 #pragma unroll
@@ -138,16 +151,14 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict
     *(uint4*)(packed ? y + xpack_index(i, 8 * c) : yr + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
   };
   if (vec) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j)
-      if (tid + 256 * j < nc) pass2(tid + 256 * j, keep[j]);
-    for (int c = tid + 256 * CPT; c < nc; c += 256) {  // re-read this thread's own pass-1 result
+    if (tid < nc) pass2(tid, keep, gkeep);
+    for (int c = tid + NT; c < nc; c += NT) {  // re-read this thread's own pass-1 result
       const uint4 v = *(const uint4*)(hr + 8 * c);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      pass2(c, w);
+      pass2(c, w, *(const uint4*)(g + 8 * c));
     }
   } else {
-    for (int k = tid; k < hidden; k += 256)
+    for (int k = tid; k < hidden; k += NT)
       (packed ? y[xpack_index(i, k)] : yr[k]) = (uint16_t)f32_to_bf16(bf16_to_f32(hr[k]) * r * bf16_to_f32(g[k]));
   }
 }
@@ -155,8 +166,8 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* __restrict
 // RMSNorm alone (no residual update): S = 0 of the fused kernel.
 static void launch_norm(const float* P, int S, int64_t pstride, int ldp, uint16_t* h, int ldh, const uint16_t* g,
                         int hidden, float eps, uint16_t* y, int ldy, int packed, int rows, hipStream_t stream) {
-  resid_norm_kernel<4><<<dim3(rows), dim3(256), 0, stream>>>(P, S, pstride, ldp, h, ldh, g, hidden, eps, y, ldy,
-                                                             packed);
+  resid_norm_kernel<<<dim3(rows), dim3(kNormThreads), 0, stream>>>(P, S, pstride, ldp, h, ldh, g, hidden, eps, y,
+                                                                   ldy, packed);
 }
 
 // One workgroup per request; the walk is sequential over nodes (parents[i] < i).
