@@ -6,22 +6,25 @@
 // exactly its own root path; section 전제와 한계 names tree attention as one
 // of the places where reduction order may flip near-ties.
 //
-// Design: per (request, kv head, key split) one workgroup of up to 8
-// wavefronts; wavefront w owns 32 query rows (row = gq * n + i for query head
-// kv_head*G + gq and node i).  Keys are staged 64 at a time through LDS with
-// fully coalesced 16-byte loads (K and V both row-major there, XOR-swizzled
-// per row).  Scores are computed as S^T = K Q^T with
+// Design: per (request, kv head, 32-row block, key split) one workgroup of
+// four wavefronts.  A row is (query head kv_head*G + gq, node i) at row
+// gq * n + i.  Each wavefront streams its own 32-key blocks of the split
+// through its own LDS tiles (fully coalesced 16-byte loads, K and V
+// row-major, XOR-swizzled per row), with the next blocks in flight in
+// registers.  Scores are computed as S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 so each lane owns one query row, masked with the
 // node's 64-bit ancestor mask and folded into an online softmax; P V is
 // accumulated with the same MFMA, its V^T operand read straight from the
 // row-major V tile with the LDS transpose read (ds_read_b64_tr_b16), and P
-// applied as a sum of two bf16 pieces.  Splits write (max, sum, O) partials
-// in the accumulator's own register layout (one coalesced 256-byte store per
-// accumulator register); a separate merge launch sums them in split order,
-// so the result is deterministic.
+// applied as a sum of two bf16 pieces.  The four wavefronts' (max, sum, O)
+// are combined in LDS in a fixed order; with several splits, each split's
+// (max, sum, O) goes out in the accumulator's register layout (coalesced
+// 256-byte stores) and a separate merge launch sums them in split order, so
+// the result is deterministic.
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -77,6 +80,7 @@ struct AttnArgs {
   int32_t s_req;
   const uint64_t* anc;
   int n_req, hq, hkv, G, max_splits, rows_total, kr;
+  int units, units8;  // (request, kv head, split) units; rounded up to a multiple of 8
   float scale_log2;
   float* po;
   float* pm;
@@ -103,37 +107,68 @@ __device__ inline int v_swz(int key) {
   return D == 128 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2);
 }
 
-template <int D, int NT>
-__global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
-  constexpr int KC = 64;        // keys per LDS stage
-  constexpr int CH = D / 8;     // 16-byte chunks per row
-  constexpr int NDB = D / 32;   // d blocks of the P V product
-  __shared__ uint4 ks[KC * CH];  // K [key][chunk ^ (key % CH)]
-  __shared__ uint4 vs[KC * CH];  // V [key][chunk ^ v_swz(key)]
+// Compiler fence for one wavefront's LDS accesses (they complete in order).
+__device__ inline void lds_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
 
-  const int split = blockIdx.x % a.max_splits;
-  const int kh = (blockIdx.x / a.max_splits) % a.hkv;
-  const int r = blockIdx.x / (a.max_splits * a.hkv);
+// Wavefronts per attention workgroup (two per SIMD).
+constexpr int kAttnWaves = 8;
+
+// One workgroup per (request, kv head, 32-row block, key split); its NW
+// wavefronts stream disjoint 32-key blocks of the split (wavefront w takes
+// blocks w, w + NW, ...) with no workgroup barrier until the end.  Each
+// wavefront stages its blocks through its own LDS tiles, keeps the next
+// NPF - 1 blocks in flight in registers and runs its own online softmax; the
+// NW (max, sum, O) states are combined in LDS in wavefront order at the end.
+// Two wavefronts per SIMD hide each other's MFMA, LDS and exp latencies.
+template <int D, int NPF>
+__global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) {
+  constexpr int NW = kAttnWaves;
+  constexpr int KB = 32;        // keys per block
+  constexpr int CH = D / 8;     // 16-byte chunks per key row
+  constexpr int NDB = D / 32;   // d blocks of the P V product
+  constexpr int PER = KB * CH / 64;  // 16-byte pieces per lane per block (K or V)
+  constexpr int NACC = NDB * 16;     // accumulator registers per lane
+  // per wavefront: V [key][chunk ^ v_swz(key)]; at the end the same memory
+  // holds the wavefronts' O
+  __shared__ uint4 tiles[NW][2][KB * CH];
+  __shared__ uint4 qs[32 * CH];    // Q of the row block [row][chunk ^ (row % CH)]
+  __shared__ float ml[NW][2][32];  // per wavefront and row: running max (raw score), sum
+  static_assert(sizeof(tiles) >= NW * NACC * 64 * sizeof(float), "O of all wavefronts fits the tiles");
+
+  // block -> (row block, unit): the row blocks of one (request, kv head,
+  // split) are a multiple of 8 apart, so they run on one XCD and share its L2
+  const int u = blockIdx.x % a.units8, rb = blockIdx.x / a.units8;
+  if (u >= a.units) return;
+  const int split = u % a.max_splits;
+  const int kh = (u / a.max_splits) % a.hkv;
+  const int r = u / (a.max_splits * a.hkv);
   const int L = a.ri.ctx_len[r], nb = a.ri.node_ptr[r], n = a.ri.node_ptr[r + 1] - nb;
   const int T = L + n, R = a.G * n;
   const int nsplit = (T + a.kr - 1) / a.kr;
-  if (split >= nsplit) return;
+  if (split >= nsplit || rb * 32 >= R) return;
   const int k0 = split * a.kr, k1 = min(T, k0 + a.kr);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
-  const int row = wave * 32 + (lane & 31);
+  const int row = rb * 32 + (lane & 31);
   const bool row_ok = row < R;
   const int gq = row_ok ? row / n : 0, node = row_ok ? row % n : 0;
   const int64_t cbase = (int64_t)kh * a.s_stride + (int64_t)r * a.s_req;  // slot 0 of this request/head
   const uint16_t* kbase = a.kc + cbase * D;
   const uint16_t* vbase = a.vc + cbase * D;
+  uint4* vs = tiles[wave][0];
 
-  // Q fragments (B operand): lane holds q[row][16 ds + 8 h .. +7]
-  uint4 qf[D / 16];
-  {
-    const uint16_t* qp = a.q + ((int64_t)(nb + node) * a.hq + kh * a.G + gq) * D;
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds)
-      qf[ds] = row_ok ? *(const uint4*)(qp + 16 * ds + 8 * h) : make_uint4(0, 0, 0, 0);
+  // Q of the row block (zero rows past R), one 16-byte piece per thread,
+  // loaded first and stored to LDS once the first K/V loads are in flight;
+  // the B operand of the score product is read from there: lane holds
+  // q[row][16 ds + 8 h .. +7]
+  static_assert(32 * CH <= NW * 64, "one Q piece per thread");
+  uint4 qv = make_uint4(0, 0, 0, 0);
+  const int qr = tid / CH, qc = tid % CH;
+  if (tid < 32 * CH && rb * 32 + qr < R) {
+    const int rr = rb * 32 + qr;
+    qv = *(const uint4*)(a.q + ((int64_t)(nb + rr % n) * a.hq + kh * a.G + rr / n) * D + 8 * qc);
   }
   const uint64_t anc = row_ok ? a.anc[nb + node] : 0ull;
 
@@ -144,30 +179,39 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[db][v] = 0.0f;
 
-  // K/V of the next 64 keys are fetched into registers while the current ones
-  // are used; CH consecutive lanes read one 2*D-byte row.
-  constexpr int PER = KC * CH / NT;
-  uint4 kpre[PER], vpre[PER];
-  auto fetch = [&](int sub) {
+  const int nblk = (k1 - k0 + KB - 1) / KB;                   // blocks of the split
+  const int nbw = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;  // blocks of this wavefront
+  auto key0_of = [&](int i) { return k0 + (wave + NW * i) * KB; };
+
+  // Block i of this wavefront into register stage st.  K arrives directly in
+  // the MFMA A-operand layout (lane: key lane % 32, 16-byte piece 2 ds + h of
+  // its row); V with CH consecutive lanes reading one 2*D-byte row, for the
+  // LDS tile.  Keys past the split are clamped to its last key (their scores
+  // are masked); a block past the wavefront's last is a placeholder in which
+  // every lane reads the same 16 bytes, so the number of loads in flight is
+  // the same on every path.
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t kpre[NPF][PER], vpre[NPF][PER];
+  auto fetch = [&](int i, int st) __attribute__((always_inline)) {
+    const bool real = i < nbw;
+    const int kb0 = key0_of(i);
+    const int kk = real ? min(kb0 + (lane & 31), k1 - 1) : k1 - 1;
+#pragma unroll
+    for (int ds = 0; ds < PER; ++ds)
+      kpre[st][ds] = *(const u32x4_t*)(kbase + (int64_t)kk * D + (real ? 16 * ds + 8 * h : 0));
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-      const int idx = tid + it * NT;
-      const int kk = sub + idx / CH, c = idx % CH;
-      kpre[it] = make_uint4(0, 0, 0, 0);
-      vpre[it] = make_uint4(0, 0, 0, 0);
-      if (kk < k1) {
-        kpre[it] = *(const uint4*)(kbase + (int64_t)kk * D + 8 * c);
-        vpre[it] = *(const uint4*)(vbase + (int64_t)kk * D + 8 * c);
-      }
+      const int pc = lane + 64 * it;
+      const int kv = real ? min(kb0 + pc / CH, k1 - 1) : k1 - 1, c = real ? pc % CH : 0;
+      vpre[st][it] = *(const u32x4_t*)(vbase + (int64_t)kv * D + 8 * c);
     }
   };
-  auto stash = [&]() {
+  auto stash = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-      const int idx = tid + it * NT;
-      const int key = idx / CH, c = idx % CH;
-      ks[key * CH + (c ^ (key % CH))] = kpre[it];
-      vs[key * CH + (c ^ v_swz<D>(key))] = vpre[it];
+      const int pc = lane + 64 * it;
+      const int key = pc / CH, c = pc % CH;
+      *(u32x4_t*)&vs[key * CH + (c ^ v_swz<D>(key))] = vpre[st][it];
     }
   };
   // transpose-read geometry: in each 16-lane group, source lane s points at
@@ -178,125 +222,169 @@ __global__ __launch_bounds__(NT) void tree_attn_kernel(AttnArgs a) {
   const int tr_d = 16 * (g16 & 1) + 4 * (s16 & 3);
   const char* vs_bytes = (const char*)vs;
 
-  fetch(k0);
-  for (int sub = k0; sub < k1; sub += KC) {
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (sub + KC < k1) fetch(sub + KC);
-    if (wave * 32 >= R) continue;
-
-    // one 32-key block at a time: scores S^T[key][row], online softmax, P V
+  // scores S^T[key][row] of one block, online softmax, P V
+  auto compute = [&](int i, int st) __attribute__((always_inline)) {
+    f32x16_t sc;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16_t sc;
+    for (int v = 0; v < 16; ++v) sc[v] = 0.0f;
+    {
+      const int qrow = lane & 31;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sc[v] = 0.0f;
-      {
-        const int key = kb * 32 + (lane & 31);
-#pragma unroll
-        for (int ds = 0; ds < D / 16; ++ds) {
-          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ks[key * CH + ((2 * ds + h) ^ (key % CH))]);
-          const bf16x8_t B = __builtin_bit_cast(bf16x8_t, qf[ds]);
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, sc, 0, 0, 0);
-        }
-      }
-      // raw scores; the 1/sqrt(d) scale (in log2 units) is applied inside the
-      // exponent.  Blocks of context keys only need no mask.
-      float mloc = -INFINITY;
-      const int kb0 = sub + kb * 32;
-      if (kb0 + 32 <= min(L, k1)) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sc[v]);
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kb0 + 8 * (v >> 2) + 4 * h + (v & 3);
-          bool vis = row_ok && key < k1;
-          if (vis && key >= L) vis = (anc >> (key - L)) & 1ull;
-          sc[v] = vis ? sc[v] : -INFINITY;
-          mloc = fmaxf(mloc, sc[v]);
-        }
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const float base = m_new == -INFINITY ? 0.0f : m_new;
-      const float nbs = -base * a.scale_log2;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - base) * a.scale_log2);
-      // P is split into two bf16 pieces (hi = bf16(p), lo = bf16(p - hi)) so the
-      // P V product on bf16 MFMA keeps 16 significant bits of every weight.
-      float lsum = 0.0f;
-      uint32_t pk[8], pl[8];
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[v], a.scale_log2, nbs));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[v + 1], a.scale_log2, nbs));
-        lsum += p0 + p1;
-        const uint32_t hk = pack_bf16x2(p0, p1);
-        pk[v / 2] = hk;
-        pl[v / 2] = pack_bf16x2(p0 - __uint_as_float(hk << 16), p1 - __uint_as_float(hk & 0xFFFF0000u));
-      }
-      lsum += __shfl_xor(lsum, 32);
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-      if (__ballot(alpha != 1.0f)) {  // the running max moved for some row: rescale
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-      }
-
-      // O^T[d][row] += V^T[d][key] P^T[key][row]; MFMA q of this key block
-      // covers keys kb*32 + 16 q + 8 (i/4) + 4 h + i%4 for k-index 8 h + i.
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]));
-        const bf16x8_t Bl = __builtin_bit_cast(bf16x8_t, make_uint4(pl[4 * q], pl[4 * q + 1], pl[4 * q + 2], pl[4 * q + 3]));
-        const int r1 = kb * 32 + 16 * q + tr_key, r2 = r1 + 8;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d = 32 * db + tr_d;  // 4 columns, 8 bytes inside one 16-byte chunk
-          const int off1 = (r1 * CH + ((d >> 3) ^ v_swz<D>(r1))) * 16 + (d & 7) * 2;
-          const int off2 = (r2 * CH + ((d >> 3) ^ v_swz<D>(r2))) * 16 + (d & 7) * 2;
-          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vs_bytes + off1));
-          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vs_bytes + off2));
-          const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
-          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, o[db], 0, 0, 0);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bl, o[db], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keeps the operand reads of the two halves apart (register pressure)
+      for (int ds = 0; ds < D / 16; ++ds) {
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, kpre[st][ds]);
+        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, qs[qrow * CH + ((2 * ds + h) ^ (qrow % CH))]);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, sc, 0, 0, 0);
       }
     }
-  }
-
-  // single split: normalise and store; otherwise write (max, sum, O) partials
-  if (nsplit == 1) {
-    if (row_ok) {
-      const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-      const int c0 = (kh * a.G + gq) * D;
+    // raw scores; the 1/sqrt(d) scale (in log2 units) is applied inside the
+    // exponent.  Blocks of context keys only need no mask.
+    float mloc = -INFINITY;
+    const int kb0 = key0_of(i);
+    if (kb0 + KB <= min(L, k1)) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sc[v]);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kb0 + 8 * (v >> 2) + 4 * h + (v & 3);
+        bool vis = row_ok && key < k1;
+        if (vis && key >= L) vis = (anc >> (key - L)) & 1ull;
+        sc[v] = vis ? sc[v] : -INFINITY;
+        mloc = fmaxf(mloc, sc[v]);
+      }
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc);
+    const float base = m_new == -INFINITY ? 0.0f : m_new;
+    const float nbs = -base * a.scale_log2;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - base) * a.scale_log2);
+    // P is split into two bf16 pieces (hi = bf16(p), lo = bf16(p - hi)) so the
+    // P V product on bf16 MFMA keeps 16 significant bits of every weight.
+    float lsum = 0.0f;
+    uint32_t pk[8], pl[8];
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[v], a.scale_log2, nbs));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[v + 1], a.scale_log2, nbs));
+      lsum += p0 + p1;
+      const uint32_t hk = pack_bf16x2(p0, p1);
+      pk[v / 2] = hk;
+      pl[v / 2] = pack_bf16x2(p0 - __uint_as_float(hk << 16), p1 - __uint_as_float(hk & 0xFFFF0000u));
+    }
+    lsum += __shfl_xor(lsum, 32);
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+    if (__ballot(alpha != 1.0f)) {  // the running max moved for some row: rescale
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          a.out[attn_out_index<D>(a, nb + node, c0 + db * 32 + 8 * (v >> 2) + 4 * h + (v & 3))] =
-              (uint16_t)f32_to_bf16(o[db][v] * inv);
+        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
     }
-    return;
+    // O^T[d][row] += V^T[d][key] P^T[key][row]; MFMA q of the block covers
+    // keys 16 q + 8 (i/4) + 4 h + i%4 for k-index 8 h + i.
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bf16x8_t B = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]));
+      const bf16x8_t Bl = __builtin_bit_cast(bf16x8_t, make_uint4(pl[4 * q], pl[4 * q + 1], pl[4 * q + 2], pl[4 * q + 3]));
+      const int r1 = 16 * q + tr_key, r2 = r1 + 8;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * db + tr_d;  // 4 columns, 8 bytes inside one 16-byte chunk
+        const int off1 = (r1 * CH + ((d >> 3) ^ v_swz<D>(r1))) * 16 + (d & 7) * 2;
+        const int off2 = (r2 * CH + ((d >> 3) ^ v_swz<D>(r2))) * 16 + (d & 7) * 2;
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vs_bytes + off1));
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vs_bytes + off2));
+        const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bl, o[db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keeps the operand reads of the two halves apart (register pressure)
+    }
+  };
+
+  // The stage index is a compile-time constant (the register ring never
+  // moves) and the main loop has no data-dependent branch around its loads,
+  // so each stash waits only for its own block.  One wavefront's LDS
+  // operations complete in order; the fences keep the compiler from moving
+  // a stash across the previous block's reads.
+  auto stage = [&](int i, auto stc, bool do_fetch) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    lds_fence();
+    stash(st);
+    lds_fence();
+    if (do_fetch) fetch(i + NPF - 1, (st + NPF - 1) % NPF);
+    compute(i, st);
+  };
+#pragma unroll
+  for (int st = 0; st < NPF - 1; ++st) fetch(st, st);
+  if (tid < 32 * CH) qs[qr * CH + (qc ^ (qr % CH))] = qv;
+  __syncthreads();  // Q in LDS
+  int c0 = 0;
+  for (; c0 + NPF <= nbw; c0 += NPF) {
+    stage(c0, std::integral_constant<int, 0>{}, true);
+    if constexpr (NPF > 1) stage(c0 + 1, std::integral_constant<int, 1 % NPF>{}, true);
+    if constexpr (NPF > 2) stage(c0 + 2, std::integral_constant<int, 2 % NPF>{}, true);
+    if constexpr (NPF > 3) stage(c0 + 3, std::integral_constant<int, 3 % NPF>{}, true);
   }
-  if (wave * 32 >= R) return;
-  // partial rows: [kv head][split][padded rows]; this wavefront's 32-row block
-  // is stored in the accumulator layout: element (db, v) of lane l at
-  // block * D + (db * 16 + v) * 64 + l
-  const int64_t pbase = ((int64_t)kh * a.max_splits + split) * a.rows_total + a.pr.prow[r] + wave * 32;
-  float* pob = a.po + pbase * D;
+  // the last nbw % NPF blocks are already in flight
+  if constexpr (NPF > 1)
+    if (c0 < nbw) stage(c0, std::integral_constant<int, 0>{}, false);
+  if constexpr (NPF > 2)
+    if (c0 + 1 < nbw) stage(c0 + 1, std::integral_constant<int, 1 % NPF>{}, false);
+  if constexpr (NPF > 3)
+    if (c0 + 2 < nbw) stage(c0 + 2, std::integral_constant<int, 2 % NPF>{}, false);
+
+  // combine the wavefronts' states (wavefront order) in LDS
+  __syncthreads();
+  float* ob = (float*)&tiles[0][0][0];  // [wave][db * 16 + v][lane]
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) pob[(db * 16 + v) * 64 + lane] = o[db][v];
-  if (h == 0) {  // the running max is a raw score (unscaled)
-    a.pm[pbase + (lane & 31)] = m_run;
-    a.pl[pbase + (lane & 31)] = l_run;
+    for (int v = 0; v < 16; ++v) ob[(wave * NACC + db * 16 + v) * 64 + lane] = o[db][v];
+  if (h == 0) {
+    ml[wave][0][lane & 31] = m_run;
+    ml[wave][1][lane & 31] = l_run;
+  }
+  __syncthreads();
+  const int64_t pbase = ((int64_t)kh * a.max_splits + split) * a.rows_total + a.pr.prow[r] + rb * 32;
+  // every element of this thread has lane tid % 64, hence row tid % 32
+  const int ln = lane, rw = lane & 31;
+  float mx = ml[0][0][rw];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, ml[w][0][rw]);
+  const float bse = mx == -INFINITY ? 0.0f : mx;
+  float wt[NW], den = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float mw = ml[w][0][rw];
+    wt[w] = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mw - bse) * a.scale_log2);
+    den += ml[w][1][rw] * wt[w];
+  }
+  static_assert(NACC % NW == 0, "whole elements per thread");
+#pragma unroll
+  for (int it = 0; it < NACC / NW; ++it) {
+    const int dv = wave + NW * it;  // element (dv, lane) of the block in accumulator layout
+    const int e = dv * 64 + ln;
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc += ob[(w * NACC + dv) * 64 + ln] * wt[w];
+    const int rr = rb * 32 + rw;
+    if (nsplit == 1) {  // normalise and store
+      if (rr < R) {
+        const int db = dv >> 4, v = dv & 15;
+        const int dd = db * 32 + 8 * (v >> 2) + 4 * (ln >> 5) + (v & 3);
+        const int g2 = rr / n, nd = rr % n;
+        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+        a.out[attn_out_index<D>(a, nb + nd, (kh * a.G + g2) * D + dd)] = (uint16_t)f32_to_bf16(acc * inv);
+      }
+    } else {  // partial rows [kv head][split][padded rows], accumulator layout
+      a.po[pbase * D + e] = acc;
+      if (dv == 0 && ln < 32) {  // the running max is a raw score (unscaled)
+        a.pm[pbase + rw] = mx;
+        a.pl[pbase + rw] = den;
+      }
+    }
   }
 }
 
@@ -388,25 +476,32 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
 }
 
 // Key splits are sized so that one launch has about this many workgroups
-// (one per compute unit: a workgroup fills a CU's register file).
-constexpr int kAttnTargetGroups = 256;
+// (one per compute unit).
+#ifndef TVP_ATTN_TARGET
+#define TVP_ATTN_TARGET 256
+#endif
+constexpr int kAttnTargetGroups = TVP_ATTN_TARGET;
+// Blocks of 32 keys per wavefront kept in flight (including the one in LDS).
+constexpr int kAttnStages = 2;
 
 struct AttnPlan {
-  int kr, max_splits, rows_total, nthreads;
+  int kr, max_splits, rows_total, row_blocks;
   size_t off_po, off_pm, off_pl, bytes;
 };
 
 // max_keys: largest ctx_len + n over the requests; r_max: largest G * n;
 // rows_total: partial rows over all requests (each request's G * n rounded
-// up to a multiple of 32).  Splits are multiples of the 64-key stage.
+// up to a multiple of 32).  A split is a multiple of 32 keys per
+// wavefront, at most 64 splits.
 static AttnPlan attn_plan(int hkv, int d, int r_max, int rows_total, int max_keys, int n_req) {
   AttnPlan p{};
-  const int target = std::max(1, kAttnTargetGroups / std::max(1, n_req * hkv));
-  p.kr = 64 * (int)ceil_div(std::max(max_keys, 1), 64LL * target);
+  p.row_blocks = (r_max + 31) / 32;
+  const int target = std::max(1, kAttnTargetGroups / std::max(1, n_req * hkv * p.row_blocks));
+  const int unit = 32 * kAttnWaves;
+  p.kr = unit * (int)ceil_div(std::max(max_keys, 1), (int64_t)unit * target);
   while (max_keys > 64 * p.kr) p.kr *= 2;  // at most 64 splits (merge weights live in LDS)
   p.max_splits = max_keys > 0 ? (max_keys + p.kr - 1) / p.kr : 1;
   p.rows_total = rows_total;
-  p.nthreads = r_max <= 128 ? 256 : 512;
   const size_t rows = (size_t)hkv * p.max_splits * p.rows_total;
   size_t off = 0;
   p.off_po = off;
@@ -461,16 +556,16 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
   a.pl = (float*)(sb + p.off_pl);
   a.out = out;
   a.out_packed = out_packed;
-  a.row_blocks = (r_max + 31) / 32;
-  const dim3 grid((unsigned)(n_req * hkv * p.max_splits));
+  a.row_blocks = p.row_blocks;
+  a.units = n_req * hkv * p.max_splits;
+  a.units8 = (int)align_up((size_t)a.units, 8);
+  const dim3 grid((unsigned)(a.units8 * p.row_blocks));
   const dim3 mgrid((unsigned)(n_req * hkv * a.row_blocks * 4));
   if (d == 128) {
-    if (p.nthreads == 256) tree_attn_kernel<128, 256><<<grid, dim3(256), 0, stream>>>(a);
-    else tree_attn_kernel<128, 512><<<grid, dim3(512), 0, stream>>>(a);
+    tree_attn_kernel<128, kAttnStages><<<grid, dim3(kAttnWaves * 64), 0, stream>>>(a);
     if (p.max_splits > 1) tree_attn_merge_kernel<128><<<mgrid, dim3(256), 0, stream>>>(a);
   } else if (d == 64) {
-    if (p.nthreads == 256) tree_attn_kernel<64, 256><<<grid, dim3(256), 0, stream>>>(a);
-    else tree_attn_kernel<64, 512><<<grid, dim3(512), 0, stream>>>(a);
+    tree_attn_kernel<64, kAttnStages><<<grid, dim3(kAttnWaves * 64), 0, stream>>>(a);
     if (p.max_splits > 1) tree_attn_merge_kernel<64><<<mgrid, dim3(256), 0, stream>>>(a);
   } else {
     return TVP_ERR_SHAPE;
