@@ -107,6 +107,18 @@ __device__ inline int v_swz(int key) {
   return D == 128 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2);
 }
 
+// Both halves of a wavefront see {x[l], x[l ^ 32]} after one
+// v_permlane32_swap (a VALU op, no LDS round trip); the reductions below
+// combine them lower half first, so lanes l and l ^ 32 get identical bits.
+__device__ inline float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Compiler fence for one wavefront's LDS accesses (they complete in order).
 __device__ inline void lds_fence() {
   asm volatile("" ::: "memory");
@@ -135,7 +147,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
   // holds the wavefronts' O
   __shared__ uint4 tiles[NW][2][KB * CH];
   __shared__ uint4 qs[32 * CH];    // Q of the row block [row][chunk ^ (row % CH)]
-  __shared__ float ml[NW][2][32];  // per wavefront and row: running max (raw score), sum
+  __shared__ float ml[NW][2][32];  // per wavefront and row: exponent base (a raw score), sum
   static_assert(sizeof(tiles) >= NW * NACC * 64 * sizeof(float), "O of all wavefronts fits the tiles");
 
   // block -> (row block, unit): the row blocks of one (request, kv head,
@@ -171,6 +183,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
     qv = *(const uint4*)(a.q + ((int64_t)(nb + rr % n) * a.hq + kh * a.G + rr / n) * D + 8 * qc);
   }
   const uint64_t anc = row_ok ? a.anc[nb + node] : 0ull;
+  const int klim = row_ok ? k1 : 0;  // keys below klim may be visible to this lane's row
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16_t o[NDB];
@@ -247,17 +260,24 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = kb0 + 8 * (v >> 2) + 4 * h + (v & 3);
-        bool vis = row_ok && key < k1;
-        if (vis && key >= L) vis = (anc >> (key - L)) & 1ull;
+        const bool anc_ok = ((anc >> ((key - L) & 63)) & 1ull) != 0;
+        const bool vis = (key < klim) & ((key < L) | anc_ok);  // no branches
         sc[v] = vis ? sc[v] : -INFINITY;
         mloc = fmaxf(mloc, sc[v]);
       }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
+    mloc = xor32_max(mloc);
+    // The exponent base m_run moves only when a row's maximum exceeds it by
+    // more than 8 in log2 units (always at the row's first visible key):
+    // the weights stay below 2^8, exact to the same relative precision in
+    // fp32, and the rescale of O is skipped on almost every block.  O, the
+    // sum and the recorded maximum all refer to the same base, so the result
+    // is the same softmax.
+    const bool grow = (mloc - m_run) * a.scale_log2 > 8.0f;
+    const float m_new = grow ? mloc : m_run;
     const float base = m_new == -INFINITY ? 0.0f : m_new;
     const float nbs = -base * a.scale_log2;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - base) * a.scale_log2);
+    const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - base) * a.scale_log2) : 1.0f;
     // P is split into two bf16 pieces (hi = bf16(p), lo = bf16(p - hi)) so the
     // P V product on bf16 MFMA keeps 16 significant bits of every weight.
     float lsum = 0.0f;
@@ -271,10 +291,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
       pk[v / 2] = hk;
       pl[v / 2] = pack_bf16x2(p0 - __uint_as_float(hk << 16), p1 - __uint_as_float(hk & 0xFFFF0000u));
     }
-    lsum += __shfl_xor(lsum, 32);
+    lsum = xor32_sum(lsum);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
-    if (__ballot(alpha != 1.0f)) {  // the running max moved for some row: rescale
+    if (__ballot(grow)) {  // the base moved for some row: rescale
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -380,7 +400,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
       }
     } else {  // partial rows [kv head][split][padded rows], accumulator layout
       a.po[pbase * D + e] = acc;
-      if (dv == 0 && ln < 32) {  // the running max is a raw score (unscaled)
+      if (dv == 0 && ln < 32) {  // the exponent base is a raw score (unscaled)
         a.pm[pbase + rw] = mx;
         a.pl[pbase + rw] = den;
       }
