@@ -9,7 +9,8 @@ argmax, acceptance walk, KV commit) plus the readback of the accepted length.
 
 Prints one JSON line: verify steps/s (``value``), tokens/s, the achieved HBM
 GB/s of the whole step, the roofline entry of the dominant kernel (the fused
-gate/up W12 GEMM, timed with HIP events on its own stream) and the CPU
+gate/up W12 GEMM and the launch that finishes its K-sliced remaining
+groups, timed together with HIP events on their stream) and the CPU
 oracle's rate on a bounded sample.
 """
 
@@ -353,7 +354,8 @@ def main() -> int:
                    "ffn": cfg.ffn, "vocab": cfg.vocab, "nodes": cfg.n_nodes, "ctx_len": cfg.ctx_len,
                    "weights": "W12 (random-init bf16, per-channel sigma log-uniform [0.005,0.05], 1% zeros, "
                               "0.05% outliers x1000)", "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "w12_skinny_kernel<32,2,2,SWIGLU> (fused gate/up, 34816x5120)", "bound": "hbm",
+        "roofline": {"kernel": ("w12_skinny_kernel<32,2,2,SWIGLU> + w12_rem_fixup_kernel<SWIGLU> "
+                                "(fused gate/up, 34816x5120: 512 whole groups, 32 in 8 K slices)"), "bound": "hbm",
                      "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "us_per_launch": round(g_ms * 1000.0, 2), "bytes_per_launch": int(g_bytes)},

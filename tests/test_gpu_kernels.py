@@ -208,6 +208,69 @@ def test_gemm_fused_epilogues(tvp, cuda):
     assert np.array_equal(am.cpu().numpy(), np.argmax(lg.cpu().numpy(), axis=1))
 
 
+@pytest.mark.parametrize("m", [9, 32])
+def test_gemm_remaining_groups_split_over_k(tvp, cuda, m):
+    """More channel groups than CUs, not a multiple of them: the groups past
+    the last full round are computed as K slices and finished by a second
+    launch.  Each whole-K epilogue through that path against the oracle."""
+    H, F, hq, hkv, d = 1000, 4200, 120, 8, 64  # 263, 263 and 272 tiles of 32 channels
+    print(f"[gemm remaining groups] m={m} swiglu/resid/qkv", flush=True)
+    rng = np.random.default_rng(m)
+    w_gu = bf16_bits_numpy(gen_linear_bf16(make_generator(41), 2 * F, H, TINY_RECIPE))
+    xb = _x(m, H, 42, cuda)
+    u = torch.zeros(m, F, dtype=torch.bfloat16, device=cuda)
+    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=u.data_ptr(), ldy=F)
+    pgu = _packed(tvp, w_gu, cuda, tvp.TVP_CHAN_GATEUP, F)
+    tvp.w12_gemm_ex(xb, pgu, epi)
+    torch.cuda.synchronize()
+    gu = from_bits(_u16(xb)) @ from_bits(w_gu).T
+    ref = round_bf16(om.silu(gu[:, :F]) * gu[:, F:])
+    got = from_bits(_u16(u))
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+    u2 = torch.zeros_like(u)
+    tvp.w12_gemm_ex(xb, pgu, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=u2.data_ptr(), ldy=F))
+    torch.cuda.synchronize()
+    assert torch.equal(u, u2)  # reproducible bit for bit
+    # residual add on 8400 plain channels
+    w_o = bf16_bits_numpy(gen_linear_bf16(make_generator(43), 2 * F, H, TINY_RECIPE))
+    x = _x(m, H, 44, cuda)
+    res = _x(m, 2 * F, 45, cuda)
+    y = res.clone()
+    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_RESID, y=y.data_ptr(), ldy=2 * F, resid=y.data_ptr(), ldr=2 * F)
+    tvp.w12_gemm_ex(x, _packed(tvp, w_o, cuda), epi)
+    torch.cuda.synchronize()
+    acc = from_bits(_u16(x)) @ from_bits(w_o).T
+    ref = round_bf16(from_bits(_u16(res)) + acc)
+    got = from_bits(_u16(y))
+    fp32_err = 4.0 * H * 2.0 ** -24 * (np.abs(from_bits(_u16(x))) @ np.abs(from_bits(w_o)).T)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 2.0 * fp32_err)
+    assert np.mean(got == ref) > 0.98
+    # qkv: rope at positions, k and v written to cache slots
+    w_qkv = bf16_bits_numpy(gen_linear_bf16(make_generator(46), (hq + 2 * hkv) * d, H, TINY_RECIPE))
+    xa = _x(m, H, 47, cuda)
+    s_max = 64
+    kc = torch.zeros(hkv, s_max, d, dtype=torch.bfloat16, device=cuda)
+    vc = torch.zeros_like(kc)
+    q = torch.zeros(m, hq * d, dtype=torch.bfloat16, device=cuda)
+    pos = rng.integers(0, 9000, m).astype(np.int32)
+    slot = rng.permutation(s_max)[:m].astype(np.int32)
+    pos_t, slot_t = torch.as_tensor(pos, device=cuda), torch.as_tensor(slot, device=cuda)
+    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_QKV, y=q.data_ptr(), ldy=hq * d, pos=pos_t.data_ptr(),
+                              slot=slot_t.data_ptr(), k_cache=kc.data_ptr(), v_cache=vc.data_ptr(),
+                              s_stride=s_max, rope_theta=1e6)
+    tvp.w12_gemm_ex(xa, _packed(tvp, w_qkv, cuda, tvp.TVP_CHAN_QKV, hq, hkv, d), epi)
+    torch.cuda.synchronize()
+    qkv = from_bits(_u16(xa)) @ from_bits(w_qkv).T
+    q_ref = round_bf16(om.rope(qkv[:, : hq * d].reshape(m, hq, d), pos, 1e6)).reshape(m, hq * d)
+    k_ref = round_bf16(om.rope(qkv[:, hq * d: (hq + hkv) * d].reshape(m, hkv, d), pos, 1e6))
+    v_ref = round_bf16(qkv[:, (hq + hkv) * d:].reshape(m, hkv, d))
+    for got, ref in ((from_bits(_u16(q)), q_ref),
+                     (from_bits(_u16(kc)).transpose(1, 0, 2)[slot], k_ref),
+                     (from_bits(_u16(vc)).transpose(1, 0, 2)[slot], v_ref)):
+        assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-4 * np.abs(ref).max())
+        assert np.mean(got == ref) > 0.97
+
+
 def test_argmax_ties_go_to_smallest_id(tvp, cuda):
     # identical channels produce exactly equal logits: the smallest id must win
     H, V = 256, 2048

@@ -63,9 +63,17 @@ struct GemmArgs {
   float* logits;
   int64_t ldl;
   int y_packed;  // SWIGLU: write y in the packed activation layout (rows <= 32)
+  // Skinny, whole-K epilogues: workgroups 0 .. full_groups-1 take whole
+  // groups; the remaining groups are cut into rem_splits K slices of rem_kps
+  // blocks (rem_kbs per wavefront) whose sums go to rpart [slice][row][ldrp]
+  // and are finished by w12_rem_fixup_kernel.
+  int full_groups, rem_splits, rem_kps, rem_kbs, rem_tpw;
+  float* rpart;
+  int ldrp;
 };
 
 constexpr int kArgmaxMaxRows = 192;
+constexpr int kRemMaxSplits = 16;  // K slices of a remaining group (whole-K epilogues)
 
 // Row-major x [m][ldx] -> packed (rows >= m and columns >= k_in are zero).
 __global__ __launch_bounds__(256) void pack_x_kernel(const uint16_t* __restrict__ x, int64_t ldx, int m,
@@ -266,13 +274,32 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
   const int KW = blockDim.x >> 6;
   // Workgroup -> work: one workgroup per group of TPW tiles over the whole K
   // range, or, with the partial-sum epilogue, one per (group, K slice).
+  // With a whole-K epilogue, workgroups past full_groups take one K slice of
+  // a remaining group (so every CU gets the same share of the stream).
   const int b = blockIdx.x;
-  const int grp = MODE == kEpiPartial ? b / a.splits : b;
-  const int slice = MODE == kEpiPartial ? b % a.splits : 0;
+  const bool rem = MODE != kEpiPartial && b >= a.full_groups;
+  int grp, slice, ks0, ks1, kbs;  // ks0 .. ks1: this workgroup's K range
+  if (MODE == kEpiPartial) {
+    grp = b / a.splits;
+    slice = b % a.splits;
+    ks0 = slice * a.kps;
+    ks1 = min(a.n_kb, ks0 + a.kps);
+    kbs = a.kbs_split;
+  } else if (!rem) {
+    grp = b;
+    slice = 0;
+    ks0 = 0;
+    ks1 = a.n_kb;
+    kbs = a.kbs;
+  } else {
+    const int rr = b - a.full_groups;
+    grp = a.full_groups + rr / a.rem_splits;
+    slice = rr % a.rem_splits;
+    ks0 = slice * a.rem_kps;
+    ks1 = min(a.n_kb, ks0 + a.rem_kps);
+    kbs = a.rem_kbs;
+  }
   const int t0 = grp * TPW;
-  const int ks0 = MODE == kEpiPartial ? slice * a.kps : 0;
-  const int ks1 = MODE == kEpiPartial ? min(a.n_kb, ks0 + a.kps) : a.n_kb;  // this workgroup's K range
-  const int kbs = MODE == kEpiPartial ? a.kbs_split : a.kbs;
   const int kb0 = ks0 + wave * kbs;
   const int kb1 = min(ks1, kb0 + kbs);
   const int nblk = kb1 > kb0 ? kb1 - kb0 : 0;  // <= 63
@@ -485,7 +512,36 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
     return v;
   };
   const int nc = min(NC, a.n_pad - t0 * 32);
+  if (MODE != kEpiPartial && rem) {  // this K slice's sums, [slice][row][channel - first remaining channel]
+    const int cb = t0 * 32 - a.full_groups * TPW * 32;
+    for (int idx = threadIdx.x; idx < M * nc; idx += KW * 64) {
+      const int row = idx / nc, c = idx % nc;
+      a.rpart[((int64_t)slice * M + row) * a.ldrp + cb + c] = sum_waves(row, t0 * 32 + c);
+    }
+    return;
+  }
   epilogue<MODE>(a, t0 * 32, nc, M, threadIdx.x, KW * 64, blockIdx.x, sum_waves, slice);
+}
+
+// One workgroup per tile of the remaining groups: the K slices summed in
+// slice order, then the same epilogue as a whole group.
+template <int MODE>
+__global__ __launch_bounds__(512) void w12_rem_fixup_kernel(GemmArgs a) {
+  const int cfirst = a.full_groups * a.rem_tpw * 32;
+  const int c0 = cfirst + blockIdx.x * 32;
+  const int nc = min(32, a.n_pad - c0);
+  auto sum_slices = [&](int row, int col) {
+    const float* src = a.rpart + (int64_t)row * a.ldrp + (col - cfirst);
+    const int64_t sstride = (int64_t)a.m * a.ldrp;
+    float v[kRemMaxSplits];
+#pragma unroll
+    for (int sl = 0; sl < kRemMaxSplits; ++sl) v[sl] = sl < a.rem_splits ? src[sl * sstride] : 0.0f;  // all in flight
+    float acc = v[0];
+#pragma unroll
+    for (int sl = 1; sl < kRemMaxSplits; ++sl) acc = sl < a.rem_splits ? acc + v[sl] : acc;
+    return acc;
+  };
+  epilogue<MODE>(a, c0, nc, a.m, threadIdx.x, 512, 0, sum_slices, 0);
 }
 
 template <int ROWS>
@@ -731,7 +787,8 @@ struct GemmPlan {
   bool skinny;
   int MT, RB, TPW, RD, KW, TG, groups, splits, kbs, kps, ntasks, grid;
   int kbs_split, key_slots;
-  size_t keys_off, scratch_bytes;
+  int full_groups, rem_groups, rem_splits, rem_kps, rem_kbs;  // whole-K epilogues, see GemmArgs
+  size_t keys_off, rem_off, scratch_bytes;
 };
 
 // Work decomposition.  Skinny (m <= 32): one workgroup per TPW tiles whose KW
@@ -770,7 +827,9 @@ static double slice_cost(int gsplit, int s, int kps) {
   return per_cu <= 1 ? 1.5 * cost : cost;
 }
 
-static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1) {
+// rem_ok: the epilogue can be finished by w12_rem_fixup_kernel (not argmax,
+// whose per-row reduction over 32 columns would run on too few lanes).
+static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bool rem_ok = true) {
   GemmPlan p{};
   const int64_t n_pad = (int64_t)w->n_tiles * 32;
   const int nkb = w->n_kb;
@@ -807,6 +866,33 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1) {
     p.kbs_split = p.kps > 0 ? (int)ceil_div(p.kps, p.KW) : 0;
     p.ntasks = nwg;
     p.grid = nwg;
+    // Whole-K epilogue with more groups than CUs but not a multiple of them:
+    // the groups past the last full round go out as K slices, about one
+    // slice per CU, so no CU streams a whole extra group at the end.
+    p.full_groups = p.groups;
+    const int R = p.groups > kNumCUs ? p.groups % kNumCUs : 0;
+    if (!partial && rem_ok && R > 0 && nkb >= 4) {
+      // slices per remaining group: the fewest that minimise the busiest
+      // CU's share of slices, ceil(R * s / CUs) / s
+      int sl = 1;
+      double best = 1.0;
+      for (int c = 2; c <= std::min(kRemMaxSplits, nkb / 2); ++c) {
+        const double v = (double)ceil_div((int64_t)R * c, kNumCUs) / c;
+        if (v < best - 1e-9) best = v, sl = c;
+      }
+      p.rem_kps = (int)ceil_div(nkb, sl);
+      p.rem_splits = (int)ceil_div(nkb, p.rem_kps);
+      p.rem_kbs = (int)ceil_div(p.rem_kps, p.KW);
+      p.rem_groups = R;
+      p.full_groups = p.groups - R;
+      p.grid = p.full_groups + R * p.rem_splits;
+      p.ntasks = p.grid;
+      if (p.rem_splits < 2) {  // no gain: whole groups
+        p.rem_groups = 0;
+        p.full_groups = p.groups;
+        p.grid = p.ntasks = p.groups;
+      }
+    }
   } else {
     p.TPW = 1;
     p.RD = 0;
@@ -829,7 +915,8 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1) {
   p.key_slots = p.skinny ? p.grid : p.groups;
   p.keys_off = p.skinny ? align_up((size_t)std::max(nkb, 1) * 4096, 256)
                         : align_up((size_t)p.splits * m * n_pad * 4, 256);
-  p.scratch_bytes = p.keys_off + align_up((size_t)std::max(p.key_slots, 1) * m * 8, 256);
+  p.rem_off = p.keys_off + align_up((size_t)std::max(p.key_slots, 1) * m * 8, 256);
+  p.scratch_bytes = p.rem_off + align_up((size_t)p.rem_splits * m * p.rem_groups * p.TPW * 32 * 4, 256);
   return p;
 }
 
@@ -845,6 +932,17 @@ static void launch_skinny(const GemmArgs& a, const GemmPlan& p, hipStream_t stre
     case TVP_EPI_QKV: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_QKV><<<grid, block, lds, stream>>>(a); break;
     case kEpiPartial: w12_skinny_kernel<MT, TPW, RD, kEpiPartial><<<grid, block, lds, stream>>>(a); break;
     default: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_ARGMAX><<<grid, block, lds, stream>>>(a); break;
+  }
+  if (p.rem_groups > 0) {  // launch errors of both are read by the caller's check
+    const dim3 fgrid((unsigned)(a.n_tiles - p.full_groups * TPW));
+    switch (a.mode) {
+      case TVP_EPI_F32: w12_rem_fixup_kernel<TVP_EPI_F32><<<fgrid, 512, 0, stream>>>(a); break;
+      case TVP_EPI_BF16: w12_rem_fixup_kernel<TVP_EPI_BF16><<<fgrid, 512, 0, stream>>>(a); break;
+      case TVP_EPI_RESID: w12_rem_fixup_kernel<TVP_EPI_RESID><<<fgrid, 512, 0, stream>>>(a); break;
+      case TVP_EPI_SWIGLU: w12_rem_fixup_kernel<TVP_EPI_SWIGLU><<<fgrid, 512, 0, stream>>>(a); break;
+      case TVP_EPI_QKV: w12_rem_fixup_kernel<TVP_EPI_QKV><<<fgrid, 512, 0, stream>>>(a); break;
+      default: break;  // argmax and partial-sum launches never split their remaining groups
+    }
   }
 }
 
@@ -892,7 +990,7 @@ int gemm_ksplits(int64_t m, const tvp_w12_packed* w, int ksplit) {
 void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes, int ksplit) {
   const GemmPlan p = make_plan(m, w, ksplit);
   *groups = p.groups;
-  *scratch_bytes = p.scratch_bytes;
+  *scratch_bytes = std::max(p.scratch_bytes, make_plan(m, w, ksplit, false).scratch_bytes);  // argmax: no split
 }
 
 int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
@@ -901,7 +999,7 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
   if (!w || !epi || !w->blob || !cnt) return TVP_ERR_ARG;
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
   if (ksplit > 1 && epi->mode != kEpiPartial) return TVP_ERR_ARG;
-  const GemmPlan p = make_plan(m, w, ksplit);
+  const GemmPlan p = make_plan(m, w, ksplit, epi->mode != TVP_EPI_ARGMAX);
   if (xp) {
     if (!p.skinny || ((uintptr_t)xp) % 16 != 0) return TVP_ERR_ARG;
   } else if (w->k_in > 0) {
@@ -939,6 +1037,13 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
   a.kbs = p.kbs;
   a.kps = p.kps;
   a.kbs_split = p.kbs_split;
+  a.full_groups = p.full_groups;
+  a.rem_splits = std::max(p.rem_splits, 1);
+  a.rem_kps = p.rem_kps;
+  a.rem_kbs = p.rem_kbs;
+  a.rem_tpw = p.TPW;
+  a.rpart = (float*)((uint8_t*)scratch + p.rem_off);
+  a.ldrp = p.rem_groups * p.TPW * 32;
   a.ntasks = p.ntasks;
   a.cnt = cnt;
   a.keys = (unsigned long long*)((uint8_t*)scratch + p.keys_off);
