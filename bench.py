@@ -8,7 +8,8 @@ SwiGLU 17408, vocab 151936, random-init W12 weights), committed context 4096,
 argmax, acceptance walk, KV commit) plus the readback of the accepted length.
 
 Prints one JSON line: verify steps/s (``value``), tokens/s, the achieved HBM
-GB/s of the whole step, the roofline entry of the dominant kernel (the fused
+GB/s of the whole step (also as a fraction of a streaming-read probe run on
+the same GPU), the roofline entry of the dominant kernel (the fused
 gate/up W12 GEMM and the launch that finishes its K-sliced remaining
 groups, timed together with HIP events on their stream) and the CPU
 oracle's rate on a bounded sample.
@@ -174,6 +175,31 @@ def time_gateup(dm, cfg, iters: int):
     return ms, nbytes, p
 
 
+def read_probe_gbs(gib: int = 4, iters: int = 5) -> float:
+    """Sustained HBM read rate of a plain sequential stream on this GPU
+    (``tvp_read_probe`` over ``gib`` GiB, past the memory-side cache)."""
+    import torch
+
+    import tree_verification_pass_amd as tvp
+
+    dev = torch.device("cuda:0")
+    src = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    tvp.tvp_read_probe(src, sink)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        tvp.tvp_read_probe(src, sink)
+    e.record()
+    torch.cuda.synchronize()
+    rate = iters * src.numel() / (s.elapsed_time(e) * 1e-3) / 1e9
+    del src
+    torch.cuda.empty_cache()
+    return rate
+
+
 def cpu_baseline(dm, cfg, seed: int, tree):
     """The oracle (untuned) on one of the 64 decoder layers of one step: W12
     decode of the layer's four weights plus the layer's forward over the 32
@@ -324,6 +350,8 @@ def main() -> int:
     g_ms, g_bytes, _ = time_gateup(dm, cfg, args.gemm_iters)
     g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
     log(f"bench: gate/up W12 GEMM {g_ms * 1000:.1f} us/launch, {g_gbs:.0f} GB/s")
+    probe = read_probe_gbs()
+    log(f"bench: streaming-read probe {probe:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -348,6 +376,8 @@ def main() -> int:
         "mean_accepted": round(mean_acc, 3),
         "achieved_hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "read_probe_gbs": round(probe, 1),
+        "probe_frac": round(gbs / probe, 4),
         "bytes_per_step": int(nbytes),
         "config": {"workload": f"{cfg.name}-like verify step, {cfg.n_nodes}-node best-first tree, ctx {cfg.ctx_len}",
                    "n_layers": cfg.n_layers, "hidden": cfg.hidden, "heads": f"{cfg.n_heads}/{cfg.n_kv_heads}x{cfg.head_dim}",
@@ -357,7 +387,8 @@ def main() -> int:
         "roofline": {"kernel": ("w12_skinny_kernel<32,2,2,SWIGLU> + w12_rem_fixup_kernel<SWIGLU> "
                                 "(fused gate/up, 34816x5120: 512 whole groups, 32 in 8 K slices)"), "bound": "hbm",
                      "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
+                     "frac": round(g_gbs / HBM_PEAK_GBS, 4), "probe_frac": round(g_gbs / probe, 4),
+                     "traffic": recorded_traffic(),
                      "us_per_launch": round(g_ms * 1000.0, 2), "bytes_per_launch": int(g_bytes)},
         "cpu_baseline": cpu,
     }

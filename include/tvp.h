@@ -302,6 +302,17 @@ int verify_step_batched(tvp_plan* plan, int32_t n_req, const int32_t* ctx_len,
                         const int32_t* parents, int32_t commit, const tvp_verify_out* out,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------- measurement
+ * Streaming-read probe for the roofline (the measurement asks for each rate
+ * as a fraction of both the nominal HBM bandwidth and a read stream measured
+ * on the same GPU).  Reads the first bytes/16*16 bytes of src once, as a
+ * plain sequential stream, and writes 4096 words to sink.  Nothing else is
+ * touched; time it with events on `stream`.
+ *   src   device, 16-byte aligned, >= 16 bytes (caller-owned)
+ *   sink  device uint32 [4096] (caller-owned; contents meaningless)
+ * TVP_ERR_ARG on a null or misaligned pointer.                             */
+int tvp_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -440,3 +440,18 @@ def test_host_validation_launches_nothing(tvp, cuda):
     with pytest.raises(tvp.TvpError) as e:
         tvp.w12_gemm_px(xp, 4, pw, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_F32, y=y.data_ptr(), ldy=64, y_packed=1))
     assert e.value.status == tvp.TVP_ERR_ARG
+
+
+def test_read_probe_reads_every_word_once(tvp, cuda):
+    """The streaming-read probe of the measurement folds every 32-bit word of
+    its input exactly once: the XOR of its 4096 output words is the XOR of the
+    input (checked on a buffer that is not a multiple of the grid's stride)."""
+    print("[read probe] 3 MiB + 48 B", flush=True)
+    n_words = (3 << 20) // 4 + 12
+    words = np.random.default_rng(5).integers(0, 2 ** 32, n_words, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32).copy()).to(cuda)
+    sink = torch.zeros(4096, dtype=torch.int32, device=cuda)
+    tvp.tvp_read_probe(src, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert int(got) == int(np.bitwise_xor.reduce(words))

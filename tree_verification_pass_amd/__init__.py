@@ -118,12 +118,14 @@ _lib_verify_step = _sig("verify_step", ctypes.c_int,
 _lib_verify_step_batched = _sig("verify_step_batched", ctypes.c_int,
                                 [c_vp, c_i32, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32), c_i32, c_vp, c_vp,
                                  c_i32, ctypes.POINTER(TvpVerifyOut), c_vp, c_sz, c_vp])
+_lib_tvp_read_probe = _sig("tvp_read_probe", ctypes.c_int, [c_vp, c_sz, c_vp, c_vp])
 
 EXPORTED = ("tvp_status_string", "w12_encode_count", "w12_encode", "w12_decode", "w12_pack_size",
             "w12_pack_workspace", "w12_pack", "w12_gemm_workspace", "w12_gemm", "w12_gemm_ex",
             "w12_packed_x_elems", "w12_pack_x",
             "tree_attention_workspace", "tree_attention", "accept_path", "tvp_plan_create",
-            "tvp_plan_destroy", "verify_step_workspace", "verify_step", "verify_step_batched")
+            "tvp_plan_destroy", "verify_step_workspace", "verify_step", "verify_step_batched",
+            "tvp_read_probe")
 
 
 # ------------------------------------------------------------------ helpers
@@ -442,6 +444,16 @@ def verify_step_batched(plan: Plan, ctx_lens: Sequence[int], node_ptr: Sequence[
                                     1 if commit else 0, ctypes.byref(o), _ptr(plan.ws), plan.ws_bytes,
                                     _stream(tokens.device)), "verify_step_batched")
     return out
+
+
+def tvp_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """One streaming read of ``src`` (device, 16-byte aligned) on the current
+    stream; ``sink`` is a device int32/uint32 tensor of >= 4096 words."""
+    _dev_check(src, sink)
+    if sink.numel() * sink.element_size() < 4096 * 4:
+        raise ValueError("sink needs 4096 words")
+    _check(_lib_tvp_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(src.device)),
+           "tvp_read_probe")
 
 
 __all__ = [n for n in dir() if not n.startswith("_lib")]
