@@ -119,6 +119,10 @@ __device__ inline float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle):
+// loads past num_records return zero.
+constexpr int kBufWord3 = 0x00020000;
+
 // Compiler fence for one wavefront's LDS accesses (they complete in order).
 __device__ inline void lds_fence() {
   asm volatile("" ::: "memory");
@@ -162,7 +166,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
   const int nsplit = (T + a.kr - 1) / a.kr;
   if (split >= nsplit || rb * 32 >= R) return;
   const int k0 = split * a.kr, k1 = min(T, k0 + a.kr);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: block offsets stay scalar
   const int row = rb * 32 + (lane & 31);
   const bool row_ok = row < R;
   const int gq = row_ok ? row / n : 0, node = row_ok ? row % n : 0;
@@ -196,28 +201,27 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
   const int nbw = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;  // blocks of this wavefront
   auto key0_of = [&](int i) { return k0 + (wave + NW * i) * KB; };
 
-  // Block i of this wavefront into register stage st.  K arrives directly in
-  // the MFMA A-operand layout (lane: key lane % 32, 16-byte piece 2 ds + h of
-  // its row); V with CH consecutive lanes reading one 2*D-byte row, for the
-  // LDS tile.  Keys past the split are clamped to its last key (their scores
-  // are masked); a block past the wavefront's last is a placeholder in which
-  // every lane reads the same 16 bytes, so the number of loads in flight is
-  // the same on every path.
+  // Block i of this wavefront into register stage st, with buffer loads whose
+  // range ends at the split's last key: keys past it (the split's ragged end,
+  // or a whole placeholder block past the wavefront's last) read as zero
+  // without touching memory, their scores are masked, and every path keeps
+  // the same number of loads in flight.  K arrives directly in the MFMA
+  // A-operand layout (lane: key lane % 32, 16-byte piece 2 ds + h of its
+  // row); V with CH consecutive lanes reading one 2*D-byte row, for the LDS
+  // tile.  Only the scalar block offset changes from block to block.
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   u32x4_t kpre[NPF][PER], vpre[NPF][PER];
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, k1 * D * 2, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, k1 * D * 2, kBufWord3);
+  const int koff = (lane & 31) * D * 2 + 16 * h;
   auto fetch = [&](int i, int st) __attribute__((always_inline)) {
-    const bool real = i < nbw;
-    const int kb0 = key0_of(i);
-    const int kk = real ? min(kb0 + (lane & 31), k1 - 1) : k1 - 1;
+    const int soff = key0_of(i) * D * 2;
 #pragma unroll
     for (int ds = 0; ds < PER; ++ds)
-      kpre[st][ds] = *(const u32x4_t*)(kbase + (int64_t)kk * D + (real ? 16 * ds + 8 * h : 0));
+      kpre[st][ds] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 32 * ds, soff, 0));
 #pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int pc = lane + 64 * it;
-      const int kv = real ? min(kb0 + pc / CH, k1 - 1) : k1 - 1, c = real ? pc % CH : 0;
-      vpre[st][it] = *(const u32x4_t*)(vbase + (int64_t)kv * D + 8 * c);
-    }
+    for (int it = 0; it < PER; ++it)
+      vpre[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, 16 * lane + 1024 * it, soff, 0));
   };
   auto stash = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
