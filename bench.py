@@ -130,9 +130,11 @@ def make_trees(dm, cfg, n_trees: int, seed: int):
     return trees
 
 
-def step_bytes(dm, cfg, mean_accepted: float) -> float:
-    """Algorithmic HBM bytes of one step (W12 stream + KV + embedding rows + commit)."""
-    n, L, hkv, d = cfg.n_nodes, cfg.ctx_len, cfg.n_kv_heads, cfg.head_dim
+def step_bytes(dm, cfg, mean_accepted: float, n: int = 0) -> float:
+    """Algorithmic HBM bytes of one step over n nodes (default: the config's
+    tree size): W12 stream + KV + embedding rows + commit."""
+    n = n or cfg.n_nodes
+    L, hkv, d = cfg.ctx_len, cfg.n_kv_heads, cfg.head_dim
     w = 0
     for p in [dm.lm_head] + [x for Lr in dm.layers for x in (Lr.wqkv, Lr.wo, Lr.wgu, Lr.wdown)]:
         w += w12_algorithmic_bytes(p.n_out, p.k_in, int(p.desc.n_esc))
@@ -270,6 +272,47 @@ def rocprof_summary(out_dir: str, top: int = 24) -> None:
             print(f"{len(vals):7d} {sum(vals) / len(vals):14.1f} {min(vals):14.1f} {max(vals):14.1f}  {cn}  {kn[:100]}")
 
 
+def bench_ar(args, cfg, dm) -> int:
+    """Greedy autoregressive decoding with the same pass on a one-node tree:
+    each step feeds the previous bonus token back as the root (the step's one
+    readback), at a fixed committed length, and emits one token."""
+    import torch
+
+    import tree_verification_pass_amd as tvp
+
+    dev = torch.device("cuda:0")
+    out = tvp._alloc_out(dm.plan, 1, 1, False)
+    parents = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    tok = torch.full((1,), 11, dtype=torch.int32, device=dev)
+
+    def step():
+        tvp.verify_step(dm.plan, cfg.ctx_len, tok, parents, commit=True, out=out)
+        tok.fill_(int(out.bonus.item()))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} greedy decode steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    gbs = step_bytes(dm, cfg, 0.0, n=1) / (ms * 1e-3) / 1e9
+    log(f"bench: {ms:.3f} ms/token, {1000.0 / ms:.1f} tokens/s, {gbs:.0f} GB/s")
+    line = {
+        "metric": "W12 greedy AR decode tokens/s (27B-like, one node per pass), 1 GPU",
+        "value": round(1000.0 / ms, 3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "achieved_hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "config": {"workload": f"{cfg.name}-like greedy decode, ctx {cfg.ctx_len}", "n_layers": cfg.n_layers,
+                   "hidden": cfg.hidden, "nodes": 1, "ctx_len": cfg.ctx_len},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +323,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--gemm-iters", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ar", action="store_true",
+                    help="time W12 greedy autoregressive decoding instead (one node per pass, M = 1)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run three plain device copies of MIB MiB (calibrates HBM byte counters)")
     ap.add_argument("--rocprof-summary", metavar="DIR", default="",
@@ -317,6 +362,8 @@ def main() -> int:
     cfg = CONFIGS[args.config]
     s_max = cfg.ctx_len + 64
     dm = build_model(cfg, args.seed, s_max, cfg.n_nodes)
+    if args.ar:
+        return bench_ar(args, cfg, dm)
     log("bench: drafting trees from the target's top-4")
     trees = make_trees(dm, cfg, args.trees, args.seed + 1)
     out = tvp._alloc_out(dm.plan, cfg.n_nodes, 1, False)

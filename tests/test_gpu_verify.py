@@ -130,6 +130,30 @@ def test_speculative_loop_reproduces_greedy_stream(cuda):
     assert stream[:want] == ref_stream[:want]
 
 
+def test_ar_decoding_loop_reproduces_greedy_stream(cuda):
+    """W12 autoregressive decoding (one node per pass: M = 1, no speculation)
+    is the same pass on a one-node tree: its bonus tokens are the oracle's
+    greedy stream and its commits keep the cache equal to the oracle's."""
+    cfg = CONFIGS["tiny"]
+    L0 = cfg.ctx_len
+    dm, orc, cache = build_pair(cfg, 7, s_max=L0 + 64)
+    want = 24
+    ref_stream = om.ar_greedy(orc, cache, L0, 5, want)
+    ctx, root, stream = L0, 5, []
+    for _ in range(want):
+        tokens, parents = np.array([root], np.int32), np.array([-1], np.int32)
+        ref = om.verify(orc, cache, ctx, tokens, parents)
+        res = _run(dm, ctx, tokens, parents, commit=True)
+        chk = check_logits(res.logits.cpu().numpy().astype(np.float64), ref["logits"])
+        if not chk["decidable"][0]:
+            pytest.skip("a near-tie in the greedy stream: it may legitimately diverge")
+        assert int(res.n_accepted.item()) == 0
+        root = int(res.bonus.item())
+        stream.append(root)
+        ctx = om.commit(cache, ctx, ref["path"], ref["kv_new"])
+    assert stream == ref_stream
+
+
 def test_batched_equals_per_request(cuda):
     cfg = CONFIGS["ragged"]
     import tree_verification_pass_amd as tvp
