@@ -799,15 +799,7 @@ constexpr int kWideTargetGroups = 1024;
 #ifndef TVP_TPW2_MIN_TILES
 #define TVP_TPW2_MIN_TILES 1024  // tiles from which a workgroup takes two tiles
 #endif
-#ifndef TVP_KW_FEW
-#define TVP_KW_FEW 4  // waves per workgroup when workgroups are few
-#endif
-#ifndef TVP_KW_MANY
-#define TVP_KW_MANY 4  // ... and when they are many
-#endif
-#ifndef TVP_KW_SWITCH
-#define TVP_KW_SWITCH 512  // workgroup count that separates few from many
-#endif
+constexpr int kWavesPerCU = 12;  // skinny kernel: three wavefronts per SIMD (136-156 VGPRs)
 #ifndef TVP_RD1
 #define TVP_RD1 3  // register-ring depth, one tile per workgroup
 #endif
@@ -859,8 +851,12 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
     }
     const int nwg = partial ? p.groups * p.splits : p.groups;
     const int krange = partial ? p.kps : nkb;
-    p.KW = nwg >= TVP_KW_SWITCH ? TVP_KW_MANY : TVP_KW_FEW;
-    if (krange > 4 * 63) p.KW = 8;
+    // Waves per workgroup: 4, or 2 when a CU would get more workgroups than it
+    // holds at once (kWavesPerCU at this kernel's register use), so that all
+    // of a CU's workgroups stream together instead of in two rounds; more
+    // when a wave would exceed 63 blocks.
+    p.KW = (int)ceil_div(nwg, kNumCUs) * 4 > kWavesPerCU ? 2 : 4;
+    while (p.KW < 8 && ceil_div(krange, p.KW) > 63) p.KW *= 2;
     p.KW = std::max(1, std::min(p.KW, std::max(krange, 1)));
     p.kbs = nkb > 0 ? (int)ceil_div(nkb, p.KW) : 0;
     p.kbs_split = p.kps > 0 ? (int)ceil_div(p.kps, p.KW) : 0;
