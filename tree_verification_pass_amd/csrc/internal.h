@@ -17,9 +17,14 @@ static_assert(kGemmMaxGroups * 4 <= kGemmZeroBytes, "zero region");
 // `y_packed`: the SwiGLU epilogue writes its output packed (m <= 32).
 // `ksplit` > 1 (skinny path, epilogue kEpiPartial only) also splits K over
 // workgroups.
+// rope_cs (QKV epilogue, optional): per GEMM row r and rotated dim i < d/2,
+// (cos, sin) of pos[r] * theta^(-2i/d) at rope_cs[2 * (r * d/2 + i)] -- the
+// values the epilogue would otherwise compute itself, formed once per pass.
 int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
              const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, void* scratch, size_t scratch_bytes,
-             hipStream_t stream, int ksplit = 1);
+             hipStream_t stream, int ksplit = 1, const float* rope_cs = nullptr);
+// (cos, sin) table of the QKV epilogue for rows 0..n-1 at positions pos[].
+int launch_rope_table(const int32_t* pos, int n, int d, double theta, float* rope_cs, hipStream_t stream);
 
 // Internal epilogue (not part of the ABI): each K slice's fp32 partial result
 // goes to y = P[slice][m][ldy] (canonical columns); the consumer sums the

@@ -275,7 +275,7 @@ struct tvp_plan {
   // workspace layout
   size_t off_gcnt, zero_end;
   size_t off_h, off_a, off_q, off_o, off_u;
-  size_t off_anc, off_pos, off_slot, off_tstat, off_bad;
+  size_t off_anc, off_pos, off_slot, off_tstat, off_bad, off_rope;
   size_t off_gscr, gscr_bytes;
   size_t off_part;  // K-slice partial sums of the O and down projections (packed path)
   int ks_o, ks_down;  // their K slices at 32 rows
@@ -382,6 +382,8 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   off = align_up(off + (size_t)kMaxReq * 4, 256);
   p->off_bad = off;
   off = align_up(off + (size_t)mn * 4, 256);
+  p->off_rope = off;  // (cos, sin) per node and rotated dim, shared by every layer's QKV epilogue
+  off = align_up(off + (size_t)mn * (hd / 2) * 8, 256);
   // O and down projections in the packed path: K split over workgroups, the
   // slices' partial sums reduced by the fused residual + RMSNorm kernel
   p->ks_o = 1;
@@ -444,6 +446,8 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   int st;
 
   if ((st = launch_tree_prep(parents, ri, s_req, anc, pos, slot, tstat, stream))) return st;
+  float* rope = (float*)(w + p->off_rope);
+  if ((st = launch_rope_table(pos, n_total, hd, d.rope_theta, rope, stream))) return st;
   embed_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(tokens, d.embed, H, d.vocab, h, p->ld_h, bad);
   TVP_LAUNCH_CHECK();
   float* part = (float*)(w + p->off_part);
@@ -466,7 +470,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     e.s_stride = d.s_max;
     e.rope_theta = d.rope_theta;
     if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wqkv, &e, 0, gcnt, gscr, p->gscr_bytes,
-                       stream)))
+                       stream, 1, rope)))
       return st;
     if ((st = launch_tree_attention(q, L.k_cache, L.v_cache, d.s_max, ri, s_req, anc, hq, hkv, hd, G * max_n,
                                     max_keys, o, pk, ascr, p->ascr_bytes, stream)))

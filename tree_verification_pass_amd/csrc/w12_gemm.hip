@@ -70,6 +70,7 @@ struct GemmArgs {
   int full_groups, rem_splits, rem_kps, rem_kbs, rem_tpw;
   float* rpart;
   int ldrp;
+  const float* rope_cs;  // QKV: optional per-pass (cos, sin) table, see gemm_run
 };
 
 constexpr int kArgmaxMaxRows = 192;
@@ -129,6 +130,22 @@ __device__ inline unsigned long long argmax_key(float v, int32_t id) {
 
 // Epilogue over packed channels [c0, c0+nc) x rows [0, M) by `nthr` threads
 // (thread index `tid`), reading fp32 results through V(row, col).
+// RoPE angle of rotated dim i (< d/2) at position pos, formed in fp64.
+__device__ inline double rope_angle(int pos, double theta, int i, int d) {
+  return (double)pos * pow(theta, -2.0 * (double)i / (double)d);
+}
+
+// One thread per (row, rotated dim): the (cos, sin) table of a pass.
+__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restrict__ pos, int n, int d,
+                                                         double theta, float2* __restrict__ cs) {
+  const int half = d / 2;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n * half) return;
+  const int r = idx / half, i = idx % half;
+  const double ang = rope_angle(pos[r], theta, i, d);
+  cs[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
 template <int MODE, typename Get>
 __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int tid, int nthr, int key_slot,
                                 Get V, int slice = 0) {
@@ -178,8 +195,16 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
         const int head = t / tph, u = t % tph;
         const int da = 16 * u + c, db = d / 2 + 16 * u + c;
         const float xa = V(row, col), xb = V(row, col + 16);
-        const double ang = (double)a.pos[row] * pow(a.theta, -2.0 * (double)da / (double)d);
-        const float cs = (float)cos(ang), sn = (float)sin(ang);
+        float cs, sn;
+        if (a.rope_cs) {
+          const float2 t = ((const float2*)a.rope_cs)[(int64_t)row * (d / 2) + da];
+          cs = t.x;
+          sn = t.y;
+        } else {
+          const double ang = rope_angle(a.pos[row], a.theta, da, d);
+          cs = (float)cos(ang);
+          sn = (float)sin(ang);
+        }
         const float oa = xa * cs - xb * sn, ob = xb * cs + xa * sn;
         if (head < a.hq) {
           uint16_t* q = (uint16_t*)a.y + (int64_t)row * a.ldy + (int64_t)head * d;
@@ -976,6 +1001,15 @@ static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   return TVP_OK;
 }
 
+int launch_rope_table(const int32_t* pos, int n, int d, double theta, float* rope_cs, hipStream_t stream) {
+  if (n <= 0) return TVP_OK;
+  const int total = n * (d / 2);
+  rope_table_kernel<<<dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, stream>>>(pos, n, d, theta,
+                                                                                    (float2*)rope_cs);
+  TVP_LAUNCH_CHECK();
+  return TVP_OK;
+}
+
 bool gemm_is_skinny(int64_t m, const tvp_w12_packed* w) { return make_plan(m, w).skinny; }
 
 int gemm_ksplits(int64_t m, const tvp_w12_packed* w, int ksplit) {
@@ -991,7 +1025,7 @@ void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* 
 
 int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
              const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, void* scratch, size_t scratch_bytes,
-             hipStream_t stream, int ksplit) {
+             hipStream_t stream, int ksplit, const float* rope_cs) {
   if (!w || !epi || !w->blob || !cnt) return TVP_ERR_ARG;
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
   if (ksplit > 1 && epi->mode != kEpiPartial) return TVP_ERR_ARG;
@@ -1040,6 +1074,7 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
   a.rem_tpw = p.TPW;
   a.rpart = (float*)((uint8_t*)scratch + p.rem_off);
   a.ldrp = p.rem_groups * p.TPW * 32;
+  a.rope_cs = epi->mode == TVP_EPI_QKV ? rope_cs : nullptr;
   a.ntasks = p.ntasks;
   a.cnt = cnt;
   a.keys = (unsigned long long*)((uint8_t*)scratch + p.keys_off);
