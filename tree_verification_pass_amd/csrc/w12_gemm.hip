@@ -128,8 +128,6 @@ __device__ inline unsigned long long argmax_key(float v, int32_t id) {
   return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)id);
 }
 
-// Epilogue over packed channels [c0, c0+nc) x rows [0, M) by `nthr` threads
-// (thread index `tid`), reading fp32 results through V(row, col).
 // RoPE angle of rotated dim i (< d/2) at position pos, formed in fp64.
 __device__ inline double rope_angle(int pos, double theta, int i, int d) {
   return (double)pos * pow(theta, -2.0 * (double)i / (double)d);
@@ -146,6 +144,8 @@ __global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restri
   cs[idx] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
+// Epilogue over packed channels [c0, c0+nc) x rows [0, M) by `nthr` threads
+// (thread index `tid`), reading fp32 results through V(row, col).
 template <int MODE, typename Get>
 __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int tid, int nthr, int key_slot,
                                 Get V, int slice = 0) {
