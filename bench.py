@@ -241,6 +241,76 @@ def cpu_baseline(dm, cfg, seed: int, tree):
                        f"weights ({cfg.streamed_params() / w_layer:.2f}x) to a whole step of {est:.1f} s")}
 
 
+# once-per-pass kernels, by the name they carry in a trace
+SMALL_ROLES = (("argmax_finalize_kernel", "LM-head argmax finalize"), ("tree_prep_kernel", "tree preparation"),
+               ("rope_table_kernel", "RoPE table"), ("embed_kernel", "embedding"),
+               ("accept_kernel", "acceptance walk"), ("kv_commit_kernel", "KV commit"))
+
+
+def pass_roles(trace_csv: str) -> dict:
+    """Durations (us) of the pass's launches by role, from a rocprofv3 kernel
+    trace: the library's dispatches in start order, each named by its kernel
+    and, where one kernel serves two roles, by the launch before it (the O
+    projection follows the attention merge, the down projection the gate/up
+    fix-up; each residual + RMSNorm is named for the projection it follows).
+    Gate/up launches outside the pass (bench.py's own timing leg) follow
+    another gate/up launch and are left out."""
+    import csv
+    import re
+
+    rows = []
+    for r in csv.DictReader(open(trace_csv)):
+        if "tvp::" in r["Kernel_Name"]:
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+
+    def kind(name):
+        m = re.search(r"w12_skinny_kernel<\d+, \d+, \d+, (\d+)>", name)
+        if m:
+            return {"3": "gateup", "4": "qkv", "5": "lmhead", "16": "partial"}.get(m.group(1), "gemm")
+        for key, lab in (("rem_fixup", "fixup"), ("tree_attn_merge", "merge"), ("tree_attn_kernel", "attn"),
+                         ("resid_norm", "norm")):
+            if key in name:
+                return lab
+        for key, lab in SMALL_ROLES:
+            if key in name:
+                return lab
+        return "other"
+
+    kinds = [kind(r[2]) for r in rows]
+    out = {}
+    role_of = []
+    for i, k in enumerate(kinds):
+        prev = role_of[i - 1] if i else None
+        role = None
+        if k == "qkv":
+            role = "QKV GEMM + RoPE + KV write"
+        elif k == "attn":
+            role = "tree attention"
+        elif k == "merge":
+            role = "attention merge"
+        elif k == "partial":
+            role = {"attention merge": "O GEMM (K slices)", "gate/up fix-up": "down GEMM (K slices)"}.get(prev)
+        elif k == "norm":
+            role = {"O GEMM (K slices)": "residual + norm after O",
+                    "down GEMM (K slices)": "residual + norm after down"}.get(prev, "norm (first or final)")
+        elif k == "gateup":
+            role = "gate/up GEMM" if prev == "residual + norm after O" else None
+        elif k == "fixup":
+            role = "gate/up fix-up" if prev == "gate/up GEMM" else None
+        elif k == "lmhead":
+            role = "LM head + argmax"
+        elif k != "other":
+            role = k
+        role_of.append(role)
+        if role:
+            out.setdefault(role, []).append((rows[i][1] - rows[i][0]) / 1e3)
+    order = ["QKV GEMM + RoPE + KV write", "tree attention", "attention merge", "O GEMM (K slices)",
+             "residual + norm after O", "gate/up GEMM", "gate/up fix-up", "down GEMM (K slices)",
+             "residual + norm after down", "norm (first or final)", "LM head + argmax"] + [r for _, r in SMALL_ROLES]
+    return {r: out[r] for r in order if r in out}
+
+
 def rocprof_summary(out_dir: str, top: int = 24) -> None:
     """Prints the short text summary of a rocprofv3 csv output folder: the
     per-kernel duration table of ``--kernel-trace --stats`` runs and, for
@@ -257,6 +327,14 @@ def rocprof_summary(out_dir: str, top: int = 24) -> None:
             print(f"{int(r['Calls']):7d} {float(r['TotalDurationNs']) / 1e3:12.1f} {float(r['AverageNs']) / 1e3:9.2f} "
                   f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}  "
                   f"{r['Name'][:110]}")
+    for path in sorted(glob.glob(os.path.join(out_dir, "**", "*_kernel_trace.csv"), recursive=True)):
+        roles = pass_roles(path)
+        if roles:
+            print(f"per-role durations inside the pass ({os.path.basename(path)}): role, dispatches, mean us, "
+                  f"median us")
+            for role, vals in roles.items():
+                vals.sort()
+                print(f"  {role:28s} {len(vals):7d} {sum(vals) / len(vals):9.2f} {vals[len(vals) // 2]:9.2f}")
     for path in sorted(glob.glob(os.path.join(out_dir, "**", "*_counter_collection.csv"), recursive=True)):
         per = defaultdict(float)
         names = {}
@@ -285,27 +363,34 @@ def bench_ar(args, cfg, dm) -> int:
     parents = torch.full((1,), -1, dtype=torch.int32, device=dev)
     tok = torch.full((1,), 11, dtype=torch.int32, device=dev)
 
+    enq = []  # host time to enqueue a step's launches
+
     def step():
+        ta = time.perf_counter()
         tvp.verify_step(dm.plan, cfg.ctx_len, tok, parents, commit=True, out=out)
+        enq.append(time.perf_counter() - ta)
         tok.fill_(int(out.bonus.item()))
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} greedy decode steps")
+    enq.clear()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1000.0 / args.steps
     gbs = step_bytes(dm, cfg, 0.0, n=1) / (ms * 1e-3) / 1e9
-    log(f"bench: {ms:.3f} ms/token, {1000.0 / ms:.1f} tokens/s, {gbs:.0f} GB/s")
+    enq_ms = float(np.mean(enq)) * 1000.0
+    log(f"bench: {ms:.3f} ms/token, {1000.0 / ms:.1f} tokens/s, {gbs:.0f} GB/s, host enqueue {enq_ms:.2f} ms/step")
     line = {
         "metric": "W12 greedy AR decode tokens/s (27B-like, one node per pass), 1 GPU",
         "value": round(1000.0 / ms, 3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "achieved_hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "host_enqueue_ms_per_step": round(enq_ms, 4),
         "config": {"workload": f"{cfg.name}-like greedy decode, ctx {cfg.ctx_len}", "n_layers": cfg.n_layers,
                    "hidden": cfg.hidden, "nodes": 1, "ctx_len": cfg.ctx_len},
     }
@@ -368,9 +453,13 @@ def main() -> int:
     trees = make_trees(dm, cfg, args.trees, args.seed + 1)
     out = tvp._alloc_out(dm.plan, cfg.n_nodes, 1, False)
 
+    enq = []  # host time to enqueue a step's launches (the call returns before the GPU is done)
+
     def step(i):
         tokens, parents = trees[i % len(trees)]
+        ta = time.perf_counter()
         tvp.verify_step(dm.plan, cfg.ctx_len, tokens, parents, commit=True, out=out)
+        enq.append(time.perf_counter() - ta)
         return int(out.n_accepted.item())  # the step's one device-to-host readback
 
     for i in range(args.warmup):
@@ -378,6 +467,7 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps")
     acc = []
+    enq.clear()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
@@ -388,11 +478,13 @@ def main() -> int:
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1000.0 / args.steps
     dev_ms = ev0.elapsed_time(ev1) / args.steps
+    enq_ms = float(np.mean(enq)) * 1000.0
     mean_acc = float(np.mean(acc))
     steps_s = 1000.0 / ms
     nbytes = step_bytes(dm, cfg, mean_acc)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    log(f"bench: {ms:.3f} ms/step, {steps_s:.1f} steps/s, {gbs:.0f} GB/s, mean accepted {mean_acc:.2f}")
+    log(f"bench: {ms:.3f} ms/step, {steps_s:.1f} steps/s, {gbs:.0f} GB/s, mean accepted {mean_acc:.2f}, "
+        f"host enqueue {enq_ms:.2f} ms/step")
 
     g_ms, g_bytes, _ = time_gateup(dm, cfg, args.gemm_iters)
     g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
@@ -414,6 +506,7 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "device_ms_per_step": round(dev_ms, 4),
+        "host_enqueue_ms_per_step": round(enq_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
