@@ -283,7 +283,9 @@ typedef struct tvp_verify_out {
  * length is ctx_len + n_accepted + 1 and the bonus token is the next root.
  *   tokens, parents  device int32 [n]; tokens[0] is the root token (the last
  *                    committed-but-unprocessed token, e.g. the previous bonus)
- * Requires ctx_len + n <= s_max and n <= max_nodes; depth <= 63.            */
+ * Requires ctx_len + n <= s_max and n <= min(max_nodes, 64)
+ * (TVP_ERR_CAPACITY otherwise), (n_heads / n_kv_heads) * n <= 256 (the
+ * attention's rows per kv head; TVP_ERR_SHAPE otherwise); depth <= 63.     */
 int verify_step(tvp_plan* plan, int32_t ctx_len, const int32_t* tokens, const int32_t* parents,
                 int32_t n, int32_t commit, const tvp_verify_out* out, void* ws, size_t ws_bytes,
                 hipStream_t stream);
@@ -296,7 +298,9 @@ int verify_step(tvp_plan* plan, int32_t ctx_len, const int32_t* tokens, const in
  * runs once over all Σ n_r rows; attention, acceptance and commit run per
  * request.  Outputs are per request: path [node_ptr[r] ..] (request-local
  * node indices), n_accepted/bonus/status [r]; argmax/logits per global node.
- *   ctx_len, node_ptr  host int32 arrays ([n_req], [n_req+1])              */
+ *   ctx_len, node_ptr  host int32 arrays ([n_req], [n_req+1])
+ * Per request the limits of verify_step hold, with ctx_len[r] + n_r <= s_req;
+ * n_req * s_req <= s_max and Σ n_r <= max_nodes.                           */
 int verify_step_batched(tvp_plan* plan, int32_t n_req, const int32_t* ctx_len,
                         const int32_t* node_ptr, int32_t s_req, const int32_t* tokens,
                         const int32_t* parents, int32_t commit, const tvp_verify_out* out,

@@ -301,7 +301,7 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   if (max_nodes < 1 || max_nodes > 192) return TVP_ERR_CAPACITY;
   const int hq = d->n_heads, hkv = d->n_kv_heads, hd = d->head_dim, H = d->hidden, F = d->ffn;
   const int G = hq / hkv;
-  if (G * std::min(max_nodes, 64) > 256) return TVP_ERR_SHAPE;
+  if (G > 256) return TVP_ERR_SHAPE;  // a one-node request must fit the attention's 256 rows
   if ((uintptr_t)d->final_norm % 16) return TVP_ERR_ARG;
   int st = check_packed(d->lm_head, d->vocab, H, TVP_CHAN_PLAIN);
   if (st) return st;
@@ -400,7 +400,11 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   p->gscr_bytes = gscr;
   off = align_up(off + gscr, 256);
   p->off_ascr = off;
-  p->ascr_bytes = attention_scratch_bytes(hkv, G, hd, G * std::min(mn, 64), mn, d->s_max);
+  // the attention's split count depends on the largest request's rows, so
+  // the scratch covers every per-request node count a pass may bring
+  p->ascr_bytes = 0;
+  for (int nr = 1; nr <= std::min(mn, 64) && G * nr <= 256; ++nr)
+    p->ascr_bytes = std::max(p->ascr_bytes, attention_scratch_bytes(hkv, G, hd, G * nr, mn, d->s_max));
   off = align_up(off + p->ascr_bytes, 256);
   p->bytes = off;
   *out = p;
@@ -563,6 +567,7 @@ int verify_step(tvp_plan* p, int32_t ctx_len, const int32_t* tokens, const int32
   if (n < 1 || ctx_len < 0) return TVP_ERR_SHAPE;
   if (n > p->max_nodes || n > 64) return TVP_ERR_CAPACITY;
   if ((int64_t)ctx_len + n > p->desc.s_max) return TVP_ERR_CAPACITY;
+  if ((p->desc.n_heads / p->desc.n_kv_heads) * n > 256) return TVP_ERR_SHAPE;  // attention rows per kv head
   if (!ws || ws_bytes < p->bytes) return TVP_ERR_WORKSPACE;
   ReqInfo ri{};
   ri.n_req = 1;
@@ -586,6 +591,7 @@ int verify_step_batched(tvp_plan* p, int32_t n_req, const int32_t* ctx_len, cons
     const int n = node_ptr[r + 1] - node_ptr[r];
     if (n < 1 || ctx_len[r] < 0) return TVP_ERR_SHAPE;
     if (n > 64 || (int64_t)ctx_len[r] + n > s_req) return TVP_ERR_CAPACITY;
+    if ((p->desc.n_heads / p->desc.n_kv_heads) * n > 256) return TVP_ERR_SHAPE;
     ri.ctx_len[r] = ctx_len[r];
     ri.node_ptr[r] = node_ptr[r];
   }
