@@ -80,22 +80,22 @@ def w12_algorithmic_bytes(n_out: int, k_in: int, n_esc: int) -> int:
     return n_out * k_in + n_out * ((k_in + 1) // 2) + n_out + 4 * (n_out + 1) + 4 * n_esc
 
 
-def build_model(cfg, seed: int, s_max: int, max_nodes: int):
+def build_model(cfg, seed: int, s_max: int, max_nodes: int, kv_fn=None):
     import torch
 
     from synth.configs import gen_embed, gen_final_norm, gen_kv_context, gen_layer, gen_lm_head
     from tree_verification_pass_amd.model import DeviceModel, Dims
 
     dev = torch.device("cuda:0")
-    esc = {}
 
     def layer_fn(layer):
         if layer % 8 == 0:
             log(f"bench: converting layer {layer}/{cfg.n_layers} to W12")
         return gen_layer(cfg, seed, layer, device=dev, gains="ones")
 
-    def kv_fn(layer):
-        return gen_kv_context(cfg, seed, layer, cfg.ctx_len, s_max, device=dev)
+    if kv_fn is None:
+        def kv_fn(layer):
+            return gen_kv_context(cfg, seed, layer, cfg.ctx_len, s_max, device=dev)
 
     t0 = time.perf_counter()
     dm = DeviceModel(Dims.of(cfg), gen_embed(cfg, seed, dev), gen_final_norm(cfg, seed, dev),
@@ -398,6 +398,103 @@ def bench_ar(args, cfg, dm) -> int:
     return 0
 
 
+def bench_batched(args, cfg) -> int:
+    """Batched verification: 24 requests share a 192-node budget (per-request
+    trees of 4-16 nodes, best-first topology, drafts from the target's own
+    top-4 at p = 0.7), each over its own committed context (uniform in
+    [512, 8192]) in its own KV region; one ``verify_step_batched`` per step
+    (every GEMM over all 192 rows, attention, acceptance and commit per
+    request) plus the readback of the accepted lengths."""
+    import torch
+
+    import tree_verification_pass_amd as tvp
+    from synth import best_first_topology
+    from synth.configs import gen_kv_context
+    from synth.trees import assign_tokens_by_depth, batch_sizes
+
+    dev = torch.device("cuda:0")
+    n_req, total, cap, ctx_lo, ctx_hi = 24, 192, 16, 512, 8192
+    rng = np.random.default_rng(args.seed + 2)
+    sizes = batch_sizes(rng, n_req=n_req, total=total, start=4, cap=cap)
+    ctxs = rng.integers(ctx_lo, ctx_hi + 1, n_req)
+    s_req = ctx_hi + cap
+    s_max = n_req * s_req
+    hkv, d = cfg.n_kv_heads, cfg.head_dim
+
+    def kv_fn(layer):  # request r's committed context in slots [r * s_req, r * s_req + ctx_r)
+        kc = torch.zeros(hkv, s_max, d, dtype=torch.bfloat16, device=dev)
+        vc = torch.zeros_like(kc)
+        for r in range(n_req):
+            k_r, v_r = gen_kv_context(cfg, args.seed * 1000 + r, layer, int(ctxs[r]), int(ctxs[r]), device=dev)
+            kc[:, r * s_req: r * s_req + ctxs[r]] = k_r
+            vc[:, r * s_req: r * s_req + ctxs[r]] = v_r
+        return kc, vc
+
+    dm = build_model(cfg, args.seed, s_max, total, kv_fn=kv_fn)
+    node_ptr = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    log("bench: drafting the batch's trees from the target's top-4")
+    batches = []
+    for _ in range(2):
+        trees = [best_first_topology(rng, int(sizes[r])) for r in range(n_req)]
+        toks = np.zeros(total, np.int32)
+        par = np.concatenate([t[0] for t in trees]).astype(np.int32)
+        P = torch.as_tensor(par, device=dev)
+        for r in range(n_req):
+            sl = slice(node_ptr[r], node_ptr[r + 1])
+
+            def topk_fn(tokens, parents, sl=sl):  # the other requests do not affect request r
+                toks[sl] = tokens
+                res = tvp.verify_step_batched(dm.plan, ctxs.tolist(), node_ptr.tolist(), s_req,
+                                              torch.as_tensor(toks, device=dev), P, commit=False,
+                                              want_logits=True)
+                return torch.topk(res.logits[sl], 4, dim=1).indices.cpu().numpy()
+
+            toks[sl] = assign_tokens_by_depth(rng, trees[r][0], trees[r][1], int(rng.integers(cfg.vocab)),
+                                              cfg.vocab, topk_fn, p_top=0.7)
+        batches.append((torch.as_tensor(toks.copy(), device=dev), P))
+    out = tvp._alloc_out(dm.plan, total, n_req, False)
+
+    def step(i):
+        T, P = batches[i % len(batches)]
+        tvp.verify_step_batched(dm.plan, ctxs.tolist(), node_ptr.tolist(), s_req, T, P, commit=True, out=out)
+        return out.n_accepted.cpu().numpy()  # the step's one device-to-host readback
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} batched steps")
+    acc = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        acc.append(step(i))
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    acc = np.asarray(acc, dtype=np.float64)
+    emitted = float(np.mean(acc.sum(axis=1) + n_req))  # accepted + one bonus per request
+    w = sum(w12_algorithmic_bytes(p.n_out, p.k_in, int(p.desc.n_esc))
+            for p in [dm.lm_head] + [x for Lr in dm.layers for x in (Lr.wqkv, Lr.wo, Lr.wgu, Lr.wdown)])
+    kv_read = sum(2 * (int(ctxs[r]) + int(sizes[r])) * hkv * d * 2 for r in range(n_req))
+    kv_write = 2 * total * hkv * d * 2
+    commit = 2 * 2 * float(np.mean(acc.sum(axis=1))) * hkv * d * 2
+    nbytes = w + cfg.n_layers * (kv_read + kv_write + commit) + total * cfg.hidden * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"bench: {ms:.3f} ms/step, {1000.0 / ms:.2f} steps/s, {emitted * 1000.0 / ms:.0f} tokens/s, {gbs:.0f} GB/s")
+    line = {
+        "metric": "W12 batched tree-verify steps/s (27B-like, 24 requests sharing a 192-node budget), 1 GPU",
+        "value": round(1000.0 / ms, 3), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "tokens_per_s": round(emitted * 1000.0 / ms, 2), "mean_emitted_per_step": round(emitted, 2),
+        "achieved_hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": int(nbytes),
+        "config": {"workload": (f"{cfg.name}-like batched verify step, {n_req} requests, {total} nodes "
+                                f"(trees of {int(sizes.min())}-{int(sizes.max())}), ctx {int(ctxs.min())}-"
+                                f"{int(ctxs.max())} (mean {float(ctxs.mean()):.0f})"),
+                   "n_layers": cfg.n_layers, "hidden": cfg.hidden, "nodes": total, "requests": n_req},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,6 +507,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ar", action="store_true",
                     help="time W12 greedy autoregressive decoding instead (one node per pass, M = 1)")
+    ap.add_argument("--batched", action="store_true",
+                    help="time the batched pass instead (24 requests sharing a 192-node budget)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run three plain device copies of MIB MiB (calibrates HBM byte counters)")
     ap.add_argument("--rocprof-summary", metavar="DIR", default="",
@@ -445,6 +544,8 @@ def main() -> int:
     from synth.configs import CONFIGS
 
     cfg = CONFIGS[args.config]
+    if args.batched:
+        return bench_batched(args, cfg)
     s_max = cfg.ctx_len + 64
     dm = build_model(cfg, args.seed, s_max, cfg.n_nodes)
     if args.ar:

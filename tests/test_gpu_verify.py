@@ -158,9 +158,10 @@ def test_batched_equals_per_request(cuda):
     cfg = CONFIGS["ragged"]
     import tree_verification_pass_amd as tvp
     rng = np.random.default_rng(7)
-    n_req, s_req = 3, 400
-    sizes = [5, 9, 13]
-    ctxs = [250, 310, 123]
+    # 47 rows in all: the GEMMs take the wide (row-major, more than 32 rows) path
+    n_req, s_req = 4, 400
+    sizes = [5, 9, 13, 20]
+    ctxs = [250, 310, 123, 77]
     dm, orc, cache = build_pair(cfg, 2, s_max=n_req * s_req, max_nodes=64)
     # request r owns slots [r*s_req, (r+1)*s_req): give each its own context
     for layer_i, layer in enumerate(dm.layers):

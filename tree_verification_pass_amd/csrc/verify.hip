@@ -490,15 +490,13 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
         return st;
       launch_norm(part, gemm_ksplits(n_total, &L.wo, TVP_KSPLIT_MAX), pstride, H, h, p->ld_h, L.ffn_norm, H,
                   d.norm_eps, a, p->ld_h, 1, n_total, stream);
-    } else {
-      e.mode = TVP_EPI_RESID;
-      e.y = h;
-      e.ldy = p->ld_h;
-      e.resid = h;
-      e.ldr = p->ld_h;
+    } else {  // wide kernel: its split sums stay in the GEMM scratch and the norm adds them in split order
+      e.mode = kEpiPartial;
       if ((st = gemm_run(o, nullptr, n_total, p->ld_q, &L.wo, &e, 0, gcnt, gscr, p->gscr_bytes, stream)))
         return st;
-      launch_norm(part, 0, pstride, H, h, p->ld_h, L.ffn_norm, H, d.norm_eps, a, p->ld_h, 0, n_total, stream);
+      const int ldp = L.wo.n_tiles * 32;
+      launch_norm((const float*)gscr, gemm_ksplits(n_total, &L.wo, 1), (int64_t)n_total * ldp, ldp, h, p->ld_h,
+                  L.ffn_norm, H, d.norm_eps, a, p->ld_h, 0, n_total, stream);
     }
     TVP_LAUNCH_CHECK();
     e = tvp_gemm_epilogue{};
@@ -520,15 +518,12 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
       launch_norm(part, gemm_ksplits(n_total, &L.wdown, TVP_KSPLIT_MAX), pstride, H, h, p->ld_h, next_norm, H,
                   d.norm_eps, a, p->ld_h, 1, n_total, stream);
     } else {
-      e.mode = TVP_EPI_RESID;
-      e.y = h;
-      e.ldy = p->ld_h;
-      e.resid = h;
-      e.ldr = p->ld_h;
-      if ((st = gemm_run(u, nullptr, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gscr, p->gscr_bytes,
-                         stream)))
+      e.mode = kEpiPartial;
+      if ((st = gemm_run(u, nullptr, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gscr, p->gscr_bytes, stream)))
         return st;
-      launch_norm(part, 0, pstride, H, h, p->ld_h, next_norm, H, d.norm_eps, a, p->ld_h, 0, n_total, stream);
+      const int ldp = L.wdown.n_tiles * 32;
+      launch_norm((const float*)gscr, gemm_ksplits(n_total, &L.wdown, 1), (int64_t)n_total * ldp, ldp, h,
+                  p->ld_h, next_norm, H, d.norm_eps, a, p->ld_h, 0, n_total, stream);
     }
     TVP_LAUNCH_CHECK();
   }

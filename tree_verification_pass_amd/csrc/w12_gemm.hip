@@ -71,6 +71,7 @@ struct GemmArgs {
   float* rpart;
   int ldrp;
   const float* rope_cs;  // QKV: optional per-pass (cos, sin) table, see gemm_run
+  int cache_rowmap;      // epilogue: stage the group's channel rows in LDS first (many rows per thread)
 };
 
 constexpr int kArgmaxMaxRows = 192;
@@ -149,6 +150,16 @@ __global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restri
 template <int MODE, typename Get>
 __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int tid, int nthr, int key_slot,
                                 Get V, int slice = 0) {
+  // When each thread walks many (row, column) pairs, the channels' canonical
+  // rows come from LDS (no dependent global load per element); the loops are
+  // unrolled so independent loads overlap.
+  __shared__ int32_t rm_s[128];
+  const bool cached = a.cache_rowmap && nc <= 128;  // uniform over the workgroup
+  if (cached) {
+    for (int i = tid; i < nc; i += nthr) rm_s[i] = a.rowmap[c0 + i];
+    __syncthreads();
+  }
+  auto rowmap_of = [&](int col) { return cached ? rm_s[col - c0] : a.rowmap[col]; };
   if constexpr (MODE == kEpiPartial) {
     float* P = (float*)a.y + (int64_t)slice * M * a.ldy;
     for (int idx = tid; idx < M * nc; idx += nthr) {
@@ -157,9 +168,10 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
       if (r >= 0) P[row * a.ldy + r] = V(row, col);
     }
   } else if constexpr (MODE == TVP_EPI_F32 || MODE == TVP_EPI_BF16 || MODE == TVP_EPI_RESID) {
+#pragma unroll 4
     for (int idx = tid; idx < M * nc; idx += nthr) {
       const int row = idx / nc, col = c0 + idx % nc;
-      const int32_t r = a.rowmap[col];
+      const int32_t r = rowmap_of(col);
       if (r < 0) continue;
       const float v = V(row, col);
       if constexpr (MODE == TVP_EPI_F32) {
@@ -173,10 +185,11 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
     }
   } else if constexpr (MODE == TVP_EPI_SWIGLU) {
     const int half = nc / 2;  // nc is a multiple of 32
+#pragma unroll 4
     for (int idx = tid; idx < M * half; idx += nthr) {
       const int row = idx / half, p = idx % half;
       const int col = c0 + (p / 16) * 32 + (p % 16);
-      const int32_t r = a.rowmap[col];
+      const int32_t r = rowmap_of(col);
       if (r < 0) continue;
       const float gv = V(row, col), uv = V(row, col + 16);
       const uint16_t o = (uint16_t)f32_to_bf16(silu_f32(gv) * uv);
@@ -186,6 +199,7 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
   } else if constexpr (MODE == TVP_EPI_QKV) {
     const int d = a.d, tph = d / 32;
     const int rot_tiles = (a.hq + a.hkv) * tph;
+#pragma unroll 4
     for (int idx = tid; idx < M * nc; idx += nthr) {
       const int row = idx / nc, col = c0 + idx % nc;
       const int t = col / 32, c = col % 32;
@@ -228,7 +242,7 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
       unsigned long long best = 0ull;
       for (int cc = tid; cc < nc; cc += nthr) {
         const int col = c0 + cc;
-        const int32_t r = a.rowmap[col];
+        const int32_t r = rowmap_of(col);
         if (r < 0) continue;
         const float v = V(row, col);
         if (a.logits) a.logits[row * a.ldl + r] = v;
@@ -569,242 +583,240 @@ __global__ __launch_bounds__(512) void w12_rem_fixup_kernel(GemmArgs a) {
   epilogue<MODE>(a, c0, nc, a.m, threadIdx.x, 512, 0, sum_slices, 0);
 }
 
-template <int ROWS>
-struct XChunk {
-  static constexpr int CB = ROWS <= 16 ? 8 : (ROWS <= 32 ? 4 : 2);  // blocks per X chunk
-};
+// ----------------------------------------------------------------------------
+// Wide kernel (33..192 rows): a workgroup owns 4 tiles (one per wavefront)
+// and a K range; all four wavefronts walk the same 64-column blocks, so one
+// copy of X per block serves them from LDS.  Per block: X for the block after
+// next is fetched into registers while this block is multiplied, and stored
+// to the other half of a double-buffered LDS tile behind one barrier; each
+// wavefront's records sit in a three-block register ring, are decoded into
+// its own LDS scratch, patched with the block's escapes, and multiplied
+// against RB row blocks of X (v_mfma_f32_32x32x16_bf16).  64 KB of LDS, so
+// two workgroups share a CU.  Rows are XOR-swizzled by their 16-byte column
+// group inside the X tile: the row-major fill and the column reads of the
+// MFMA A operand are both free of bank conflicts.
+template <int RB>
+__global__ __launch_bounds__(256, 2) void w12_wide_kernel(GemmArgs a) {
+  constexpr int ROWS = 32 * RB;
+  constexpr int RD = 3;  // register-ring depth (blocks in flight per wavefront)
+  __shared__ uint4 xs[2][8 * ROWS];  // X block [k group][row ^ k group]
+  __shared__ uint4 scr[4][256];      // per-wavefront decode scratch: one 32 x 64 tile block
 
-template <int MT, int RB, int TPW>
-__global__ __launch_bounds__(256) void w12_wide_kernel(GemmArgs a) {
-  constexpr int ROWS = MT * RB;
-  constexpr int CB = XChunk<ROWS>::CB;
-  constexpr int TG = 4 * TPW;
-  constexpr int KG = CB * 8;  // 16-byte k groups per X chunk
-  __shared__ uint4 xs[KG * ROWS];
-  __shared__ uint4 scr[4][2][256];
-  __shared__ uint32_t s_last;
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  // uniform per wavefront, so the escape offsets below are scalar loads and
+  // no vector load in the ring waits on another
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
   const int kb0 = sp * a.kbs;
   const int kb1 = min(a.n_kb, kb0 + a.kbs);
   const int nblk = kb1 > kb0 ? kb1 - kb0 : 0;
-  const int tw = g * TG + wave * TPW;
-  const int nsteps = TPW == 2 ? nblk : (nblk + 1) / 2;
+  const int tile = g * 4 + wave;
+  const int tt = min(tile, a.n_tiles - 1);  // a tile past the end runs clamped; its results are dropped
+  const uint32_t b2v = a.b2[tt * 32 + (lane & 31)];
 
-  constexpr int NACC = MT == 32 ? 16 : 4;
-  constexpr int NCH = MT == 32 ? 1 : 2;
-  typedef float accv __attribute__((ext_vector_type(NACC)));
-  accv acc[TPW][RB][NCH];
+  f32x16_t acc[RB];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[rb][v] = 0.0f;
+
+  // X block j (row-major x; rows >= m and columns >= k_in read as zero):
+  // thread piece i is row (tid + 256 i) / 8, 16-byte group (tid % 8)
+  uint4 xr[RB];
+  auto load_x = [&](int j) {
+    const int64_t k = (int64_t)j * kBlockK + 8 * (tid & 7);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < a.m) {
+        const uint16_t* src = a.x + (int64_t)row * a.ldx + k;
+        if (k + 8 <= a.k_in) {
+          v = *(const uint4*)src;
+        } else if (k < a.k_in) {
+          uint32_t hh[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hh[e] = (k + e < a.k_in) ? src[e] : 0u;
+          v = make_uint4(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16), hh[4] | (hh[5] << 16), hh[6] | (hh[7] << 16));
+        }
+      }
+      xr[i] = v;
+    }
+  };
+  auto store_x = [&](int buf) {
+    const int kg = tid & 7;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) xs[buf][kg * ROWS + (((tid >> 3) + 32 * i) ^ kg)] = xr[i];
+  };
+
+  // records and escape entries of block i into ring slot `slot` (past the
+  // end: the last block again, result unused)
+  uint4 R[RD][3];
+  uint32_t E[RD], EO[RD], EC[RD];
+  auto issue = [&](int i, int slot) {
+    const int j = kb0 + min(i, max(nblk - 1, 0));
+    const int64_t un = (int64_t)tt * a.n_kb + j;
+    const uint32_t eo = a.escoff[un];
+    const uint32_t ec = a.escoff[un + 1] - eo;
+    const uint4* blk = (const uint4*)(a.rec + rec_block(tt, j, a.n_tiles) * kBlockBytes);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) R[slot][q] = load_nt(blk + q * 64 + lane);
+    // lanes past the count read a neighbour (the blob continues past the
+    // escape list) and are never used
+    E[slot] = a.esc[(uint32_t)lane < ec ? eo + lane : eo];
+    EO[slot] = eo;
+    EC[slot] = ec;
+  };
+
+  auto process = [&](int slot, int buf) {
+    uint32_t o[16];
+    decode_block(R[slot], b2v, o);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+      scr[wave][64 * s4 + lane] = make_uint4(o[4 * s4], o[4 * s4 + 1], o[4 * s4 + 2], o[4 * s4 + 3]);
+    lds_order();
+    {
+      uint16_t* sh = (uint16_t*)&scr[wave][0];
+      const uint32_t ec = EC[slot];
+      if ((uint32_t)lane < ec) sh[E[slot] & 0x7FFu] = (uint16_t)(E[slot] >> 16);
+      for (uint32_t e = 64 + lane; e < ec; e += 64) {  // more escapes than lanes (rare)
+        const uint32_t ent = a.esc[EO[slot] + e];
+        sh[ent & 0x7FFu] = (uint16_t)(ent >> 16);
+      }
+    }
+    lds_order();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8_t B = as_bf16x8(scr[wave][64 * ks + lane]);
+      const int kg = 2 * ks + h;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const bf16x8_t A = as_bf16x8(xs[buf][kg * ROWS + ((rb * 32 + (lane & 31)) ^ kg)]);
+        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[rb], 0, 0, 0);
+      }
+    }
+    lds_order();
+  };
+
+  if (nblk > 0) {
+#pragma unroll
+    for (int p = 0; p < RD - 1; ++p) issue(p, p);
+    load_x(kb0);
+    store_x(0);
+    if (nblk > 1) load_x(kb0 + 1);
+    __syncthreads();
+    // The ring slot is a compile-time constant inside each unrolled group,
+    // and the loads run unconditionally (clamped to the last block past the
+    // end), so the wait counts stay exact.
+    for (int i0 = 0; i0 < nblk; i0 += RD) {
+#pragma unroll
+      for (int r = 0; r < RD; ++r) {
+        const int i = i0 + r;
+        issue(i + RD - 1, (r + RD - 1) % RD);
+        if (i < nblk) process(r, i & 1);
+        store_x((i + 1) & 1);  // block i + 1, fetched one block ago (its buffer was last read before
+                               // the previous barrier)
+        load_x(kb0 + min(i + 2, nblk - 1));
+        __syncthreads();
+      }
+    }
+  }
+
+  // this split's sums: part [split][row][packed channel]
+  if (tile < a.n_tiles) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-        for (int v = 0; v < NACC; ++v) acc[t][rb][ch][v] = 0.0f;
-
-  uint32_t b2v[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) b2v[t] = (tw + t < a.n_tiles) ? a.b2[(tw + t) * 32 + (lane & 31)] : 0u;
-
-  auto unit_tile = [&](int u) { return TPW == 2 ? tw + u : tw; };
-  auto unit_blk = [&](int st, int u) { return TPW == 2 ? kb0 + st : kb0 + 2 * st + u; };
-  auto unit_ok = [&](int st, int u) { return unit_tile(u) < a.n_tiles && unit_blk(st, u) < kb1; };
-
-  uint4 R[2][3], Rn[2][3];
-  uint32_t E[2], En[2];
-  uint32_t eo[2], ec[2], eon[2], ecn[2];
-
-  auto load_escoff = [&](int st, uint32_t (&o)[2], uint32_t (&c)[2]) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      o[u] = 0;
-      c[u] = 0;
-      if (st < nsteps && unit_ok(st, u)) {
-        const int64_t un = (int64_t)unit_tile(u) * a.n_kb + unit_blk(st, u);
-        o[u] = a.escoff[un];
-        c[u] = a.escoff[un + 1] - o[u];
+      for (int v = 0; v < 16; ++v) {
+        const int row = rb * 32 + (v >> 2) * 8 + 4 * h + (v & 3);
+        const int col = tile * 32 + (lane & 31);
+        if (row < a.m) a.part[((int64_t)sp * a.m + row) * a.n_pad + col] = acc[rb][v];
       }
-    }
-  };
-  auto load_recs = [&](int st, const uint32_t (&o)[2], const uint32_t (&c)[2], uint4 (&r)[2][3],
-                       uint32_t (&e)[2]) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      e[u] = 0;
-      if (st < nsteps && unit_ok(st, u)) {
-        const uint4* blk =
-            (const uint4*)(a.rec + rec_block(unit_tile(u), unit_blk(st, u), a.n_tiles) * kBlockBytes);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) r[u][i] = load_nt(blk + i * 64 + lane);
-        if ((uint32_t)lane < c[u]) e[u] = a.esc[o[u] + lane];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) r[u][i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  load_escoff(0, eo, ec);
-  load_recs(0, eo, ec, R, E);
-  load_escoff(1, eon, ecn);
-
-  for (int st = 0; st < nsteps; ++st) {
-    // prefetch the next step
-    load_recs(st + 1, eon, ecn, Rn, En);
-    uint32_t eonn[2], ecnn[2];
-    load_escoff(st + 2, eonn, ecnn);
-
-    const int blk_first = unit_blk(st, 0);
-    const int jj = (blk_first - kb0) % CB;  // block index inside the X chunk
-    if (jj == 0) {
-      __syncthreads();
-      const int64_t k0 = (int64_t)blk_first * kBlockK;
-      for (int idx = tid; idx < KG * ROWS; idx += 256) {
-        const int row = idx / KG, kg = idx % KG;
-        const int64_t k = k0 + 8 * kg;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < a.m) {
-          const uint16_t* src = a.x + (int64_t)row * a.ldx + k;
-          if (k + 8 <= a.k_in) {
-            v = *(const uint4*)src;
-          } else if (k < a.k_in) {
-            uint32_t h[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) h[i] = (k + i < a.k_in) ? src[i] : 0u;
-            v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-          }
-        }
-        xs[kg * ROWS + row] = v;
-      }
-      __syncthreads();
-    }
-
-    // decode into LDS, then patch escapes
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (unit_ok(st, u)) {
-        uint32_t o[16];
-        decode_block(R[u], b2v[TPW == 2 ? u : 0], o);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          scr[wave][u][64 * s + lane] = make_uint4(o[4 * s], o[4 * s + 1], o[4 * s + 2], o[4 * s + 3]);
-      }
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (unit_ok(st, u) && ec[u] > 0) {
-        uint16_t* sh = (uint16_t*)&scr[wave][u][0];
-        if ((uint32_t)lane < ec[u]) sh[E[u] & 0x7FFu] = (uint16_t)(E[u] >> 16);
-        for (uint32_t e = 64 + lane; e < ec[u]; e += 64) {
-          const uint32_t ent = a.esc[eo[u] + e];
-          sh[ent & 0x7FFu] = (uint16_t)(ent >> 16);
-        }
-      }
-    }
-    wave_lds_sync();
-
-    // MFMA over the step's units
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (unit_ok(st, u)) {
-        const int ti = TPW == 2 ? u : 0;
-        const int jb = TPW == 2 ? jj : jj + u;
-        if constexpr (MT == 32) {
-          const int h = lane >> 5;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8_t B = as_bf16x8(scr[wave][u][64 * ks + lane]);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-              const bf16x8_t A = as_bf16x8(xs[(jb * 8 + 2 * ks + h) * ROWS + rb * 32 + (lane & 31)]);
-              acc[ti][rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[ti][rb][0], 0, 0, 0);
-            }
-          }
-        } else {
-          const int q = lane >> 4;
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-            for (int ch = 0; ch < 2; ++ch) {
-              const bf16x8_t B = as_bf16x8(scr[wave][u][(4 * ks + q) * 32 + 16 * ch + (lane & 15)]);
-#pragma unroll
-              for (int rb = 0; rb < RB; ++rb) {
-                const bf16x8_t A = as_bf16x8(xs[(jb * 8 + 4 * ks + q) * ROWS + rb * 16 + (lane & 15)]);
-                acc[ti][rb][ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[ti][rb][ch], 0, 0, 0);
-              }
-            }
-          }
-        }
-      }
-    }
-    wave_lds_sync();
-
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      E[u] = En[u];
-      eo[u] = eon[u];
-      ec[u] = ecn[u];
-      eon[u] = eonn[u];
-      ecn[u] = ecnn[u];
-#pragma unroll
-      for (int i = 0; i < 3; ++i) R[u][i] = Rn[u][i];
-    }
   }
+  // The next launch adds the splits in split order and applies the epilogue
+  // (w12_wide_fixup_kernel, or the fused residual + RMSNorm for partial-sum
+  // epilogues): no device-scope fence or completion counter here (on a part
+  // with one L2 per XCD a device-scope release writes back the L2, and one
+  // per workgroup serialises the launch).
+}
 
-  // partial sums of this split
+// One workgroup per (group of 4 tiles, 32-row block): the wide kernel's split
+// sums (visible here through the kernel boundary) are added in split order
+// into LDS, with several pieces' loads of every split in flight together,
+// then the epilogue runs on the block's rows (its row-indexed pointers
+// offset to the block).  ARGMAX scans a row per thread.
+constexpr int kWideSumStride = 33;  // float4 per row of the LDS sums (padded: row-parallel reads spread over banks)
+__global__ __launch_bounds__(256) void w12_wide_fixup_kernel(GemmArgs a) {
+  __shared__ float4 sums[32 * kWideSumStride];  // [row][128 channels / 4 (+1)]
+  const int rbn = (a.m + 31) / 32;
+  const int g = blockIdx.x / rbn, r0 = (blockIdx.x % rbn) * 32, tid = threadIdx.x;
+  const int c0 = g * 4 * 32;
+  const int nc = min(a.n_pad, c0 + 4 * 32) - c0;  // a multiple of 32
+  const int M = min(32, a.m - r0), nq = nc / 4;
+  const int64_t sstride = (int64_t)a.m * a.n_pad / 4;  // float4 units
+  const float4* base = (const float4*)(a.part + (int64_t)r0 * a.n_pad + c0);
+  constexpr int U = 4, SJ = 4;  // pieces per thread and splits per round: U x SJ loads in flight
+  for (int i0 = 0; i0 < M * nq; i0 += 256 * U) {
+    float4 acc[U];
+    const float4* src[U];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    if (tw + t >= a.n_tiles) continue;
+    for (int u = 0; u < U; ++u) {
+      const int idx = min(i0 + tid + 256 * u, M * nq - 1);  // past the end: a repeat, not stored
+      src[u] = base + (int64_t)(idx / nq) * (a.n_pad / 4) + idx % nq;
+      acc[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    for (int s0 = 0; s0 < a.splits; s0 += SJ) {
+      float4 t[U][SJ];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch)
+        for (int j = 0; j < SJ; ++j) t[u][j] = src[u][min(s0 + j, a.splits - 1) * sstride];
 #pragma unroll
-        for (int v = 0; v < NACC; ++v) {
-          int row, col;
-          if constexpr (MT == 32) {
-            row = rb * 32 + (v >> 2) * 8 + 4 * (lane >> 5) + (v & 3);
-            col = (tw + t) * 32 + (lane & 31);
-          } else {
-            row = rb * 16 + 4 * (lane >> 4) + v;
-            col = (tw + t) * 32 + 16 * ch + (lane & 15);
-          }
-          if (row < a.m) a.part[((int64_t)sp * a.m + row) * a.n_pad + col] = acc[t][rb][ch][v];
-        }
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&a.cnt[g], 1u);
-    s_last = (old == (uint32_t)a.splits - 1u) ? 1u : 0u;
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < SJ; ++j)
+          if (s0 + j < a.splits) acc[u].x += t[u][j].x, acc[u].y += t[u][j].y, acc[u].z += t[u][j].z,
+                                 acc[u].w += t[u][j].w;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = i0 + tid + 256 * u;
+      if (idx < M * nq) sums[(idx / nq) * kWideSumStride + idx % nq] = acc[u];
+    }
   }
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid == 0) a.cnt[g] = 0u;
-
-  // ---------------------------------------------- reduction + epilogue
-  const int c0 = g * TG * 32;
-  const int c1 = min(a.n_pad, c0 + TG * 32);
-  const int nc = c1 - c0;
-  const int M = a.m;
-  auto red = [&](int row, int col) {
-    float v = 0.0f;
-    for (int s = 0; s < a.splits; ++s) v += a.part[((int64_t)s * M + row) * a.n_pad + col];
-    return v;
-  };
-  const int bucket = g;  // key slot: one per group
+  const float* sm = (const float*)sums;
+  auto red = [&](int row, int col) { return sm[row * (4 * kWideSumStride) + (col - c0)]; };
+  if (a.mode == TVP_EPI_ARGMAX) {  // one row per thread: best (value, smallest id) over the group's channels
+    if (tid < M) {
+      const int row = tid;
+      unsigned long long best = 0ull;
+      for (int cc = 0; cc < nc; ++cc) {
+        const int32_t r = a.rowmap[c0 + cc];  // the same address in every lane: one broadcast load
+        if (r < 0) continue;
+        const float v = red(row, c0 + cc);
+        if (a.logits) a.logits[(int64_t)(r0 + row) * a.ldl + r] = v;
+        const unsigned long long k = argmax_key(v, r);
+        best = k > best ? k : best;
+      }
+      a.keys[(int64_t)g * a.m + r0 + row] = best;
+    }
+    return;
+  }
+  GemmArgs b = a;  // row-indexed pointers moved to the block's first row
+  b.cache_rowmap = 1;
+  b.y = a.mode == TVP_EPI_F32 ? (void*)((float*)a.y + (int64_t)r0 * a.ldy)
+                              : (void*)((uint16_t*)a.y + (int64_t)r0 * a.ldy);
+  if (a.resid) b.resid = a.resid + (int64_t)r0 * a.ldr;
+  if (a.pos) b.pos = a.pos + r0;
+  if (a.slot) b.slot = a.slot + r0;
+  if (a.rope_cs) b.rope_cs = a.rope_cs + (int64_t)r0 * a.d;  // (cos, sin) pairs of d/2 dims per row
   switch (a.mode) {
-    case TVP_EPI_F32: epilogue<TVP_EPI_F32>(a, c0, nc, M, tid, 256, bucket, red); break;
-    case TVP_EPI_BF16: epilogue<TVP_EPI_BF16>(a, c0, nc, M, tid, 256, bucket, red); break;
-    case TVP_EPI_RESID: epilogue<TVP_EPI_RESID>(a, c0, nc, M, tid, 256, bucket, red); break;
-    case TVP_EPI_SWIGLU: epilogue<TVP_EPI_SWIGLU>(a, c0, nc, M, tid, 256, bucket, red); break;
-    case TVP_EPI_QKV: epilogue<TVP_EPI_QKV>(a, c0, nc, M, tid, 256, bucket, red); break;
-    default: epilogue<TVP_EPI_ARGMAX>(a, c0, nc, M, tid, 256, bucket, red); break;
+    case TVP_EPI_F32: epilogue<TVP_EPI_F32>(b, c0, nc, M, tid, 256, g, red); break;
+    case TVP_EPI_BF16: epilogue<TVP_EPI_BF16>(b, c0, nc, M, tid, 256, g, red); break;
+    case TVP_EPI_RESID: epilogue<TVP_EPI_RESID>(b, c0, nc, M, tid, 256, g, red); break;
+    case TVP_EPI_SWIGLU: epilogue<TVP_EPI_SWIGLU>(b, c0, nc, M, tid, 256, g, red); break;
+    default: epilogue<TVP_EPI_QKV>(b, c0, nc, M, tid, 256, g, red); break;
   }
 }
 
@@ -820,7 +832,7 @@ struct GemmPlan {
 // wavefronts split K (kbs <= 63 blocks each, so a wave's escape offsets fit
 // one VGPR).  Wide (m > 32, or K too long for 8 waves of 63 blocks):
 // workgroups of 4 tiles sharing X through LDS, split K over workgroups.
-constexpr int kWideTargetGroups = 1024;
+constexpr int kWideMaxSplits = 32;
 #ifndef TVP_TPW2_MIN_TILES
 #define TVP_TPW2_MIN_TILES 1024  // tiles from which a workgroup takes two tiles
 #endif
@@ -915,19 +927,25 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
       }
     }
   } else {
+    // K splits: the fewest that minimise the busiest CU's bytes -- its
+    // workgroups' record blocks (4 tiles x 3 KB each) plus its share of the
+    // fp32 split sums written and read back (none for a whole-K group)
     p.TPW = 1;
     p.RD = 0;
     p.KW = 4;
     p.TG = 4;
     p.groups = (int)ceil_div(w->n_tiles, p.TG);
-    int s = (int)((kWideTargetGroups + p.groups / 2) / p.groups);
-    s = std::max(s, 1);
-    const int smax = std::max((int)ceil_div(nkb, 2), 1);
-    s = std::min(s, smax);
-    int kbs = nkb > 0 ? (int)ceil_div(nkb, s) : 0;
-    kbs += kbs & 1;
-    p.kbs = kbs;
-    p.splits = kbs > 0 ? (int)ceil_div(nkb, kbs) : 1;
+    int best_s = 1;
+    double best = 1e300;
+    for (int sl = 1; sl <= std::min(kWideMaxSplits, std::max(nkb, 1)); ++sl) {
+      const int kbs = (int)ceil_div(std::max(nkb, 1), sl);
+      if ((int)ceil_div(std::max(nkb, 1), kbs) != sl) continue;
+      const double per_cu = (double)ceil_div((int64_t)p.groups * sl, kNumCUs) * kbs * 4 * kBlockBytes;
+      const double sums = sl > 1 ? 2.0 * sl * m * n_pad * 4 / kNumCUs : 0.0;
+      if (per_cu + sums < best - 1e-9) best = per_cu + sums, best_s = sl;
+    }
+    p.kbs = nkb > 0 ? (int)ceil_div(nkb, best_s) : 0;
+    p.splits = best_s;
     p.ntasks = p.groups * p.splits;
     p.grid = p.ntasks;
   }
@@ -969,7 +987,10 @@ static void launch_skinny(const GemmArgs& a, const GemmPlan& p, hipStream_t stre
 
 template <int RB>
 static void launch_wide(const GemmArgs& a, int grid, hipStream_t stream) {
-  w12_wide_kernel<32, RB, 1><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(a);
+  w12_wide_kernel<RB><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(a);
+  // partial-sum epilogues leave the split sums to their consumer
+  if (a.mode != kEpiPartial)
+    w12_wide_fixup_kernel<<<dim3((unsigned)(a.groups * ceil_div(a.m, 32))), dim3(256), 0, stream>>>(a);
 }
 
 static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
@@ -983,7 +1004,8 @@ static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
         else launch_skinny<32, 1, TVP_RD1>(a, p, stream);
       }
     } else {
-      switch (p.RB) {
+      switch ((int)ceil_div(a.m, 32)) {  // 32-row blocks
+        case 1: launch_wide<1>(a, p.grid, stream); break;
         case 2: launch_wide<2>(a, p.grid, stream); break;
         case 3: launch_wide<3>(a, p.grid, stream); break;
         case 4: launch_wide<4>(a, p.grid, stream); break;
@@ -1014,7 +1036,7 @@ bool gemm_is_skinny(int64_t m, const tvp_w12_packed* w) { return make_plan(m, w)
 
 int gemm_ksplits(int64_t m, const tvp_w12_packed* w, int ksplit) {
   const GemmPlan p = make_plan(m, w, ksplit);
-  return p.skinny ? p.splits : 1;
+  return p.splits;
 }
 
 void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes, int ksplit) {
@@ -1120,7 +1142,10 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
       if (epi->logits && epi->ldl < w->n_out) return TVP_ERR_ARG;
       break;
     case kEpiPartial:
-      if (!p.skinny || w->chan_map != TVP_CHAN_PLAIN || !epi->y || epi->ldy < w->n_out) return TVP_ERR_ARG;
+      // skinny: slices to y [slice][row][ldy]; wide: the split sums stay in
+      // the scratch, [split][row][n_pad] at its start, for the consumer
+      if (w->chan_map != TVP_CHAN_PLAIN) return TVP_ERR_ARG;
+      if (p.skinny && (!epi->y || epi->ldy < w->n_out)) return TVP_ERR_ARG;
       break;
     default:
       return TVP_ERR_ARG;
