@@ -584,23 +584,24 @@ __global__ __launch_bounds__(512) void w12_rem_fixup_kernel(GemmArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Wide kernel (33..192 rows): a workgroup owns 4 tiles (one per wavefront)
-// and a K range; all four wavefronts walk the same 64-column blocks, so one
-// copy of X per block serves them from LDS.  Per block: X for the block after
-// next is fetched into registers while this block is multiplied, and stored
-// to the other half of a double-buffered LDS tile behind one barrier; each
-// wavefront's records sit in a three-block register ring, are decoded into
-// its own LDS scratch, patched with the block's escapes, and multiplied
-// against RB row blocks of X (v_mfma_f32_32x32x16_bf16).  64 KB of LDS, so
-// two workgroups share a CU.  Rows are XOR-swizzled by their 16-byte column
-// group inside the X tile: the row-major fill and the column reads of the
-// MFMA A operand are both free of bank conflicts.
-template <int RB>
-__global__ __launch_bounds__(256, 2) void w12_wide_kernel(GemmArgs a) {
+// Wide kernel (33..192 rows): a workgroup owns 4 x TPW tiles (TPW per
+// wavefront) and a K range; all four wavefronts walk the same 64-column
+// blocks, so one copy of X per block serves them from LDS, and each A
+// fragment read from there feeds the MFMAs of the wavefront's TPW tiles.
+// Per block: X for the block after next is fetched into registers while this
+// block is multiplied, and stored to the other half of a double-buffered LDS
+// tile behind one barrier; each wavefront's records sit in a register ring,
+// are decoded into its own LDS scratch, patched with the block's escapes, and
+// multiplied against RB row blocks of X (v_mfma_f32_32x32x16_bf16).  Rows are
+// XOR-swizzled by their 16-byte column group inside the X tile: the
+// row-major fill and the column reads of the MFMA A operand are both free of
+// bank conflicts.
+template <int RB, int TPW, int RD>
+__global__ __launch_bounds__(256, TPW == 1 ? 2 : 1) void w12_wide_kernel(GemmArgs a) {
   constexpr int ROWS = 32 * RB;
-  constexpr int RD = 3;  // register-ring depth (blocks in flight per wavefront)
+  // RD: register-ring depth (blocks of records in flight per wavefront).
   __shared__ uint4 xs[2][8 * ROWS];  // X block [k group][row ^ k group]
-  __shared__ uint4 scr[4][256];      // per-wavefront decode scratch: one 32 x 64 tile block
+  __shared__ uint4 scr[4][TPW][256];  // per-wavefront decode scratch: one 32 x 64 block per tile
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   // uniform per wavefront, so the escape offsets below are scalar loads and
@@ -610,15 +611,22 @@ __global__ __launch_bounds__(256, 2) void w12_wide_kernel(GemmArgs a) {
   const int kb0 = sp * a.kbs;
   const int kb1 = min(a.n_kb, kb0 + a.kbs);
   const int nblk = kb1 > kb0 ? kb1 - kb0 : 0;
-  const int tile = g * 4 + wave;
-  const int tt = min(tile, a.n_tiles - 1);  // a tile past the end runs clamped; its results are dropped
-  const uint32_t b2v = a.b2[tt * 32 + (lane & 31)];
+  const int tile0 = (g * 4 + wave) * TPW;
+  int tt[TPW];
+  uint32_t b2v[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    tt[t] = min(tile0 + t, a.n_tiles - 1);  // a tile past the end runs clamped; its results are dropped
+    b2v[t] = a.b2[tt[t] * 32 + (lane & 31)];
+  }
 
-  f32x16_t acc[RB];
+  f32x16_t acc[TPW][RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[rb][v] = 0.0f;
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[t][rb][v] = 0.0f;
 
   // X block j (row-major x; rows >= m and columns >= k_in read as zero):
   // thread piece i is row (tid + 256 i) / 8, 16-byte group (tid % 8)
@@ -651,48 +659,59 @@ __global__ __launch_bounds__(256, 2) void w12_wide_kernel(GemmArgs a) {
 
   // records and escape entries of block i into ring slot `slot` (past the
   // end: the last block again, result unused)
-  uint4 R[RD][3];
-  uint32_t E[RD], EO[RD], EC[RD];
+  uint4 R[RD][TPW][3];
+  uint32_t E[RD][TPW], EO[RD][TPW], EC[RD][TPW];
   auto issue = [&](int i, int slot) {
     const int j = kb0 + min(i, max(nblk - 1, 0));
-    const int64_t un = (int64_t)tt * a.n_kb + j;
-    const uint32_t eo = a.escoff[un];
-    const uint32_t ec = a.escoff[un + 1] - eo;
-    const uint4* blk = (const uint4*)(a.rec + rec_block(tt, j, a.n_tiles) * kBlockBytes);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) R[slot][q] = load_nt(blk + q * 64 + lane);
-    // lanes past the count read a neighbour (the blob continues past the
-    // escape list) and are never used
-    E[slot] = a.esc[(uint32_t)lane < ec ? eo + lane : eo];
-    EO[slot] = eo;
-    EC[slot] = ec;
+    for (int t = 0; t < TPW; ++t) {
+      const int64_t un = (int64_t)tt[t] * a.n_kb + j;
+      const uint32_t eo = a.escoff[un];
+      const uint32_t ec = a.escoff[un + 1] - eo;
+      const uint4* blk = (const uint4*)(a.rec + rec_block(tt[t], j, a.n_tiles) * kBlockBytes);
+#pragma unroll
+      for (int q = 0; q < 3; ++q) R[slot][t][q] = load_nt(blk + q * 64 + lane);
+      // lanes past the count read a neighbour (the blob continues past the
+      // escape list) and are never used
+      E[slot][t] = a.esc[(uint32_t)lane < ec ? eo + lane : eo];
+      EO[slot][t] = eo;
+      EC[slot][t] = ec;
+    }
   };
 
   auto process = [&](int slot, int buf) {
-    uint32_t o[16];
-    decode_block(R[slot], b2v, o);
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
-      scr[wave][64 * s4 + lane] = make_uint4(o[4 * s4], o[4 * s4 + 1], o[4 * s4 + 2], o[4 * s4 + 3]);
+    for (int t = 0; t < TPW; ++t) {
+      uint32_t o[16];
+      decode_block(R[slot][t], b2v[t], o);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        scr[wave][t][64 * s4 + lane] = make_uint4(o[4 * s4], o[4 * s4 + 1], o[4 * s4 + 2], o[4 * s4 + 3]);
+    }
     lds_order();
-    {
-      uint16_t* sh = (uint16_t*)&scr[wave][0];
-      const uint32_t ec = EC[slot];
-      if ((uint32_t)lane < ec) sh[E[slot] & 0x7FFu] = (uint16_t)(E[slot] >> 16);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      uint16_t* sh = (uint16_t*)&scr[wave][t][0];
+      const uint32_t ec = EC[slot][t];
+      if ((uint32_t)lane < ec) sh[E[slot][t] & 0x7FFu] = (uint16_t)(E[slot][t] >> 16);
       for (uint32_t e = 64 + lane; e < ec; e += 64) {  // more escapes than lanes (rare)
-        const uint32_t ent = a.esc[EO[slot] + e];
+        const uint32_t ent = a.esc[EO[slot][t] + e];
         sh[ent & 0x7FFu] = (uint16_t)(ent >> 16);
       }
     }
     lds_order();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t B = as_bf16x8(scr[wave][64 * ks + lane]);
+      bf16x8_t B[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) B[t] = as_bf16x8(scr[wave][t][64 * ks + lane]);
       const int kg = 2 * ks + h;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const bf16x8_t A = as_bf16x8(xs[buf][kg * ROWS + ((rb * 32 + (lane & 31)) ^ kg)]);
-        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[rb], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          acc[t][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[t], acc[t][rb], 0, 0, 0);
       }
     }
     lds_order();
@@ -723,14 +742,16 @@ __global__ __launch_bounds__(256, 2) void w12_wide_kernel(GemmArgs a) {
   }
 
   // this split's sums: part [split][row][packed channel]
-  if (tile < a.n_tiles) {
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    if (tile0 + t >= a.n_tiles) continue;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = rb * 32 + (v >> 2) * 8 + 4 * h + (v & 3);
-        const int col = tile * 32 + (lane & 31);
-        if (row < a.m) a.part[((int64_t)sp * a.m + row) * a.n_pad + col] = acc[rb][v];
+        const int col = (tile0 + t) * 32 + (lane & 31);
+        if (row < a.m) a.part[((int64_t)sp * a.m + row) * a.n_pad + col] = acc[t][rb][v];
       }
   }
   // The next launch adds the splits in split order and applies the epilogue
@@ -833,6 +854,14 @@ struct GemmPlan {
 // one VGPR).  Wide (m > 32, or K too long for 8 waves of 63 blocks):
 // workgroups of 4 tiles sharing X through LDS, split K over workgroups.
 constexpr int kWideMaxSplits = 32;
+#ifndef TVP_WIDE_TPW
+#define TVP_WIDE_TPW 2
+#endif
+#ifndef TVP_WIDE_RD
+#define TVP_WIDE_RD 2
+#endif
+constexpr int kWideTPW = TVP_WIDE_TPW;  // wide kernel: tiles per wavefront (a workgroup owns 4 x kWideTPW)
+constexpr int kWideRD = TVP_WIDE_RD;    // wide kernel: register-ring depth
 #ifndef TVP_TPW2_MIN_TILES
 #define TVP_TPW2_MIN_TILES 1024  // tiles from which a workgroup takes two tiles
 #endif
@@ -930,17 +959,17 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
     // K splits: the fewest that minimise the busiest CU's bytes -- its
     // workgroups' record blocks (4 tiles x 3 KB each) plus its share of the
     // fp32 split sums written and read back (none for a whole-K group)
-    p.TPW = 1;
+    p.TPW = kWideTPW;
     p.RD = 0;
     p.KW = 4;
-    p.TG = 4;
+    p.TG = 4 * kWideTPW;
     p.groups = (int)ceil_div(w->n_tiles, p.TG);
     int best_s = 1;
     double best = 1e300;
     for (int sl = 1; sl <= std::min(kWideMaxSplits, std::max(nkb, 1)); ++sl) {
       const int kbs = (int)ceil_div(std::max(nkb, 1), sl);
       if ((int)ceil_div(std::max(nkb, 1), kbs) != sl) continue;
-      const double per_cu = (double)ceil_div((int64_t)p.groups * sl, kNumCUs) * kbs * 4 * kBlockBytes;
+      const double per_cu = (double)ceil_div((int64_t)p.groups * sl, kNumCUs) * kbs * p.TG * kBlockBytes;
       const double sums = sl > 1 ? 2.0 * sl * m * n_pad * 4 / kNumCUs : 0.0;
       if (per_cu + sums < best - 1e-9) best = per_cu + sums, best_s = sl;
     }
@@ -951,7 +980,7 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
   }
   // skinny: room to pack row-major activations; wide: split-K partial sums;
   // then the argmax key slots (one per workgroup / group)
-  p.key_slots = p.skinny ? p.grid : p.groups;
+  p.key_slots = p.skinny ? p.grid : (int)ceil_div(w->n_tiles, 4);  // wide: one per fix-up group of 4 tiles
   p.keys_off = p.skinny ? align_up((size_t)std::max(nkb, 1) * 4096, 256)
                         : align_up((size_t)p.splits * m * n_pad * 4, 256);
   p.rem_off = p.keys_off + align_up((size_t)std::max(p.key_slots, 1) * m * 8, 256);
@@ -987,10 +1016,15 @@ static void launch_skinny(const GemmArgs& a, const GemmPlan& p, hipStream_t stre
 
 template <int RB>
 static void launch_wide(const GemmArgs& a, int grid, hipStream_t stream) {
-  w12_wide_kernel<RB><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(a);
-  // partial-sum epilogues leave the split sums to their consumer
+  // one tile per wavefront: the deepest ring that fits two wavefronts per
+  // SIMD without spills; two tiles: one wavefront per SIMD
+  constexpr int rd = kWideTPW == 2 ? kWideRD : (RB <= 4 ? kWideRD : 4);
+  w12_wide_kernel<RB, kWideTPW, rd><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(a);
+  // partial-sum epilogues leave the split sums to their consumer; the fix-up
+  // takes groups of 4 tiles (one ARGMAX key slot each)
   if (a.mode != kEpiPartial)
-    w12_wide_fixup_kernel<<<dim3((unsigned)(a.groups * ceil_div(a.m, 32))), dim3(256), 0, stream>>>(a);
+    w12_wide_fixup_kernel<<<dim3((unsigned)(ceil_div(a.n_tiles, 4) * ceil_div(a.m, 32))), dim3(256), 0,
+                            stream>>>(a);
 }
 
 static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
