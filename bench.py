@@ -268,8 +268,8 @@ def pass_roles(trace_csv: str) -> dict:
         m = re.search(r"w12_skinny_kernel<\d+, \d+, \d+, (\d+)>", name)
         if m:
             return {"3": "gateup", "4": "qkv", "5": "lmhead", "16": "partial"}.get(m.group(1), "gemm")
-        for key, lab in (("rem_fixup", "fixup"), ("tree_attn_merge", "merge"), ("tree_attn_kernel", "attn"),
-                         ("resid_norm", "norm")):
+        for key, lab in (("rem_fixup", "fixup"), ("wide_fixup", "wfix"), ("w12_wide_kernel", "wide"),
+                         ("tree_attn_merge", "merge"), ("tree_attn_kernel", "attn"), ("resid_norm", "norm")):
             if key in name:
                 return lab
         for key, lab in SMALL_ROLES:
@@ -292,22 +292,36 @@ def pass_roles(trace_csv: str) -> dict:
         elif k == "partial":
             role = {"attention merge": "O GEMM (K slices)", "gate/up fix-up": "down GEMM (K slices)"}.get(prev)
         elif k == "norm":
-            role = {"O GEMM (K slices)": "residual + norm after O",
-                    "down GEMM (K slices)": "residual + norm after down"}.get(prev, "norm (first or final)")
+            role = {"O GEMM (K slices)": "residual + norm after O", "wide O GEMM (split sums)": "residual + norm after O",
+                    "down GEMM (K slices)": "residual + norm after down",
+                    "wide down GEMM (split sums)": "residual + norm after down"}.get(prev, "norm (first or final)")
         elif k == "gateup":
             role = "gate/up GEMM" if prev == "residual + norm after O" else None
         elif k == "fixup":
             role = "gate/up fix-up" if prev == "gate/up GEMM" else None
         elif k == "lmhead":
             role = "LM head + argmax"
+        elif k == "wide":  # more than 32 rows: named by the launch before it
+            role = {"norm (first or final)": "wide QKV GEMM", "residual + norm after down": "wide QKV GEMM",
+                    "tree attention": "wide O GEMM (split sums)", "attention merge": "wide O GEMM (split sums)",
+                    "residual + norm after O": "wide gate/up GEMM",
+                    "wide gate/up fix-up (SwiGLU)": "wide down GEMM (split sums)"}.get(prev)
+            if role == "wide QKV GEMM" and i + 2 < len(kinds) and kinds[i + 2] == "LM-head argmax finalize":
+                role = "wide LM head"
+        elif k == "wfix":
+            role = {"wide QKV GEMM": "wide QKV fix-up (RoPE, KV write)", "wide gate/up GEMM": "wide gate/up fix-up (SwiGLU)",
+                    "wide LM head": "wide LM-head fix-up (argmax keys)"}.get(prev)
         elif k != "other":
             role = k
         role_of.append(role)
         if role:
             out.setdefault(role, []).append((rows[i][1] - rows[i][0]) / 1e3)
-    order = ["QKV GEMM + RoPE + KV write", "tree attention", "attention merge", "O GEMM (K slices)",
-             "residual + norm after O", "gate/up GEMM", "gate/up fix-up", "down GEMM (K slices)",
-             "residual + norm after down", "norm (first or final)", "LM head + argmax"] + [r for _, r in SMALL_ROLES]
+    order = ["QKV GEMM + RoPE + KV write", "wide QKV GEMM", "wide QKV fix-up (RoPE, KV write)", "tree attention",
+             "attention merge", "O GEMM (K slices)", "wide O GEMM (split sums)", "residual + norm after O",
+             "gate/up GEMM", "gate/up fix-up", "wide gate/up GEMM", "wide gate/up fix-up (SwiGLU)",
+             "down GEMM (K slices)", "wide down GEMM (split sums)", "residual + norm after down",
+             "norm (first or final)", "LM head + argmax", "wide LM head", "wide LM-head fix-up (argmax keys)"] + \
+        [r for _, r in SMALL_ROLES]
     return {r: out[r] for r in order if r in out}
 
 
@@ -625,8 +639,8 @@ def main() -> int:
                    "ffn": cfg.ffn, "vocab": cfg.vocab, "nodes": cfg.n_nodes, "ctx_len": cfg.ctx_len,
                    "weights": "W12 (random-init bf16, per-channel sigma log-uniform [0.005,0.05], 1% zeros, "
                               "0.05% outliers x1000)", "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": ("w12_skinny_kernel<32,2,2,SWIGLU> + w12_rem_fixup_kernel<SWIGLU> "
-                                "(fused gate/up, 34816x5120: 512 whole groups, 32 in 8 K slices)"), "bound": "hbm",
+        "roofline": {"kernel": (f"w12_skinny_kernel<32,2,2,SWIGLU> + w12_rem_fixup_kernel<SWIGLU> "
+                                f"(fused gate/up, {2 * cfg.ffn}x{cfg.hidden})"), "bound": "hbm",
                      "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(g_gbs / HBM_PEAK_GBS, 4), "probe_frac": round(g_gbs / probe, 4),
                      "traffic": recorded_traffic(),

@@ -657,17 +657,36 @@ __global__ __launch_bounds__(256, TPW == 1 ? 2 : 1) void w12_wide_kernel(GemmArg
     for (int i = 0; i < RB; ++i) xs[buf][kg * ROWS + (((tid >> 3) + 32 * i) ^ kg)] = xr[i];
   };
 
+  // Escape offsets of a window of 64 blocks, one VGPR per tile (lane l:
+  // block wbase + l), read with readlane: no load in the ring waits on
+  // another (a dependent offset load per block would make every step wait
+  // for all older loads, the ring's included).  A window serves 60 blocks
+  // plus the ring's lookahead.
+  constexpr int kWin = 60;
+  static_assert(kWin % RD == 0 && kWin + RD <= 64, "window");
+  uint32_t ewin[TPW];
+  int wbase = 0;
+  auto load_win = [&](int w0) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) ewin[t] = a.escoff[(int64_t)tt[t] * a.n_kb + min(kb0 + w0 + lane, a.n_kb)];
+    wbase = w0;
+    // consumed here, once per window: the inner loop's header then never
+    // waits for it (which would drain the whole ring)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) asm volatile("" ::"v"(ewin[t]));
+  };
+
   // records and escape entries of block i into ring slot `slot` (past the
   // end: the last block again, result unused)
   uint4 R[RD][TPW][3];
   uint32_t E[RD][TPW], EO[RD][TPW], EC[RD][TPW];
   auto issue = [&](int i, int slot) {
-    const int j = kb0 + min(i, max(nblk - 1, 0));
+    const int ic = min(i, max(nblk - 1, 0));
+    const int j = kb0 + ic;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const int64_t un = (int64_t)tt[t] * a.n_kb + j;
-      const uint32_t eo = a.escoff[un];
-      const uint32_t ec = a.escoff[un + 1] - eo;
+      const uint32_t eo = __builtin_amdgcn_readlane(ewin[t], ic - wbase);
+      const uint32_t ec = __builtin_amdgcn_readlane(ewin[t], ic - wbase + 1) - eo;
       const uint4* blk = (const uint4*)(a.rec + rec_block(tt[t], j, a.n_tiles) * kBlockBytes);
 #pragma unroll
       for (int q = 0; q < 3; ++q) R[slot][t][q] = load_nt(blk + q * 64 + lane);
@@ -718,6 +737,7 @@ __global__ __launch_bounds__(256, TPW == 1 ? 2 : 1) void w12_wide_kernel(GemmArg
   };
 
   if (nblk > 0) {
+    load_win(0);
 #pragma unroll
     for (int p = 0; p < RD - 1; ++p) issue(p, p);
     load_x(kb0);
@@ -727,16 +747,20 @@ __global__ __launch_bounds__(256, TPW == 1 ? 2 : 1) void w12_wide_kernel(GemmArg
     // The ring slot is a compile-time constant inside each unrolled group,
     // and the loads run unconditionally (clamped to the last block past the
     // end), so the wait counts stay exact.
-    for (int i0 = 0; i0 < nblk; i0 += RD) {
+    for (int w0 = 0; w0 < nblk; w0 += kWin) {
+      if (w0 > 0) load_win(w0);  // blocks issued ahead from the last window are in this one too
+      const int wend = min(nblk, w0 + kWin);
+      for (int i0 = w0; i0 < wend; i0 += RD) {
 #pragma unroll
-      for (int r = 0; r < RD; ++r) {
-        const int i = i0 + r;
-        issue(i + RD - 1, (r + RD - 1) % RD);
-        if (i < nblk) process(r, i & 1);
-        store_x((i + 1) & 1);  // block i + 1, fetched one block ago (its buffer was last read before
-                               // the previous barrier)
-        load_x(kb0 + min(i + 2, nblk - 1));
-        __syncthreads();
+        for (int r = 0; r < RD; ++r) {
+          const int i = i0 + r;
+          issue(i + RD - 1, (r + RD - 1) % RD);
+          if (i < wend) process(r, i & 1);
+          store_x((i + 1) & 1);  // block i + 1, fetched one block ago (its buffer was last read before
+                                 // the previous barrier)
+          load_x(kb0 + min(i + 2, nblk - 1));
+          __syncthreads();
+        }
       }
     }
   }
