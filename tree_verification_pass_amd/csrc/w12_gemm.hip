@@ -628,27 +628,34 @@ __global__ __launch_bounds__(256, TPW == 1 ? 2 : 1) void w12_wide_kernel(GemmArg
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][rb][v] = 0.0f;
 
-  // X block j (row-major x; rows >= m and columns >= k_in read as zero):
-  // thread piece i is row (tid + 256 i) / 8, 16-byte group (tid % 8)
+  // X block j (row-major x): thread piece i is row (tid + 256 i) / 8,
+  // 16-byte group (tid % 8).  A block inside k_in loads without branches:
+  // rows past m read row m - 1 and only feed output rows that are never
+  // stored.  The ragged last block (a uniform branch) reads zeros past k_in
+  // and past m.
   uint4 xr[RB];
   auto load_x = [&](int j) {
     const int64_t k = (int64_t)j * kBlockK + 8 * (tid & 7);
+    if ((int64_t)(j + 1) * kBlockK <= a.k_in) {
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < a.m) {
-        const uint16_t* src = a.x + (int64_t)row * a.ldx + k;
-        if (k + 8 <= a.k_in) {
-          v = *(const uint4*)src;
-        } else if (k < a.k_in) {
+      for (int i = 0; i < RB; ++i) {
+        const int row = min((tid >> 3) + 32 * i, a.m - 1);
+        xr[i] = *(const uint4*)(a.x + (int64_t)row * a.ldx + k);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int row = (tid >> 3) + 32 * i;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < a.m && k < a.k_in) {
+          const uint16_t* src = a.x + (int64_t)row * a.ldx + k;
           uint32_t hh[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) hh[e] = (k + e < a.k_in) ? src[e] : 0u;
           v = make_uint4(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16), hh[4] | (hh[5] << 16), hh[6] | (hh[7] << 16));
         }
+        xr[i] = v;
       }
-      xr[i] = v;
     }
   };
   auto store_x = [&](int buf) {
@@ -660,9 +667,9 @@ __global__ __launch_bounds__(256, TPW == 1 ? 2 : 1) void w12_wide_kernel(GemmArg
   // Escape offsets of a window of 64 blocks, one VGPR per tile (lane l:
   // block wbase + l), read with readlane: no load in the ring waits on
   // another (a dependent offset load per block would make every step wait
-  // for all older loads, the ring's included).  A window serves 60 blocks
-  // plus the ring's lookahead.
-  constexpr int kWin = 60;
+  // for all older loads, the ring's included).  A window serves kWin blocks
+  // (a multiple of the ring depth) plus the ring's lookahead.
+  constexpr int kWin = (64 - RD) / RD * RD;
   static_assert(kWin % RD == 0 && kWin + RD <= 64, "window");
   uint32_t ewin[TPW];
   int wbase = 0;
@@ -879,13 +886,17 @@ struct GemmPlan {
 // workgroups of 4 tiles sharing X through LDS, split K over workgroups.
 constexpr int kWideMaxSplits = 32;
 #ifndef TVP_WIDE_TPW
-#define TVP_WIDE_TPW 2
+#define TVP_WIDE_TPW 1
 #endif
 #ifndef TVP_WIDE_RD
-#define TVP_WIDE_RD 2
+#define TVP_WIDE_RD 4
 #endif
 constexpr int kWideTPW = TVP_WIDE_TPW;  // wide kernel: tiles per wavefront (a workgroup owns 4 x kWideTPW)
+#ifndef TVP_WIDE_RD_BIG
+#define TVP_WIDE_RD_BIG 4
+#endif
 constexpr int kWideRD = TVP_WIDE_RD;    // wide kernel: register-ring depth
+constexpr int kWideRDBig = TVP_WIDE_RD_BIG;  // ... above 128 rows (one tile per wavefront, two wavefronts per SIMD)
 #ifndef TVP_TPW2_MIN_TILES
 #define TVP_TPW2_MIN_TILES 1024  // tiles from which a workgroup takes two tiles
 #endif
@@ -1042,7 +1053,7 @@ template <int RB>
 static void launch_wide(const GemmArgs& a, int grid, hipStream_t stream) {
   // one tile per wavefront: the deepest ring that fits two wavefronts per
   // SIMD without spills; two tiles: one wavefront per SIMD
-  constexpr int rd = kWideTPW == 2 ? kWideRD : (RB <= 4 ? kWideRD : 4);
+  constexpr int rd = kWideTPW == 2 ? kWideRD : (RB <= 4 ? kWideRD : kWideRDBig);
   w12_wide_kernel<RB, kWideTPW, rd><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(a);
   // partial-sum epilogues leave the split sums to their consumer; the fix-up
   // takes groups of 4 tiles (one ARGMAX key slot each)
