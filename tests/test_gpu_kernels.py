@@ -271,16 +271,17 @@ def test_gemm_remaining_groups_split_over_k(tvp, cuda, m):
         assert np.mean(got == ref) > 0.97
 
 
-def test_argmax_ties_go_to_smallest_id(tvp, cuda):
+@pytest.mark.parametrize("m", [4, 70])  # skinny kernel's epilogue; wide kernel's fix-up (8 threads per row)
+def test_argmax_ties_go_to_smallest_id(tvp, cuda, m):
     # identical channels produce exactly equal logits: the smallest id must win
     H, V = 256, 2048
     base = bf16_bits_numpy(gen_linear_bf16(make_generator(31), 1, H, TINY_RECIPE))
     w = np.repeat(base, V, axis=0)
     rng = np.random.default_rng(2)
     w[rng.permutation(V)[:1500]] = bf16_bits_numpy(gen_linear_bf16(make_generator(32), 1500, H, TINY_RECIPE))
-    x = _x(4, H, 9, cuda)
-    am = torch.zeros(4, dtype=torch.int32, device=cuda)
-    lg = torch.zeros(4, V, dtype=torch.float32, device=cuda)
+    x = _x(m, H, 9, cuda)
+    am = torch.zeros(m, dtype=torch.int32, device=cuda)
+    lg = torch.zeros(m, V, dtype=torch.float32, device=cuda)
     epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_ARGMAX, argmax=am.data_ptr(), logits=lg.data_ptr(), ldl=V)
     tvp.w12_gemm_ex(x, _packed(tvp, w, cuda), epi)
     torch.cuda.synchronize()

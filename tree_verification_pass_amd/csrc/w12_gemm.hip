@@ -839,20 +839,27 @@ __global__ __launch_bounds__(256) void w12_wide_fixup_kernel(GemmArgs a) {
   __syncthreads();
   const float* sm = (const float*)sums;
   auto red = [&](int row, int col) { return sm[row * (4 * kWideSumStride) + (col - c0)]; };
-  if (a.mode == TVP_EPI_ARGMAX) {  // one row per thread: best (value, smallest id) over the group's channels
-    if (tid < M) {
-      const int row = tid;
-      unsigned long long best = 0ull;
-      for (int cc = 0; cc < nc; ++cc) {
-        const int32_t r = a.rowmap[c0 + cc];  // the same address in every lane: one broadcast load
+  if (a.mode == TVP_EPI_ARGMAX) {  // best (value, smallest id) over the group's channels, 8 threads per row
+    __shared__ int32_t rmap[128];
+    if (tid < nc) rmap[tid] = a.rowmap[c0 + tid];
+    __syncthreads();
+    const int row = tid >> 3, part = tid & 7;  // part p scans channels p, p + 8, ...
+    unsigned long long best = 0ull;
+    if (row < M) {
+      for (int cc = part; cc < nc; cc += 8) {
+        const int32_t r = rmap[cc];
         if (r < 0) continue;
         const float v = red(row, c0 + cc);
         if (a.logits) a.logits[(int64_t)(r0 + row) * a.ldl + r] = v;
         const unsigned long long k = argmax_key(v, r);
         best = k > best ? k : best;
       }
-      a.keys[(int64_t)g * a.m + r0 + row] = best;
     }
+    for (int off = 4; off > 0; off >>= 1) {  // the row's 8 threads are adjacent lanes
+      const unsigned long long o = __shfl_xor(best, off);
+      best = o > best ? o : best;
+    }
+    if (row < M && part == 0) a.keys[(int64_t)g * a.m + r0 + row] = best;
     return;
   }
   GemmArgs b = a;  // row-indexed pointers moved to the block's first row
