@@ -86,6 +86,7 @@ struct AttnArgs {
   float* pm;
   float* pl;
   int row_blocks;  // merge: 32-row blocks per (request, kv head)
+  int8_t order[kMaxReq];  // request of each unit slot: longest key range first (batched passes)
   PartRows pr;
   uint16_t* out;
   int out_packed;  // out in the packed activation layout (<= 32 nodes) instead of [node][hq * D]
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
   if (u >= a.units) return;
   const int split = u % a.max_splits;
   const int kh = (u / a.max_splits) % a.hkv;
-  const int r = u / (a.max_splits * a.hkv);
+  const int r = a.order[u / (a.max_splits * a.hkv)];
   const int L = a.ri.ctx_len[r], nb = a.ri.node_ptr[r], n = a.ri.node_ptr[r + 1] - nb;
   const int T = L + n, R = a.G * n;
   const int nsplit = (T + a.kr - 1) / a.kr;
@@ -501,7 +502,10 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
 
 // Key splits are sized so that one launch has about this many workgroups
 // (one per compute unit).
-constexpr int kAttnTargetGroups = 256;
+#ifndef TVP_ATTN_TARGET_GROUPS
+#define TVP_ATTN_TARGET_GROUPS 256
+#endif
+constexpr int kAttnTargetGroups = TVP_ATTN_TARGET_GROUPS;
 // Blocks of 32 keys per wavefront kept in flight (including the one in LDS).
 constexpr int kAttnStages = 2;
 
@@ -578,6 +582,13 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
   a.out = out;
   a.out_packed = out_packed;
   a.row_blocks = p.row_blocks;
+  // Workgroups start in index order and run for a time proportional to
+  // their request's key range, so the longest requests go first (the tail of
+  // the launch is then the shortest work).  Ties keep request order.
+  for (int i = 0; i < n_req; ++i) a.order[i] = (int8_t)i;
+  std::stable_sort(a.order, a.order + n_req, [&](int8_t x, int8_t y) {
+    return ri.ctx_len[x] + (ri.node_ptr[x + 1] - ri.node_ptr[x]) > ri.ctx_len[y] + (ri.node_ptr[y + 1] - ri.node_ptr[y]);
+  });
   a.units = n_req * hkv * p.max_splits;
   a.units8 = (int)align_up((size_t)a.units, 8);
   const dim3 grid((unsigned)(a.units8 * p.row_blocks));

@@ -907,7 +907,10 @@ constexpr int kWideRDBig = TVP_WIDE_RD_BIG;  // ... above 128 rows (one tile per
 #ifndef TVP_TPW2_MIN_TILES
 #define TVP_TPW2_MIN_TILES 1024  // tiles from which a workgroup takes two tiles
 #endif
-constexpr int kWavesPerCU = 12;  // skinny kernel: three wavefronts per SIMD (136-156 VGPRs)
+#ifndef TVP_WAVES_PER_CU
+#define TVP_WAVES_PER_CU 12
+#endif
+constexpr int kWavesPerCU = TVP_WAVES_PER_CU;  // skinny kernel: three wavefronts per SIMD (136-156 VGPRs)
 #ifndef TVP_RD1
 #define TVP_RD1 3  // register-ring depth, one tile per workgroup
 #endif
