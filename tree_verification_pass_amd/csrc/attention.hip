@@ -87,6 +87,7 @@ struct AttnArgs {
   float* pl;
   int row_blocks;  // merge: 32-row blocks per (request, kv head)
   int8_t order[kMaxReq];  // request of each unit slot: longest key range first (batched passes)
+  int grouped;            // block order: units in groups of 8, row blocks inner (batched passes)
   PartRows pr;
   uint16_t* out;
   int out_packed;  // out in the packed activation layout (<= 32 nodes) instead of [node][hq * D]
@@ -155,9 +156,13 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
   __shared__ float ml[NW][2][32];  // per wavefront and row: exponent base (a raw score), sum
   static_assert(sizeof(tiles) >= NW * NACC * 64 * sizeof(float), "O of all wavefronts fits the tiles");
 
-  // block -> (row block, unit): the row blocks of one (request, kv head,
-  // split) are a multiple of 8 apart, so they run on one XCD and share its L2
-  const int u = blockIdx.x % a.units8, rb = blockIdx.x / a.units8;
+  // block -> (row block, unit).  The row blocks of one (request, kv head,
+  // split) are a multiple of 8 apart, so they run on one XCD and share its
+  // L2.  Batched passes take units in groups of 8 with all their row blocks
+  // before the next group (with the longest requests first, their work all
+  // starts first); one request takes row block by row block.
+  const int u = a.grouped ? (blockIdx.x / (8 * a.row_blocks)) * 8 + blockIdx.x % 8 : blockIdx.x % a.units8;
+  const int rb = a.grouped ? (blockIdx.x / 8) % a.row_blocks : blockIdx.x / a.units8;
   if (u >= a.units) return;
   const int split = u % a.max_splits;
   const int kh = (u / a.max_splits) % a.hkv;
@@ -589,6 +594,7 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
   std::stable_sort(a.order, a.order + n_req, [&](int8_t x, int8_t y) {
     return ri.ctx_len[x] + (ri.node_ptr[x + 1] - ri.node_ptr[x]) > ri.ctx_len[y] + (ri.node_ptr[y + 1] - ri.node_ptr[y]);
   });
+  a.grouped = n_req > 1 ? 1 : 0;
   a.units = n_req * hkv * p.max_splits;
   a.units8 = (int)align_up((size_t)a.units, 8);
   const dim3 grid((unsigned)(a.units8 * p.row_blocks));
