@@ -892,6 +892,13 @@ struct GemmPlan {
 // one VGPR).  Wide (m > 32, or K too long for 8 waves of 63 blocks):
 // workgroups of 4 tiles sharing X through LDS, split K over workgroups.
 constexpr int kWideMaxSplits = 32;
+#ifndef TVP_WIDE_SUM_WEIGHT
+#define TVP_WIDE_SUM_WEIGHT 0.5
+#endif
+// Cost of a split-sum byte against a record byte: the sums are written and
+// read back within microseconds, mostly from the caches (measured: 0.5 beat
+// 1 by 3.5% on the batched 27B-like step, 0.25 by 2%, 0 lost 50%).
+constexpr double kWideSumWeight = TVP_WIDE_SUM_WEIGHT;
 #ifndef TVP_WIDE_TPW
 #define TVP_WIDE_TPW 1
 #endif
@@ -1003,7 +1010,8 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
   } else {
     // K splits: the fewest that minimise the busiest CU's bytes -- its
     // workgroups' record blocks (4 tiles x 3 KB each) plus its share of the
-    // fp32 split sums written and read back (none for a whole-K group)
+    // fp32 split sums written and read back (none for a whole-K group),
+    // weighted by kWideSumWeight
     p.TPW = kWideTPW;
     p.RD = 0;
     p.KW = 4;
@@ -1015,7 +1023,7 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
       const int kbs = (int)ceil_div(std::max(nkb, 1), sl);
       if ((int)ceil_div(std::max(nkb, 1), kbs) != sl) continue;
       const double per_cu = (double)ceil_div((int64_t)p.groups * sl, kNumCUs) * kbs * p.TG * kBlockBytes;
-      const double sums = sl > 1 ? 2.0 * sl * m * n_pad * 4 / kNumCUs : 0.0;
+      const double sums = sl > 1 ? kWideSumWeight * 2.0 * sl * m * n_pad * 4 / kNumCUs : 0.0;
       if (per_cu + sums < best - 1e-9) best = per_cu + sums, best_s = sl;
     }
     p.kbs = nkb > 0 ? (int)ceil_div(nkb, best_s) : 0;
