@@ -634,14 +634,19 @@ __global__ __launch_bounds__(256, TPW == 1 ? 2 : 1) void w12_wide_kernel(GemmArg
   // stored.  The ragged last block (a uniform branch) reads zeros past k_in
   // and past m.
   uint4 xr[RB];
+  // this thread's row pointers (clamped rows) and LDS slots, formed once
+  const uint16_t* xrow[RB];
+  int xslot[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    xrow[i] = a.x + (int64_t)min((tid >> 3) + 32 * i, a.m - 1) * a.ldx + 8 * (tid & 7);
+    xslot[i] = (tid & 7) * ROWS + (((tid >> 3) + 32 * i) ^ (tid & 7));
+  }
   auto load_x = [&](int j) {
     const int64_t k = (int64_t)j * kBlockK + 8 * (tid & 7);
     if ((int64_t)(j + 1) * kBlockK <= a.k_in) {
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int row = min((tid >> 3) + 32 * i, a.m - 1);
-        xr[i] = *(const uint4*)(a.x + (int64_t)row * a.ldx + k);
-      }
+      for (int i = 0; i < RB; ++i) xr[i] = *(const uint4*)(xrow[i] + (int64_t)j * kBlockK);
     } else {
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
@@ -659,9 +664,8 @@ __global__ __launch_bounds__(256, TPW == 1 ? 2 : 1) void w12_wide_kernel(GemmArg
     }
   };
   auto store_x = [&](int buf) {
-    const int kg = tid & 7;
 #pragma unroll
-    for (int i = 0; i < RB; ++i) xs[buf][kg * ROWS + (((tid >> 3) + 32 * i) ^ kg)] = xr[i];
+    for (int i = 0; i < RB; ++i) xs[buf][xslot[i]] = xr[i];
   };
 
   // Escape offsets of a window of 64 blocks, one VGPR per tile (lane l:
