@@ -935,10 +935,16 @@ constexpr int kNumCUs = 256;
 // Per-CU cost, in K blocks, of `gsplit` groups cut into `s` K slices of
 // `kps` blocks (partial-sum epilogue): the busiest CU's blocks plus a fixed
 // cost per workgroup; a CU holding a single workgroup streams slower.
+#ifndef TVP_SLICE_FIXED
+#define TVP_SLICE_FIXED 4.0  // measured: 4 (down in 3 slices) beat 2 (8 slices) by 0.35% per verify step, 1 lost 1%
+#endif
+#ifndef TVP_SLICE_SINGLE
+#define TVP_SLICE_SINGLE 1.5
+#endif
 static double slice_cost(int gsplit, int s, int kps) {
   const int per_cu = (int)ceil_div((int64_t)gsplit * s, kNumCUs);
-  const double cost = (double)per_cu * kps + 2.0 * per_cu;
-  return per_cu <= 1 ? 1.5 * cost : cost;
+  const double cost = (double)per_cu * kps + TVP_SLICE_FIXED * per_cu;
+  return per_cu <= 1 ? TVP_SLICE_SINGLE * cost : cost;
 }
 
 // rem_ok: the epilogue can be finished by w12_rem_fixup_kernel (not argmax,
