@@ -509,6 +509,48 @@ def bench_batched(args, cfg) -> int:
     return 0
 
 
+def bench_cost_curve(args, cfg, dm) -> int:
+    """Verify cost against tree size: T(N) for best-first trees of N = 1, 8,
+    16, 32 nodes over the same context (random draft tokens; the pass does
+    the same work whatever is accepted), and c(N) = T(N) / T(1), where the
+    one-node pass is one step of greedy decoding."""
+    import torch
+
+    import tree_verification_pass_amd as tvp
+    from synth import best_first_topology
+
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(args.seed + 3)
+    times = {}
+    for n in (1, 8, 16, 32):
+        parents = best_first_topology(rng, n)[0] if n > 1 else np.asarray([-1])
+        tokens = rng.integers(0, cfg.vocab, n)
+        T = torch.as_tensor(np.asarray(tokens, np.int32), device=dev)
+        P = torch.as_tensor(np.asarray(parents, np.int32), device=dev)
+        out = tvp._alloc_out(dm.plan, n, 1, False)
+        for _ in range(args.warmup):
+            tvp.verify_step(dm.plan, cfg.ctx_len, T, P, commit=True, out=out)
+            int(out.n_accepted.item())
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            tvp.verify_step(dm.plan, cfg.ctx_len, T, P, commit=True, out=out)
+            int(out.n_accepted.item())  # each step's one readback
+        torch.cuda.synchronize()
+        times[n] = (time.perf_counter() - t0) * 1000.0 / args.steps
+        log(f"bench: N = {n:2d}: {times[n]:.3f} ms/step, c(N) = {times[n] / times[1]:.3f}")
+    line = {
+        "metric": "W12 verify cost curve c(N) = T(N)/T(1) (27B-like), 1 GPU",
+        "value": round(times[32] / times[1], 4), "unit": "c(32)", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "ms_per_step": {str(n): round(t, 4) for n, t in times.items()},
+        "c": {str(n): round(t / times[1], 4) for n, t in times.items()},
+        "config": {"workload": f"{cfg.name}-like verify step, best-first trees of 1-32 nodes, ctx {cfg.ctx_len}"},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -521,6 +563,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ar", action="store_true",
                     help="time W12 greedy autoregressive decoding instead (one node per pass, M = 1)")
+    ap.add_argument("--cost-curve", action="store_true",
+                    help="time the pass at 1, 8, 16 and 32 nodes instead and report c(N) = T(N)/T(1)")
     ap.add_argument("--batched", action="store_true",
                     help="time the batched pass instead (24 requests sharing a 192-node budget)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -564,6 +608,8 @@ def main() -> int:
     dm = build_model(cfg, args.seed, s_max, cfg.n_nodes)
     if args.ar:
         return bench_ar(args, cfg, dm)
+    if args.cost_curve:
+        return bench_cost_curve(args, cfg, dm)
     log("bench: drafting trees from the target's top-4")
     trees = make_trees(dm, cfg, args.trees, args.seed + 1)
     out = tvp._alloc_out(dm.plan, cfg.n_nodes, 1, False)
