@@ -142,9 +142,9 @@ int w12_pack(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hip
  *   y      device, [m][ldy] fp32 if y_fp32 else bf16 (ldy >= n_out); rows
  *          follow the canonical channel order whatever p->chan_map is
  *   ws     device scratch of w12_gemm_workspace() bytes.  Its first 256 KiB
- *          hold completion counters: they must be zero before the first call
- *          and every call leaves them zero; the rest is scratch.  Do not share
- *          one workspace between w12_gemm and other entry points.             */
+ *          are a reserved region (zero-filled by the caller before the first
+ *          call; no call changes it); the rest is scratch.  Do not share one
+ *          workspace between w12_gemm and other entry points.                 */
 size_t w12_gemm_workspace(int64_t m, const tvp_w12_packed* w);
 int w12_gemm(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w, void* y,
              int64_t ldy, int y_fp32, void* ws, size_t ws_bytes, hipStream_t stream);

@@ -5,8 +5,9 @@
 
 namespace tvp {
 
-// Zero region of a GEMM: completion counters (kGemmMaxGroups entries).
-// Zero on entry, left zero by every call.
+// Reserved region at the start of a GEMM's workspace (room for
+// kGemmMaxGroups 32-bit entries; the kernels reduce K splits in a following
+// launch and write nothing here).  Zero on entry, left zero by every call.
 constexpr size_t kGemmMaxGroups = 32768;
 constexpr size_t kGemmZeroBytes = 256 * 1024;
 static_assert(kGemmMaxGroups * 4 <= kGemmZeroBytes, "zero region");

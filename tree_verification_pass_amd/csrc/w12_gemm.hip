@@ -4,21 +4,23 @@
 // behind the weight stream; stream-K keeps it deterministic).
 //
 // MI355X design (not the page's Hopper kernel):
-//  * Each wavefront streams whole packed tile blocks (32 channels x 64 k =
-//    3072 B, lane-contiguous 16-byte loads), one or two tiles at a time, with
-//    the next step's records and escape entries prefetched while the current
-//    step is decoded and multiplied.
+//  * Skinny kernel (up to 32 rows): each wavefront streams whole packed tile
+//    blocks (32 channels x 64 k = 3072 B, lane-contiguous 16-byte loads) of
+//    one or two tiles through a register ring and reads its activation
+//    fragments from the packed activation layout (they stay in L2); a
+//    workgroup's wavefronts split K and meet in LDS in wavefront order.
+//  * Wide kernel (33..192 rows): a workgroup's four wavefronts walk the same
+//    K blocks, one tile each, and share each 64-column block of X through a
+//    double-buffered LDS tile.
 //  * Decode: 4 VALU ops per pair of weights (rotate, mask, byte spread, add)
 //    into bf16 halfwords; the decoded 32x64 tile goes through the wave's LDS
 //    scratch so escape values (about 1% of weights) are patched with one
 //    16-bit LDS store each, then the fragments feed v_mfma_f32_32x32x16_bf16
 //    (m > 16) or v_mfma_f32_16x16x32_bf16 (m <= 16).
-//  * X is staged through LDS in chunks of the workgroup's K range and shared
-//    by the 4 wavefronts (4 or 8 tiles), so activation traffic is a small
-//    fraction of the weight stream.
-//  * Split-K over workgroups; fp32 partials go to a workspace and the last
-//    workgroup of each tile group (atomic counter) reduces them in split order
-//    and applies the epilogue: results are bitwise reproducible.
+//  * K split over workgroups: fp32 partial sums go to the workspace and the
+//    next launch (a fix-up kernel, or the fused residual + RMSNorm) adds them
+//    in split order, so results are bitwise reproducible; no atomics and no
+//    device-scope fences.
 #include <math.h>
 
 #include <algorithm>
@@ -894,7 +896,8 @@ struct GemmPlan {
 // Work decomposition.  Skinny (m <= 32): one workgroup per TPW tiles whose KW
 // wavefronts split K (kbs <= 63 blocks each, so a wave's escape offsets fit
 // one VGPR).  Wide (m > 32, or K too long for 8 waves of 63 blocks):
-// workgroups of 4 tiles sharing X through LDS, split K over workgroups.
+// workgroups of 4 x kWideTPW tiles sharing X through LDS, split K over
+// workgroups (the splits finished by the next launch).
 constexpr int kWideMaxSplits = 32;
 #ifndef TVP_WIDE_SUM_WEIGHT
 #define TVP_WIDE_SUM_WEIGHT 0.5
@@ -1255,9 +1258,8 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
 
 using namespace tvp;
 
-// Standalone GEMM workspace: a fixed zero region (completion counters) so
-// that calls on tensors of different shapes sharing one workspace never find
-// another call's scratch where their counters live; then the scratch.
+// Standalone GEMM workspace: a fixed reserved region (kept for the layout
+// callers size; no kernel writes it), then the scratch.
 static size_t gemm_ws_layout(int64_t m, const tvp_w12_packed* w, size_t* off_scr, size_t* scr_bytes,
                              int* groups) {
   gemm_requirements(m, w, groups, scr_bytes);
