@@ -236,7 +236,7 @@ def cpu_baseline(dm, cfg, seed: int, tree):
     est = t_layer * cfg.streamed_params() / w_layer
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": 1.0 / est, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"1 of {cfg.n_layers} decoder layers of one 32-node verify step (W12 decode of its 4 "
+            "sample": (f"1 of {cfg.n_layers} decoder layers of one {len(tokens)}-node verify step (W12 decode of its 4 "
                        f"weights + fp64 forward, ctx {cfg.ctx_len}): {t_layer:.2f} s, scaled by streamed "
                        f"weights ({cfg.streamed_params() / w_layer:.2f}x) to a whole step of {est:.1f} s")}
 
