@@ -170,28 +170,39 @@ static void launch_norm(const float* P, int S, int64_t pstride, int ldp, uint16_
                                                                    ldy, packed);
 }
 
-// One workgroup per request; the walk is sequential over nodes (parents[i] < i).
+// One workgroup per request: its 64 threads stage the request's parents,
+// tokens and greedy tokens in LDS and validate the tree, then one thread
+// walks the nodes in order (parents[i] < i) from LDS.
 __global__ __launch_bounds__(64) void accept_kernel(const int32_t* __restrict__ argmax,
                                                     const int32_t* __restrict__ tokens,
                                                     const int32_t* __restrict__ parents, ReqInfo ri,
                                                     const int32_t* __restrict__ bad_token,
                                                     int32_t* __restrict__ path, int32_t* __restrict__ n_acc,
                                                     int32_t* __restrict__ bonus, int32_t* __restrict__ status) {
-  __shared__ int32_t depth[1024];
+  __shared__ int32_t par[1024], tok[1024], am[1024], depth[1024];
   __shared__ uint8_t okf[1024];
-  const int r = blockIdx.x;
-  if (threadIdx.x != 0) return;
+  __shared__ int bad_tree, bad_tok;
+  const int r = blockIdx.x, tid = threadIdx.x;
   const int nb = ri.node_ptr[r], n = ri.node_ptr[r + 1] - nb;
-  bool valid = n >= 1 && n <= 1024 && parents[nb] == -1;
-  for (int i = 1; valid && i < n; ++i) {
-    const int p = parents[nb + i];
-    valid = p >= 0 && p < i;
+  const bool sized = n >= 1 && n <= 1024;
+  if (tid == 0) {
+    bad_tree = sized ? 0 : 1;
+    bad_tok = 0;
   }
-  int st = valid ? TVP_OK : TVP_ERR_TREE;
-  if (valid && bad_token) {
-    for (int i = 0; i < n; ++i)
-      if (bad_token[nb + i]) st = TVP_ERR_ARG;
+  __syncthreads();
+  if (sized) {
+    for (int i = tid; i < n; i += 64) {
+      const int p = parents[nb + i];
+      par[i] = p;
+      tok[i] = tokens[nb + i];
+      am[i] = argmax[nb + i];
+      if (i == 0 ? p != -1 : (p < 0 || p >= i)) atomicOr(&bad_tree, 1);
+      if (bad_token && bad_token[nb + i]) atomicOr(&bad_tok, 1);
+    }
   }
+  __syncthreads();
+  if (tid != 0) return;
+  const int st = bad_tree ? TVP_ERR_TREE : (bad_tok ? TVP_ERR_ARG : TVP_OK);
   if (st != TVP_OK) {
     status[r] = st;
     n_acc[r] = 0;
@@ -207,19 +218,19 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t* __restrict__ 
   okf[0] = 1;
   int best = 0;
   for (int i = 1; i < n; ++i) {
-    const int p = parents[nb + i];
+    const int p = par[i];
     depth[i] = depth[p] + 1;
-    okf[i] = okf[p] && tokens[nb + i] == argmax[nb + p];
+    okf[i] = okf[p] && tok[i] == am[p];
     if (okf[i] && depth[i] > depth[best]) best = i;
   }
   const int a = depth[best];
   int v = best;
   for (int j = a; j >= 0; --j) {
     path[nb + j] = v;
-    v = j > 0 ? parents[nb + v] : 0;
+    v = j > 0 ? par[v] : 0;
   }
   n_acc[r] = a;
-  bonus[r] = argmax[nb + best];
+  bonus[r] = am[best];
   status[r] = TVP_OK;
 }
 
