@@ -248,7 +248,9 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(CacheTable ct, ReqInfo r
                                                         const int32_t* __restrict__ path,
                                                         const int32_t* __restrict__ n_acc,
                                                         const int32_t* __restrict__ status) {
-  __shared__ uint16_t buf[64 * 128];
+  constexpr int kBufVec = 1024;  // 16 KB of 16-byte pieces
+  __shared__ uint4 buf[kBufVec];
+  __shared__ int32_t src[64];     // source slot offset of accepted row j (<= 63 rows)
   const int r = blockIdx.x;
   const int layer = blockIdx.y >> 1, which = blockIdx.y & 1;
   if (status[r] != TVP_OK) return;
@@ -257,17 +259,25 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(CacheTable ct, ReqInfo r
   const int nb = ri.node_ptr[r];
   const int64_t base = (int64_t)r * s_req + ri.ctx_len[r];
   uint16_t* cache = which ? ct.vc[layer] : ct.kc[layer];
-  const int total = a * d;
-  for (int kh = 0; kh < hkv; ++kh) {
-    uint16_t* hc = cache + (int64_t)kh * s_stride * d;
-    for (int e = threadIdx.x; e < total; e += 256) {
-      const int j = 1 + e / d, dd = e % d;
-      buf[e] = hc[(base + path[nb + j]) * d + dd];
+  for (int j = threadIdx.x; j <= a; j += 256) src[j] = path[nb + j];
+  __syncthreads();
+  // Rows j = 1..a of as many heads as the buffer holds per round, in 16-byte
+  // pieces: every source row of the round is read before any is written
+  // (source and destination slots overlap).
+  const int vrow = d / 8, per_head = a * vrow;
+  const int hpr = max(1, min(hkv, kBufVec / per_head));
+  for (int h0 = 0; h0 < hkv; h0 += hpr) {
+    const int nv = min(hpr, hkv - h0) * per_head;
+    for (int e = threadIdx.x; e < nv; e += 256) {
+      const int hh = e / per_head, rem = e % per_head, j = 1 + rem / vrow, c = rem % vrow;
+      const uint4* hc = (const uint4*)(cache + (int64_t)(h0 + hh) * s_stride * d);
+      buf[e] = hc[(base + src[j]) * vrow + c];
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < total; e += 256) {
-      const int j = 1 + e / d, dd = e % d;
-      hc[(base + j) * d + dd] = buf[e];
+    for (int e = threadIdx.x; e < nv; e += 256) {
+      const int hh = e / per_head, rem = e % per_head, j = 1 + rem / vrow, c = rem % vrow;
+      uint4* hc = (uint4*)(cache + (int64_t)(h0 + hh) * s_stride * d);
+      hc[(base + j) * vrow + c] = buf[e];
     }
     __syncthreads();
   }
