@@ -35,7 +35,12 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   const bool ok = t >= 0 && t < vocab;
   if (threadIdx.x == 0) bad[i] = ok ? 0 : 1;
   const uint16_t* src = embed + (int64_t)(ok ? t : 0) * hidden;
-  for (int k = threadIdx.x; k < hidden; k += 256) h[(int64_t)i * ldh + k] = src[k];
+  uint16_t* dst = h + (int64_t)i * ldh;
+  if (((uintptr_t)embed % 16) == 0 && hidden % 8 == 0 && ldh % 8 == 0) {  // 16-byte pieces
+    for (int c = threadIdx.x; c < hidden / 8; c += 256) ((uint4*)dst)[c] = ((const uint4*)src)[c];
+  } else {
+    for (int k = threadIdx.x; k < hidden; k += 256) dst[k] = src[k];
+  }
 }
 
 // Residual update fused with the next RMSNorm, one workgroup per row:
