@@ -554,8 +554,8 @@ def bench_cost_curve(args, cfg, dm) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="27b")
     ap.add_argument("--trees", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
@@ -629,11 +629,14 @@ def main() -> int:
     log(f"bench: timing {args.steps} steps")
     acc = []
     enq.clear()
+    per_step = []  # wall time of each step (each ends in its readback)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
     for i in range(args.steps):
+        ts = time.perf_counter()
         acc.append(step(i))
+        per_step.append((time.perf_counter() - ts) * 1000.0)
     ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -666,6 +669,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_p10_median_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
         "device_ms_per_step": round(dev_ms, 4),
         "host_enqueue_ms_per_step": round(enq_ms, 4),
         "higher_is_better": True,
