@@ -7,7 +7,7 @@ target model checks every drafted token in a single forward pass; section
 flips caused by a different floating-point reduction order (GEMM tiling, tree
 attention), so the definition is ordinary bf16 greedy decoding.
 
-Definition used here (the plainest reading, listed in the design doc): for every
+Definition used here (the plainest reading of the pages): for every
 tree node ``v`` the logits are the target's next-token logits after the
 sequence ``context + tokens on the root-to-v path``, i.e. ordinary causal
 attention along that path.  ``forward_tree`` computes all nodes in one pass

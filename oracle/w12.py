@@ -7,7 +7,7 @@ sign, its exponent as a 4-bit offset from the window's lowest exponent, and
 its 7 mantissa bits.  Everything else -- values outside the window, zeros and
 subnormals -- is kept exactly in a per-channel sparse list of escapes.
 
-Readings of points the page leaves open (each listed in the design doc):
+Readings of points the page leaves open (the plainest ones the rest supports):
 
 * a channel is one row of the ``[out, in]`` weight (an output channel);
 * the window ``[base, base+15]`` covers normal exponents only, so
