@@ -20,11 +20,11 @@ SKINNY_LAYER = ["void tvp::w12_skinny_kernel<32, 1, 3, 4>(tvp::GemmArgs)",
                 "void tvp::w12_rem_fixup_kernel<3>(tvp::GemmArgs)",
                 "void tvp::w12_skinny_kernel<32, 1, 3, 16>(tvp::GemmArgs)",
                 "tvp::resid_norm_kernel(float const*)"]
-WIDE_LAYER = ["void tvp::w12_wide_kernel<6, 1, 4>(tvp::GemmArgs)", "tvp::w12_wide_fixup_kernel(tvp::GemmArgs)",
+WIDE_LAYER = ["void tvp::w12_wide_kernel<6, 1, 3>(tvp::GemmArgs)", "tvp::w12_wide_fixup_kernel(tvp::GemmArgs)",
               "void tvp::tree_attn_kernel<128, 2>(tvp::AttnArgs)",
-              "void tvp::w12_wide_kernel<6, 1, 4>(tvp::GemmArgs)", "tvp::resid_norm_kernel(float const*)",
-              "void tvp::w12_wide_kernel<6, 1, 4>(tvp::GemmArgs)", "tvp::w12_wide_fixup_kernel(tvp::GemmArgs)",
-              "void tvp::w12_wide_kernel<6, 1, 4>(tvp::GemmArgs)", "tvp::resid_norm_kernel(float const*)"]
+              "void tvp::w12_wide_kernel<6, 1, 3>(tvp::GemmArgs)", "tvp::resid_norm_kernel(float const*)",
+              "void tvp::w12_wide_kernel<6, 1, 3>(tvp::GemmArgs)", "tvp::w12_wide_fixup_kernel(tvp::GemmArgs)",
+              "void tvp::w12_wide_kernel<6, 1, 3>(tvp::GemmArgs)", "tvp::resid_norm_kernel(float const*)"]
 HEAD = ["tvp::tree_prep_kernel(int const*)", "tvp::rope_table_kernel(int const*)", "tvp::embed_kernel(int const*)",
         "tvp::resid_norm_kernel(float const*)"]
 
@@ -58,7 +58,7 @@ def test_skinny_pass_roles(tmp_path):
 
 
 def test_wide_pass_roles(tmp_path):
-    tail = ["void tvp::w12_wide_kernel<6, 1, 4>(tvp::GemmArgs)", "tvp::w12_wide_fixup_kernel(tvp::GemmArgs)",
+    tail = ["void tvp::w12_wide_kernel<6, 1, 3>(tvp::GemmArgs)", "tvp::w12_wide_fixup_kernel(tvp::GemmArgs)",
             "tvp::argmax_finalize_kernel(x)", "tvp::accept_kernel(x)"]
     roles = bench.pass_roles(_trace(tmp_path, HEAD + WIDE_LAYER * 2 + tail))
     assert {r: len(v) for r, v in roles.items()} == {
