@@ -11,14 +11,14 @@ import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-SKINNY_LAYER = ["void tvp::w12_skinny_kernel<32, 1, 3, 4>(tvp::GemmArgs)",
+SKINNY_LAYER = ["void tvp::w12_skinny_kernel<32, 1, 2, 4>(tvp::GemmArgs)",
                 "void tvp::tree_attn_kernel<128, 2>(tvp::AttnArgs)",
                 "void tvp::tree_attn_merge_kernel<128>(tvp::AttnArgs)",
-                "void tvp::w12_skinny_kernel<32, 1, 3, 16>(tvp::GemmArgs)",
+                "void tvp::w12_skinny_kernel<32, 1, 2, 16>(tvp::GemmArgs)",
                 "tvp::resid_norm_kernel(float const*)",
                 "void tvp::w12_skinny_kernel<32, 2, 2, 3>(tvp::GemmArgs)",
                 "void tvp::w12_rem_fixup_kernel<3>(tvp::GemmArgs)",
-                "void tvp::w12_skinny_kernel<32, 1, 3, 16>(tvp::GemmArgs)",
+                "void tvp::w12_skinny_kernel<32, 1, 2, 16>(tvp::GemmArgs)",
                 "tvp::resid_norm_kernel(float const*)"]
 WIDE_LAYER = ["void tvp::w12_wide_kernel<6, 1, 3>(tvp::GemmArgs)", "tvp::w12_wide_fixup_kernel(tvp::GemmArgs)",
               "void tvp::tree_attn_kernel<128, 2>(tvp::AttnArgs)",
