@@ -75,27 +75,26 @@ __global__ __launch_bounds__(kNormThreads) void resid_norm_kernel(const float* _
     w[0] = v.x, w[1] = v.y, w[2] = v.z, w[3] = v.w;
     if (S > 0) {
       float acc[8];
-      int sl = 0;
-      for (; sl + 8 <= S; sl += 8) {  // 16 independent loads in flight, added in slice order
+      // up to 8 slices per round: all their loads (16 in flight) are issued
+      // before the first add, also when fewer than 8 remain; added in slice order
+      for (int sl = 0; sl < S; sl += 8) {
+        const int cnt = min(8, S - sl);
         float4 q0[8], q1[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          q0[j] = *(const float4*)(pr + (sl + j) * pstride + 8 * c);
-          q1[j] = *(const float4*)(pr + (sl + j) * pstride + 8 * c + 4);
+          if (j < cnt) {
+            q0[j] = *(const float4*)(pr + (sl + j) * pstride + 8 * c);
+            q1[j] = *(const float4*)(pr + (sl + j) * pstride + 8 * c + 4);
+          }
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float pv[8] = {q0[j].x, q0[j].y, q0[j].z, q0[j].w, q1[j].x, q1[j].y, q1[j].z, q1[j].w};
+          if (j < cnt) {
+            const float pv[8] = {q0[j].x, q0[j].y, q0[j].z, q0[j].w, q1[j].x, q1[j].y, q1[j].z, q1[j].w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = (sl + j) == 0 ? pv[e] : acc[e] + pv[e];
+            for (int e = 0; e < 8; ++e) acc[e] = (sl + j) == 0 ? pv[e] : acc[e] + pv[e];
+          }
         }
-      }
-      for (; sl < S; ++sl) {
-        const float4 q0 = *(const float4*)(pr + sl * pstride + 8 * c);
-        const float4 q1 = *(const float4*)(pr + sl * pstride + 8 * c + 4);
-        const float pv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = sl == 0 ? pv[e] : acc[e] + pv[e];
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
