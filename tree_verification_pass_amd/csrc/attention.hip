@@ -7,7 +7,7 @@
 // of the places where reduction order may flip near-ties.
 //
 // Design: per (request, kv head, 32-row block, key split) one workgroup of
-// four wavefronts.  A row is (query head kv_head*G + gq, node i) at row
+// eight wavefronts.  A row is (query head kv_head*G + gq, node i) at row
 // gq * n + i.  Each wavefront streams its own 32-key blocks of the split
 // through its own LDS tiles (fully coalesced 16-byte loads, K and V
 // row-major, XOR-swizzled per row), with the next blocks in flight in
@@ -16,7 +16,7 @@
 // node's 64-bit ancestor mask and folded into an online softmax; P V is
 // accumulated with the same MFMA, its V^T operand read straight from the
 // row-major V tile with the LDS transpose read (ds_read_b64_tr_b16), and P
-// applied as a sum of two bf16 pieces.  The four wavefronts' (max, sum, O)
+// applied as a sum of two bf16 pieces.  The wavefronts' (max, sum, O)
 // are combined in LDS in a fixed order; with several splits, each split's
 // (max, sum, O) goes out in the accumulator's register layout (coalesced
 // 256-byte stores) and a separate merge launch sums them in split order, so
