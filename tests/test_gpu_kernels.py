@@ -93,7 +93,7 @@ def _check_gemm(y_fp32: np.ndarray, x_bits: np.ndarray, w_bits: np.ndarray):
     return ref
 
 
-@pytest.mark.parametrize("m", [1, 5, 16, 17, 32, 33, 100, 192])
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 32, 33, 100, 129, 160, 192])
 def test_gemm_ragged_shapes(tvp, cuda, m):
     w_bits = bf16_bits_numpy(gen_linear_bf16(make_generator(8), 1000, 1000, TINY_RECIPE))
     print(f"[gemm] m={m} n=1000 k=1000", flush=True)
