@@ -925,6 +925,9 @@ constexpr int kWideRDBig = TVP_WIDE_RD_BIG;  // ... above 128 rows (one tile per
 #define TVP_WAVES_PER_CU 12
 #endif
 constexpr int kWavesPerCU = TVP_WAVES_PER_CU;  // skinny kernel: three wavefronts per SIMD (136-156 VGPRs)
+#ifndef TVP_KW_ONE_ROUND
+#define TVP_KW_ONE_ROUND 8  // waves per workgroup when every workgroup has a CU to itself (4 measured 0.9% slower per verify step)
+#endif
 #ifndef TVP_RD1
 #define TVP_RD1 2  // register-ring depth, one tile per workgroup (106 VGPRs; 3 measured 1.4% slower per verify step)
 #endif
@@ -990,6 +993,7 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
     // of a CU's workgroups stream together instead of in two rounds; more
     // when a wave would exceed 63 blocks.
     p.KW = (int)ceil_div(nwg, kNumCUs) * 4 > kWavesPerCU ? 2 : 4;
+    if (nwg <= kNumCUs) p.KW = TVP_KW_ONE_ROUND;  // one workgroup per CU at most
     while (p.KW < 8 && ceil_div(krange, p.KW) > 63) p.KW *= 2;
     p.KW = std::max(1, std::min(p.KW, std::max(krange, 1)));
     p.kbs = nkb > 0 ? (int)ceil_div(nkb, p.KW) : 0;
