@@ -14,7 +14,8 @@
  * Conventions for every entry point:
  *   - Pointers named in comments as "device" point to GPU memory; "host" to
  *     CPU memory.  All device buffers are owned by the caller; the library
- *     never allocates device memory (scratch comes in through `ws`).
+ *     never allocates device memory (scratch comes in through `ws`, and no
+ *     workspace needs any initial contents).
  *   - Work is enqueued on `stream` and is complete when the stream is.  Only
  *     w12_encode_count and w12_pack synchronise (documented there).
  *   - Shapes, nulls and capacities are validated on the host before anything
@@ -93,7 +94,22 @@ int w12_encode(const uint16_t* w, const tvp_w12* t, hipStream_t stream);
 /* Exact decode back to bf16 bits, device `out` [n_out][k_in] (test hook). */
 int w12_decode(const tvp_w12* t, uint16_t* out, hipStream_t stream);
 
+/* Checks the side data of a canonical W12 tensor given in HOST memory:
+ * base[n_out], esc_ptr[n_out+1], esc_idx[n_esc] (SpecPilot summary, section
+ * 무엇과 다른가: a per-channel window and a per-channel escape list; the
+ * window of normal exponents fixes 1 <= base <= 239).  TVP_ERR_FORMAT when a
+ * base is outside 1..239, esc_ptr does not run from 0 up to n_esc without
+ * decreasing, or a channel's escape columns are not strictly ascending and
+ * below k_in (or k_in > 65536); TVP_ERR_ARG on a negative size or a null
+ * array that is needed.  Pure host code: no HIP call, no allocation beyond
+ * the stack.  w12_pack runs the same check before it launches anything. */
+int w12_validate(const uint8_t* base, const uint32_t* esc_ptr, const uint16_t* esc_idx, int64_t n_out,
+                 int64_t k_in, int64_t n_esc);
+
 /* -------------------------------------------------- packed (GPU) W12 layout
+ * SpecPilot summary, section 무엇과 다른가: the GEMM decodes W12 records in
+ * registers behind the weight stream.  The records keep the canonical bits;
+ * only their order in memory is chosen here, for that stream.
  * The GEMM streams W12 from a tiled copy of the same records: tiles of 32
  * channels x 64 k, each 3072 contiguous bytes laid out in the order the
  * 64 lanes of a wavefront load and decode them, plus per-tile-block escape
@@ -126,9 +142,11 @@ int w12_pack_size(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, 
                   int32_t map_b, int32_t map_c, tvp_w12_packed* p);
 
 /* Builds the packed copy of canonical tensor `t` into p->blob (p from
- * w12_pack_size with p->blob set).  Device scratch `ws` of
- * w12_pack_workspace() bytes.  Synchronises `stream` once (the channel map
- * is uploaded from host memory). */
+ * w12_pack_size with p->blob set), part of the offline conversion of the
+ * model (SpecPilot summary, section 무엇과 다른가).  Device scratch `ws` of
+ * w12_pack_workspace() bytes.  Synchronises `stream`: the tensor's side data
+ * is first checked on the host as w12_validate does (TVP_ERR_FORMAT, nothing
+ * launched), then the channel map is uploaded. */
 size_t w12_pack_workspace(int64_t n_out, int64_t k_in);
 int w12_pack(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -141,10 +159,9 @@ int w12_pack(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hip
  *   x      device bf16 [m][ldx], 16-byte aligned, ldx >= k_in, ldx % 8 == 0
  *   y      device, [m][ldy] fp32 if y_fp32 else bf16 (ldy >= n_out); rows
  *          follow the canonical channel order whatever p->chan_map is
- *   ws     device scratch of w12_gemm_workspace() bytes.  Its first 256 KiB
- *          are a reserved region (zero-filled by the caller before the first
- *          call; no call changes it); the rest is scratch.  Do not share one
- *          workspace between w12_gemm and other entry points.                 */
+ *   ws     device scratch of w12_gemm_workspace() bytes (any contents; a
+ *          call may overwrite all of it).  Calls that share a workspace must
+ *          not overlap in time.                                               */
 size_t w12_gemm_workspace(int64_t m, const tvp_w12_packed* w);
 int w12_gemm(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w, void* y,
              int64_t ldy, int y_fp32, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -185,7 +202,8 @@ int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed*
                 const tvp_gemm_epilogue* epi, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Packed activation layout, the GEMM's input format for up to 32 rows (and
- * what verify_step produces internally): bf16 element (row, k) lives at
+ * what verify_step produces internally; the pages leave the activation
+ * layout open, so it is chosen for the GEMM's MFMA operand loads): bf16 element (row, k) lives at
  * (k/8)*256 + row*8 + k%8, so a wavefront's MFMA A-fragment of 32 rows x 8
  * columns is 512 contiguous bytes.  k is padded to a multiple of 64:
  * w12_packed_x_elems(k_in) elements.  w12_pack_x converts row-major
@@ -210,8 +228,7 @@ int w12_pack_x(const uint16_t* x, int64_t m, int64_t ldx, int64_t k_in, uint16_t
  *   out      device bf16 [n][hq][d]
  *   status   device int32 [1]: TVP_OK or TVP_ERR_TREE (then out is zero)
  * n <= 64, d in {64, 128}, hq % hkv == 0, n * hq / hkv <= 256.
- * ws: tree_attention_workspace() bytes, its first 256 bytes zero before the
- * first call (left zero); not shared with other entry points.                */
+ * ws: tree_attention_workspace() bytes of device scratch (any contents).     */
 size_t tree_attention_workspace(int32_t n, int32_t hq, int32_t d, int32_t max_keys);
 int tree_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                    int64_t s_stride, int32_t ctx_len, const int32_t* parents, int32_t n, int32_t hq,
@@ -257,13 +274,19 @@ typedef struct tvp_model_desc {
 typedef struct tvp_plan tvp_plan;
 
 /* Validates the description and builds host state for trees of up to
- * max_nodes nodes in total (all requests of a batch together, <= 192). */
+ * max_nodes nodes in total (all requests of a batch together, <= 192): the
+ * target model whose forward pass verifies every draft-tree token at once
+ * (SpecPilot summary, section 무엇인가), its weights already converted to
+ * packed W12 (section 무엇과 다른가), and one KV cache per layer.  Device
+ * pointers in `desc` are stored, not dereferenced; the plan owns host memory
+ * only.  TVP_ERR_SHAPE / TVP_ERR_FORMAT / TVP_ERR_ARG / TVP_ERR_CAPACITY on
+ * an inconsistent description. */
 int tvp_plan_create(const tvp_model_desc* desc, int32_t max_nodes, tvp_plan** plan);
 void tvp_plan_destroy(tvp_plan* plan);
 
-/* Device scratch needed by verify_step / verify_step_batched on this plan.
- * It must be zero-filled before its first use; its counter region is left
- * zero by every call.  Use it for this plan only. */
+/* Device scratch needed by verify_step / verify_step_batched on this plan
+ * (any contents; every call overwrites what it uses).  Calls sharing a
+ * workspace must not overlap in time. */
 size_t verify_step_workspace(const tvp_plan* plan);
 
 typedef struct tvp_verify_out {
@@ -276,7 +299,9 @@ typedef struct tvp_verify_out {
 } tvp_verify_out;
 
 /* One verification pass of draft tree (tokens, parents) after ctx_len
- * committed tokens: every node's next-token logits in one forward pass
+ * committed tokens -- SpecPilot summary, section 무엇인가 (every draft token
+ * goes through the target in one forward pass) and section 무엇과 다른가
+ * (the pass returns the matched path plus a bonus token): every node's next-token logits in one forward pass
  * (node i at position ctx_len + depth(i), its K/V written to cache slot
  * ctx_len + i), greedy acceptance, and -- if `commit` -- the accepted nodes'
  * K/V moved to slots ctx_len .. ctx_len + n_accepted, so the next committed
@@ -307,9 +332,10 @@ int verify_step_batched(tvp_plan* plan, int32_t n_req, const int32_t* ctx_len,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------- measurement
- * Streaming-read probe for the roofline (the measurement asks for each rate
- * as a fraction of both the nominal HBM bandwidth and a read stream measured
- * on the same GPU).  Reads the first bytes/16*16 bytes of src once, as a
+ * Streaming-read probe: the HBM read rate a plain sequential stream reaches
+ * on this GPU, the practical ceiling the weight stream of the pass (SpecPilot
+ * summary, section 무엇인가: most of a step is reading the target's weights)
+ * is compared against, next to the nominal bandwidth.  Reads the first bytes/16*16 bytes of src once, as a
  * plain sequential stream, and writes 4096 words to sink.  Nothing else is
  * touched; time it with events on `stream`.
  *   src   device, 16-byte aligned, >= 16 bytes (caller-owned)

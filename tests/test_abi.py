@@ -62,3 +62,57 @@ def test_packed_activation_size_host_only():
     # 32 row slots x k padded to a multiple of 64
     for k, want in ((0, 0), (1, 2048), (64, 2048), (65, 4096), (5120, 80 * 2048), (17408, 272 * 2048)):
         assert tvp.w12_packed_x_elems(k) == want
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_w12_validate_host_only():
+    """The library's host-side format check of a canonical tensor's side data
+    accepts what the oracle's encoder writes and rejects each kind of damage:
+    a window base outside 1..239, escape pointers that do not run from 0 to
+    n_esc without decreasing, escape columns out of order or past k_in."""
+    import numpy as np
+
+    import tree_verification_pass_amd as tvp
+    from oracle import w12 as ow12
+    from synth import gen_linear_bf16, make_generator
+    from synth.configs import TINY_RECIPE
+    from synth.weights import bf16_bits_numpy
+
+    k = 300
+    t = ow12.encode(bf16_bits_numpy(gen_linear_bf16(make_generator(11), 40, k, TINY_RECIPE)))
+    assert t.n_esc > 40  # several escapes per channel on this recipe
+    ok = lambda b, p, i, kk=k: tvp.w12_validate(b, p, i, kk)  # noqa: E731
+    assert ok(t.base, t.esc_ptr, t.esc_idx) == tvp.TVP_OK
+    # the all-patterns channel: base 1, 61440 escapes, columns up to 65535
+    allpat = np.random.default_rng(7).permutation(65536).astype(np.uint16)[None, :]
+    ta = ow12.encode(allpat)
+    assert ok(ta.base, ta.esc_ptr, ta.esc_idx, 65536) == tvp.TVP_OK
+    bad = []
+    for b in (0, 240, 255):
+        base = t.base.copy()
+        base[7] = b
+        bad.append((base, t.esc_ptr, t.esc_idx, k))
+    p = t.esc_ptr.copy()
+    p[0] = 1
+    bad.append((t.base, p, t.esc_idx, k))
+    p = t.esc_ptr.copy()
+    p[-1] -= 1
+    bad.append((t.base, p, t.esc_idx, k))
+    p = t.esc_ptr.copy()
+    j = int(np.flatnonzero(np.diff(p.astype(np.int64)) >= 2)[0])  # a channel with >= 2 escapes
+    p[j + 1], p[j + 2] = p[j + 2] + 1, p[j + 1]  # decreasing pair inside the CSR
+    bad.append((t.base, p, t.esc_idx, k))
+    i = t.esc_idx.copy()
+    a = int(t.esc_ptr[j])
+    i[a], i[a + 1] = i[a + 1], i[a]  # two columns of one channel swapped
+    bad.append((t.base, t.esc_ptr, i, k))
+    i = t.esc_idx.copy()
+    i[a + 1] = i[a]  # a repeated column
+    bad.append((t.base, t.esc_ptr, i, k))
+    i = t.esc_idx.copy()
+    last = int(t.esc_ptr[j + 1]) - 1
+    i[last] = k  # past the last column
+    bad.append((t.base, t.esc_ptr, i, k))
+    bad.append((t.base, t.esc_ptr, t.esc_idx, 70000))  # k_in beyond uint16 columns
+    for case in bad:
+        assert ok(*case) == tvp.TVP_ERR_FORMAT

@@ -336,6 +336,34 @@ def test_tree_attention_chain_equals_causal_and_star(tvp, cuda):
         assert np.all(np.abs(got - ref) <= 2.0 ** -8 * vmax + 2.0 ** -7 * np.abs(ref))
 
 
+@pytest.mark.parametrize("n,hq,hkv,d,L,spare", [(32, 40, 8, 128, 4064, 0), (7, 8, 2, 64, 250, 0),
+                                                (13, 6, 2, 128, 500, 9)])
+def test_tree_attention_never_reads_past_the_keys(tvp, cuda, n, hq, hkv, d, L, spare):
+    """Caches whose slots from ctx_len + n on hold NaN (spare > 0), and caches
+    filled exactly to their capacity (ctx_len + n == s_stride) that sit in a
+    larger NaN-filled allocation: no key at or past the last tree slot may
+    contribute (the ragged last block of a split is read as zeros), so the
+    output is finite and equals the oracle."""
+    print(f"[tree_attention bounds] n={n} hq={hq} hkv={hkv} d={d} L={L} spare={spare}", flush=True)
+    parents, q, kc0, vc0 = _attn_case(cuda, n, hq, hkv, d, L, seed=3 * n + L)
+    s = L + n + spare
+    pad = 4096 * d
+    caches = []
+    for src in (kc0, vc0):
+        flat = torch.full((hkv * s * d + pad,), float("nan"), dtype=torch.bfloat16, device=cuda)
+        view = flat[: hkv * s * d].view(hkv, s, d)
+        view[:, : L + n] = src[:, : L + n].to(cuda)
+        caches.append((flat, view))
+    (kf, kc), (vf, vc) = caches
+    out, st = tvp.tree_attention(q.to(cuda), kc, vc, L, torch.as_tensor(parents, device=cuda))
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    got = from_bits(_u16(out))
+    assert np.isfinite(got).all()
+    ref, vmax = _attn_ref(parents, q, kc0, vc0, L)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * vmax + 2.0 ** -7 * np.abs(ref)), float(np.abs(got - ref).max())
+
+
 def test_tree_attention_malformed_tree_status(tvp, cuda):
     _, q, kc, vc = _attn_case(cuda, 4, 4, 4, 64, 10, seed=1, parents=np.array([-1, 0, 1, 2]))
     bad = torch.as_tensor(np.array([-1, 0, 3, 1], dtype=np.int32), device=cuda)
@@ -441,6 +469,27 @@ def test_host_validation_launches_nothing(tvp, cuda):
     with pytest.raises(tvp.TvpError) as e:
         tvp.w12_gemm_px(xp, 4, pw, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_F32, y=y.data_ptr(), ldy=64, y_packed=1))
     assert e.value.status == tvp.TVP_ERR_ARG
+    # a malformed canonical tensor is refused by the packer before any launch
+    w = torch.from_numpy(bf16_bits_numpy(gen_linear_bf16(make_generator(2), 64, 200, TINY_RECIPE)).view(np.int16)
+                         .copy()).view(torch.bfloat16).to(cuda)
+    t = tvp.w12_encode(w)
+    assert t.n_esc >= 2
+    for damage in ("base", "order", "column"):
+        t2 = tvp.W12Tensor(t.n_out, t.k_in, t.n_esc, t.hi, t.lo, t.base.clone(), t.esc_ptr, t.esc_idx.clone(),
+                           t.esc_val)
+        if damage == "base":
+            t2.base[5] = 240
+        elif damage == "order":
+            i = t2.esc_idx.cpu().numpy().view(np.uint16).copy()
+            ptr = t.esc_ptr.cpu().numpy()
+            r = int(np.flatnonzero(np.diff(ptr) >= 2)[0])
+            i[ptr[r]], i[ptr[r] + 1] = i[ptr[r] + 1], i[ptr[r]]
+            t2.esc_idx.copy_(torch.from_numpy(i.view(np.int16)))
+        else:
+            t2.esc_idx[0] = 200
+        with pytest.raises(tvp.TvpError) as e:
+            tvp.w12_pack(t2)
+        assert e.value.status == tvp.TVP_ERR_FORMAT, damage
 
 
 def test_read_probe_reads_every_word_once(tvp, cuda):

@@ -90,6 +90,7 @@ _lib_w12_encode_count = _sig("w12_encode_count", ctypes.c_int,
                              [c_vp, c_i64, c_i64, c_vp, c_vp, ctypes.POINTER(c_i64), c_vp])
 _lib_w12_encode = _sig("w12_encode", ctypes.c_int, [c_vp, ctypes.POINTER(TvpW12), c_vp])
 _lib_w12_decode = _sig("w12_decode", ctypes.c_int, [ctypes.POINTER(TvpW12), c_vp, c_vp])
+_lib_w12_validate = _sig("w12_validate", ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64])
 _lib_w12_pack_size = _sig("w12_pack_size", ctypes.c_int,
                           [c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(TvpW12Packed)])
 _lib_w12_pack_workspace = _sig("w12_pack_workspace", c_sz, [c_i64, c_i64])
@@ -120,7 +121,7 @@ _lib_verify_step_batched = _sig("verify_step_batched", ctypes.c_int,
                                  c_i32, ctypes.POINTER(TvpVerifyOut), c_vp, c_sz, c_vp])
 _lib_tvp_read_probe = _sig("tvp_read_probe", ctypes.c_int, [c_vp, c_sz, c_vp, c_vp])
 
-EXPORTED = ("tvp_status_string", "w12_encode_count", "w12_encode", "w12_decode", "w12_pack_size",
+EXPORTED = ("tvp_status_string", "w12_encode_count", "w12_encode", "w12_decode", "w12_validate", "w12_pack_size",
             "w12_pack_workspace", "w12_pack", "w12_gemm_workspace", "w12_gemm", "w12_gemm_ex",
             "w12_packed_x_elems", "w12_pack_x",
             "tree_attention_workspace", "tree_attention", "accept_path", "tvp_plan_create",
@@ -153,8 +154,7 @@ def _dev_check(*ts: torch.Tensor) -> None:
 
 
 class _Workspace:
-    """Zero-filled device scratch reused across calls (the kernels leave their
-    counters at zero, so the buffer never needs clearing again)."""
+    """Device scratch reused across calls (no initial contents are needed)."""
 
     def __init__(self):
         self._bufs: Dict[int, torch.Tensor] = {}
@@ -164,12 +164,12 @@ class _Workspace:
         key = dev.index if dev.index is not None else torch.cuda.current_device()
         buf = self._bufs.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+            buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
             self._bufs[key] = buf
         return buf
 
 
-# one pool per entry point: each keeps its own zero counter region
+# one pool per entry point
 _ws_gemm = _Workspace()
 _ws_attn = _Workspace()
 
@@ -230,6 +230,25 @@ def w12_decode(t: W12Tensor) -> torch.Tensor:
     s = t.struct()
     _check(_lib_w12_decode(ctypes.byref(s), _ptr(out), _stream(t.hi.device)), "w12_decode")
     return out
+
+
+def w12_validate(base, esc_ptr, esc_idx, k_in: int) -> int:
+    """Host-side format check of a canonical tensor's side data (numpy arrays
+    or CPU tensors: base uint8 [n], esc_ptr uint32/int32 [n+1], esc_idx
+    uint16/int16 [n_esc]).  Returns the status code (TVP_OK or TVP_ERR_FORMAT)."""
+    import numpy as np
+
+    b = np.ascontiguousarray(np.asarray(base).astype(np.uint8, copy=False))
+    p = np.ascontiguousarray(np.asarray(esc_ptr).view(np.uint32) if np.asarray(esc_ptr).dtype.itemsize == 4
+                             else np.asarray(esc_ptr).astype(np.uint32))
+    i = np.ascontiguousarray(np.asarray(esc_idx).view(np.uint16) if np.asarray(esc_idx).dtype.itemsize == 2
+                             else np.asarray(esc_idx).astype(np.uint16))
+    n = int(b.size)
+    if p.size != n + 1:
+        raise ValueError("esc_ptr needs n_out + 1 entries")
+    n_esc = int(i.size)
+    return int(_lib_w12_validate(b.ctypes.data_as(c_vp), p.ctypes.data_as(c_vp),
+                                 i.ctypes.data_as(c_vp) if n_esc else None, n, int(k_in), n_esc))
 
 
 @dataclass
@@ -375,7 +394,7 @@ class Plan:
         self.max_nodes = max_nodes
         self.ws_bytes = int(_lib_verify_step_workspace(h))
         self.device = keepalive[0].device if keepalive else torch.device("cuda")
-        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
 
     def __del__(self):
         h = getattr(self, "handle", None)

@@ -122,7 +122,8 @@ __device__ inline float xor32_sum(float x) {
 }
 
 // Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle):
-// loads past num_records return zero.
+// a load whose per-lane offset (plus the instruction's immediate offset)
+// reaches num_records returns zero without touching memory.
 constexpr int kBufWord3 = 0x00020000;
 
 // Compiler fence for one wavefront's LDS accesses (they complete in order).
@@ -211,23 +212,27 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
   // range ends at the split's last key: keys past it (the split's ragged end,
   // or a whole placeholder block past the wavefront's last) read as zero
   // without touching memory, their scores are masked, and every path keeps
-  // the same number of loads in flight.  K arrives directly in the MFMA
+  // the same number of loads in flight.  The block's byte offset is part of
+  // the per-lane offset, which is the operand the hardware checks against the
+  // range (the scalar offset operand is not checked), so no key at or past
+  // the split's end is ever fetched.  K arrives directly in the MFMA
   // A-operand layout (lane: key lane % 32, 16-byte piece 2 ds + h of its
   // row); V with CH consecutive lanes reading one 2*D-byte row, for the LDS
-  // tile.  Only the scalar block offset changes from block to block.
+  // tile.
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   u32x4_t kpre[NPF][PER], vpre[NPF][PER];
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, k1 * D * 2, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, k1 * D * 2, kBufWord3);
   const int koff = (lane & 31) * D * 2 + 16 * h;
   auto fetch = [&](int i, int st) __attribute__((always_inline)) {
-    const int soff = key0_of(i) * D * 2;
+    const int boff = key0_of(i) * D * 2;
+    const int kv = koff + boff, vv = 16 * lane + boff;
 #pragma unroll
     for (int ds = 0; ds < PER; ++ds)
-      kpre[st][ds] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 32 * ds, soff, 0));
+      kpre[st][ds] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, kv + 32 * ds, 0, 0));
 #pragma unroll
     for (int it = 0; it < PER; ++it)
-      vpre[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, 16 * lane + 1024 * it, soff, 0));
+      vpre[st][it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, vv + 1024 * it, 0, 0));
   };
   auto stash = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
@@ -625,12 +630,13 @@ size_t attention_scratch_bytes(int hkv, int G, int d, int r_max, int n_total, in
 
 using namespace tvp;
 
-// Standalone layout of the tree_attention workspace:
-//   [0, 256)        reserved
-//   [256, ...)      anc u64 [64], pos/slot i32 [64]
+// Standalone layout of the tree_attention workspace (no initial contents
+// needed):
+//   [0, 512)        anc u64 [64]
+//   [512, 1024)     pos/slot i32 [64] each
 //   then            attention partials
 static size_t ta_layout(int32_t n, int32_t hq, int32_t hkv, int32_t d, int32_t max_keys, size_t* off_part) {
-  const size_t off = align_up(256 + 64 * 8 + 2 * 64 * 4, 256);
+  const size_t off = align_up(64 * 8 + 2 * 64 * 4, 256);
   *off_part = off;
   const int G = hkv > 0 ? hq / hkv : 1;
   return off + attention_scratch_bytes(hkv, G, d, G * n, n, max_keys);
@@ -662,8 +668,8 @@ int tree_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v
   const size_t need = ta_layout(n, hq, hkv, d, ctx_len + n, &offp);
   if (!ws || ws_bytes < need) return TVP_ERR_WORKSPACE;
   uint8_t* w = (uint8_t*)ws;
-  uint64_t* anc = (uint64_t*)(w + 256);
-  int32_t* pos = (int32_t*)(w + 256 + 64 * 8);
+  uint64_t* anc = (uint64_t*)w;
+  int32_t* pos = (int32_t*)(w + 64 * 8);
   int32_t* slot = pos + 64;
   ReqInfo ri{};
   ri.n_req = 1;

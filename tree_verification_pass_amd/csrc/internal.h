@@ -5,15 +5,12 @@
 
 namespace tvp {
 
-// Reserved region at the start of a GEMM's workspace (room for
-// kGemmMaxGroups 32-bit entries; the kernels reduce K splits in a following
-// launch and write nothing here).  Zero on entry, left zero by every call.
+// Largest number of channel groups one GEMM launch takes (grid sizes and the
+// argmax key slots stay well inside 32-bit indexing).
 constexpr size_t kGemmMaxGroups = 32768;
-constexpr size_t kGemmZeroBytes = 256 * 1024;
-static_assert(kGemmMaxGroups * 4 <= kGemmZeroBytes, "zero region");
 
-// W12 GEMM with caller-provided counters (`cnt`, groups entries) and scratch
-// (which also holds the argmax key slots).  Activations come row-major in `x` or, for
+// W12 GEMM with caller-provided scratch (which also holds the argmax key
+// slots).  Activations come row-major in `x` or, for
 // m <= 32, already in the packed layout in `xp` (then `x` is unused).
 // `y_packed`: the SwiGLU epilogue writes its output packed (m <= 32).
 // `ksplit` > 1 (skinny path, epilogue kEpiPartial only) also splits K over
@@ -22,7 +19,7 @@ static_assert(kGemmMaxGroups * 4 <= kGemmZeroBytes, "zero region");
 // (cos, sin) of pos[r] * theta^(-2i/d) at rope_cs[2 * (r * d/2 + i)] -- the
 // values the epilogue would otherwise compute itself, formed once per pass.
 int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
-             const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, void* scratch, size_t scratch_bytes,
+             const tvp_gemm_epilogue* epi, int y_packed, void* scratch, size_t scratch_bytes,
              hipStream_t stream, int ksplit = 1, const float* rope_cs = nullptr);
 // (cos, sin) table of the QKV epilogue for rows 0..n-1 at positions pos[].
 int launch_rope_table(const int32_t* pos, int n, int d, double theta, float* rope_cs, hipStream_t stream);
@@ -43,7 +40,7 @@ inline int64_t xpack_elems(int64_t k_in) { return ((k_in + 63) / 64) * 2048; }
 bool gemm_is_skinny(int64_t m, const tvp_w12_packed* w);
 // Number of K slices gemm_run uses for `ksplit` (clamped so none is empty).
 int gemm_ksplits(int64_t m, const tvp_w12_packed* w, int ksplit);
-// Counter entries and scratch bytes gemm_run needs for m rows (and `ksplit`).
+// Channel groups and scratch bytes gemm_run needs for m rows (and `ksplit`).
 void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* scratch_bytes, int ksplit = 1);
 
 int launch_tree_prep(const int32_t* parents, const ReqInfo& ri, int32_t s_req, uint64_t* anc,

@@ -298,7 +298,6 @@ struct tvp_plan {
   int ld_h, ld_q, ld_u;
   bool pack_ok;  // every GEMM takes the skinny path at <= 32 rows
   // workspace layout
-  size_t off_gcnt, zero_end;
   size_t off_h, off_a, off_q, off_o, off_u;
   size_t off_anc, off_pos, off_slot, off_tstat, off_bad, off_rope;
   size_t off_gscr, gscr_bytes;
@@ -384,9 +383,6 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
     return std::max((size_t)mn * ld * 2, (size_t)xpack_elems(k) * 2);
   };
   size_t off = 0;
-  p->off_gcnt = off;
-  off = align_up(off + (size_t)gmax * 4, 256);
-  p->zero_end = off;
   p->off_h = off;
   off = align_up(off + (size_t)mn * p->ld_h * 2, 256);
   p->off_a = off;
@@ -459,7 +455,6 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     max_keys = std::max(max_keys, ri.ctx_len[r] + n);
   }
   uint8_t* w = (uint8_t*)ws;
-  uint32_t* gcnt = (uint32_t*)(w + p->off_gcnt);
   uint16_t* h = (uint16_t*)(w + p->off_h);
   uint16_t* a = (uint16_t*)(w + p->off_a);
   uint16_t* q = (uint16_t*)(w + p->off_q);
@@ -498,7 +493,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     e.v_cache = L.v_cache;
     e.s_stride = d.s_max;
     e.rope_theta = d.rope_theta;
-    if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wqkv, &e, 0, gcnt, gscr, p->gscr_bytes,
+    if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wqkv, &e, 0, gscr, p->gscr_bytes,
                        stream, 1, rope)))
       return st;
     if ((st = launch_tree_attention(q, L.k_cache, L.v_cache, d.s_max, ri, s_req, anc, hq, hkv, hd, G * max_n,
@@ -510,14 +505,14 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
       e.mode = kEpiPartial;
       e.y = part;
       e.ldy = H;
-      if ((st = gemm_run(o, o, n_total, p->ld_q, &L.wo, &e, 0, gcnt, gscr, p->gscr_bytes, stream,
+      if ((st = gemm_run(o, o, n_total, p->ld_q, &L.wo, &e, 0, gscr, p->gscr_bytes, stream,
                          TVP_KSPLIT_MAX)))
         return st;
       launch_norm(part, gemm_ksplits(n_total, &L.wo, TVP_KSPLIT_MAX), pstride, H, h, p->ld_h, L.ffn_norm, H,
                   d.norm_eps, a, p->ld_h, 1, n_total, stream);
     } else {  // wide kernel: its split sums stay in the GEMM scratch and the norm adds them in split order
       e.mode = kEpiPartial;
-      if ((st = gemm_run(o, nullptr, n_total, p->ld_q, &L.wo, &e, 0, gcnt, gscr, p->gscr_bytes, stream)))
+      if ((st = gemm_run(o, nullptr, n_total, p->ld_q, &L.wo, &e, 0, gscr, p->gscr_bytes, stream)))
         return st;
       const int ldp = L.wo.n_tiles * 32;
       launch_norm((const float*)gscr, gemm_ksplits(n_total, &L.wo, 1), (int64_t)n_total * ldp, ldp, h, p->ld_h,
@@ -528,7 +523,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     e.mode = TVP_EPI_SWIGLU;
     e.y = u;
     e.ldy = p->ld_u;
-    if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wgu, &e, pk, gcnt, gscr, p->gscr_bytes,
+    if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wgu, &e, pk, gscr, p->gscr_bytes,
                        stream)))
       return st;
     // down projection + residual, then the next layer's attention norm (or the final norm)
@@ -537,14 +532,14 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
       e.mode = kEpiPartial;
       e.y = part;
       e.ldy = H;
-      if ((st = gemm_run(u, u, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gscr, p->gscr_bytes, stream,
+      if ((st = gemm_run(u, u, n_total, p->ld_u, &L.wdown, &e, 0, gscr, p->gscr_bytes, stream,
                          TVP_KSPLIT_MAX)))
         return st;
       launch_norm(part, gemm_ksplits(n_total, &L.wdown, TVP_KSPLIT_MAX), pstride, H, h, p->ld_h, next_norm, H,
                   d.norm_eps, a, p->ld_h, 1, n_total, stream);
     } else {
       e.mode = kEpiPartial;
-      if ((st = gemm_run(u, nullptr, n_total, p->ld_u, &L.wdown, &e, 0, gcnt, gscr, p->gscr_bytes, stream)))
+      if ((st = gemm_run(u, nullptr, n_total, p->ld_u, &L.wdown, &e, 0, gscr, p->gscr_bytes, stream)))
         return st;
       const int ldp = L.wdown.n_tiles * 32;
       launch_norm((const float*)gscr, gemm_ksplits(n_total, &L.wdown, 1), (int64_t)n_total * ldp, ldp, h,
@@ -557,7 +552,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   e.argmax = out->argmax;
   e.logits = out->logits;
   e.ldl = d.vocab;
-  if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &d.lm_head, &e, 0, gcnt, gscr, p->gscr_bytes,
+  if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &d.lm_head, &e, 0, gscr, p->gscr_bytes,
                      stream)))
     return st;
   accept_kernel<<<dim3(ri.n_req), dim3(64), 0, stream>>>(out->argmax, tokens, parents, ri, bad, out->path,

@@ -7,6 +7,7 @@
 // exact escape.  The window holding the most normal exponents wins, the
 // smallest base on ties; records are sign<<11 | off<<7 | mantissa, stored as
 // a high byte (record >> 4) and a low nibble (two per byte, even k low).
+#include <algorithm>
 #include <vector>
 
 #include "common.h"
@@ -391,6 +392,24 @@ int w12_decode(const tvp_w12* t, uint16_t* out, hipStream_t stream) {
   return TVP_OK;
 }
 
+int w12_validate(const uint8_t* base, const uint32_t* esc_ptr, const uint16_t* esc_idx, int64_t n_out,
+                 int64_t k_in, int64_t n_esc) {
+  if (n_out < 0 || k_in < 0 || n_esc < 0) return TVP_ERR_ARG;
+  if (k_in > 65536 || n_esc > 0xFFFFFFFFll) return TVP_ERR_FORMAT;
+  if (!esc_ptr || (n_out > 0 && !base) || (n_esc > 0 && !esc_idx)) return TVP_ERR_ARG;
+  if (esc_ptr[0] != 0 || (int64_t)esc_ptr[n_out] != n_esc) return TVP_ERR_FORMAT;
+  for (int64_t r = 0; r < n_out; ++r) {
+    if (base[r] < 1 || base[r] > 239) return TVP_ERR_FORMAT;
+    const uint32_t a = esc_ptr[r], z = esc_ptr[r + 1];
+    if (z < a || z > (uint64_t)n_esc) return TVP_ERR_FORMAT;
+    for (uint32_t e = a; e < z; ++e) {
+      if ((int64_t)esc_idx[e] >= k_in) return TVP_ERR_FORMAT;
+      if (e > a && esc_idx[e] <= esc_idx[e - 1]) return TVP_ERR_FORMAT;
+    }
+  }
+  return TVP_OK;
+}
+
 int w12_pack_size(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, int32_t map_a,
                   int32_t map_b, int32_t map_c, tvp_w12_packed* p) {
   if (!p || n_out < 1 || k_in < 0 || n_esc < 0) return TVP_ERR_ARG;
@@ -447,6 +466,22 @@ int w12_pack(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hip
   const int64_t units = (int64_t)p->n_tiles * p->n_kb;
   if (!ws || ws_bytes < (size_t)(units + 1) * 4 || ws_bytes < w12_pack_workspace(t->n_out, t->k_in))
     return TVP_ERR_WORKSPACE;
+  // The packer's binary searches and the GEMM's escape patch rely on the
+  // side data being well formed: check it on the host first (this call
+  // synchronises anyway), and launch nothing if it is not.
+  {
+    std::vector<uint8_t> hb((size_t)t->n_out);
+    std::vector<uint32_t> hp((size_t)t->n_out + 1);
+    std::vector<uint16_t> hi((size_t)std::max<int64_t>(t->n_esc, 1));
+    if (!t->base || !t->esc_ptr || (t->n_esc > 0 && !t->esc_idx)) return TVP_ERR_ARG;
+    TVP_CHECK_HIP(hipMemcpyAsync(hb.data(), t->base, hb.size(), hipMemcpyDeviceToHost, stream));
+    TVP_CHECK_HIP(hipMemcpyAsync(hp.data(), t->esc_ptr, hp.size() * 4, hipMemcpyDeviceToHost, stream));
+    if (t->n_esc > 0)
+      TVP_CHECK_HIP(hipMemcpyAsync(hi.data(), t->esc_idx, (size_t)t->n_esc * 2, hipMemcpyDeviceToHost, stream));
+    TVP_CHECK_HIP(hipStreamSynchronize(stream));
+    const int vs = w12_validate(hb.data(), hp.data(), hi.data(), t->n_out, t->k_in, t->n_esc);
+    if (vs != TVP_OK) return vs;
+  }
   std::vector<int32_t> map;
   int st = build_rowmap(p, map);
   if (st != TVP_OK) return st;

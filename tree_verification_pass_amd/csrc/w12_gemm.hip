@@ -45,7 +45,6 @@ struct GemmArgs {
   int kps;    // skinny: K blocks per slice of a split group
   int kbs_split;  // skinny, partial-sum epilogue: K blocks per wavefront of a slice
   float* part;
-  uint32_t* cnt;
   unsigned long long* keys;  // ARGMAX: [slot][m] packed (value, -id) maxima, one slot per workgroup that
                              // applies the epilogue (every slot written, no zeroing)
   int key_slots;
@@ -1153,9 +1152,9 @@ void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* 
 }
 
 int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
-             const tvp_gemm_epilogue* epi, int y_packed, uint32_t* cnt, void* scratch, size_t scratch_bytes,
+             const tvp_gemm_epilogue* epi, int y_packed, void* scratch, size_t scratch_bytes,
              hipStream_t stream, int ksplit, const float* rope_cs) {
-  if (!w || !epi || !w->blob || !cnt) return TVP_ERR_ARG;
+  if (!w || !epi || !w->blob) return TVP_ERR_ARG;
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
   if (ksplit > 1 && epi->mode != kEpiPartial) return TVP_ERR_ARG;
   const GemmPlan p = make_plan(m, w, ksplit, epi->mode != TVP_EPI_ARGMAX);
@@ -1205,7 +1204,6 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
   a.ldrp = p.rem_groups * p.TPW * 32;
   a.rope_cs = epi->mode == TVP_EPI_QKV ? rope_cs : nullptr;
   a.ntasks = p.ntasks;
-  a.cnt = cnt;
   a.keys = (unsigned long long*)((uint8_t*)scratch + p.keys_off);
   a.key_slots = p.key_slots;
   a.part = (float*)scratch;  // wide: split-K partial sums
@@ -1265,38 +1263,35 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
 
 using namespace tvp;
 
-// Standalone GEMM workspace: a fixed reserved region (kept for the layout
-// callers size; no kernel writes it), then the scratch.
-static size_t gemm_ws_layout(int64_t m, const tvp_w12_packed* w, size_t* off_scr, size_t* scr_bytes,
-                             int* groups) {
+// Standalone GEMM workspace: the scratch of gemm_run, nothing else (no
+// initial contents are needed).
+static size_t gemm_ws_layout(int64_t m, const tvp_w12_packed* w, size_t* scr_bytes, int* groups) {
   gemm_requirements(m, w, groups, scr_bytes);
-  *off_scr = kGemmZeroBytes;
-  return *off_scr + *scr_bytes;
+  return *scr_bytes;
 }
 
 extern "C" {
 
 size_t w12_gemm_workspace(int64_t m, const tvp_w12_packed* w) {
   if (!w || m < 1 || m > 192) return 0;
-  size_t b, c;
+  size_t b;
   int g;
-  return gemm_ws_layout(m, w, &b, &c, &g);
+  return gemm_ws_layout(m, w, &b, &g);
 }
 
 int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
                 const tvp_gemm_epilogue* epi, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!w || !epi) return TVP_ERR_ARG;
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
-  size_t off_scr, scr_bytes;
+  size_t scr_bytes;
   int groups;
-  const size_t need = gemm_ws_layout(m, w, &off_scr, &scr_bytes, &groups);
+  const size_t need = gemm_ws_layout(m, w, &scr_bytes, &groups);
   if ((size_t)groups > kGemmMaxGroups) return TVP_ERR_SHAPE;
   if (!ws || ws_bytes < need) return TVP_ERR_WORKSPACE;
   if (epi->mode < TVP_EPI_F32 || epi->mode > TVP_EPI_ARGMAX) return TVP_ERR_ARG;
-  uint8_t* b = (uint8_t*)ws;
   if (epi->x_packed && !x) return TVP_ERR_ARG;
-  return gemm_run(epi->x_packed ? nullptr : x, epi->x_packed ? x : nullptr, m, ldx, w, epi, epi->y_packed,
-                  (uint32_t*)b, b + off_scr, scr_bytes, stream);
+  return gemm_run(epi->x_packed ? nullptr : x, epi->x_packed ? x : nullptr, m, ldx, w, epi, epi->y_packed, ws,
+                  ws_bytes, stream);
 }
 
 int64_t w12_packed_x_elems(int64_t k_in) { return k_in < 0 ? 0 : xpack_elems(k_in); }
