@@ -551,6 +551,108 @@ def bench_cost_curve(args, cfg, dm) -> int:
     return 0
 
 
+# Standalone W12 GEMM shapes of the 27B-like target, (n_out, k_in): the
+# weights [5120 x 17408], [17408 x 5120] and [5120 x 6144] read as K_in x N_out.
+GEMM_SHAPES = ((17408, 5120), (5120, 17408), (6144, 5120))
+GEMM_ROWS = (1, 16, 32)
+
+
+def bench_gemm(args) -> int:
+    """The standalone skinny W12 GEMM at the 27B-like shapes, M in {1, 16, 32}:
+    Y = X W^T, X bf16 N(0,1) in the GEMM's packed activation layout, Y bf16.
+    Per shape, distinct encoded copies totalling at least 512 MB (twice the
+    256 MB memory-side cache) are cycled, so every launch streams its weights
+    from HBM; each launch is timed with HIP events on the stream it runs on
+    (the median over the timed launches is reported)."""
+    import torch
+
+    import tree_verification_pass_amd as tvp
+    from synth import gen_linear_bf16, make_generator
+    from synth.configs import LARGE_RECIPE
+    from synth.weights import bf16_bits_numpy, sub_seed
+
+    dev = torch.device("cuda:0")
+    probe = read_probe_gbs()
+    cases = []
+    cpu = None
+    for si, (n_out, k_in) in enumerate(GEMM_SHAPES):
+        per_copy = n_out * k_in * 1.55
+        n_copies = max(4, int(np.ceil(512e6 / per_copy)))
+        log(f"bench: gemm {n_out}x{k_in}: encoding {n_copies} copies")
+        copies, alg = [], []
+        for c in range(n_copies):
+            w = gen_linear_bf16(make_generator(sub_seed(args.seed, 90, si, c), dev), n_out, k_in, LARGE_RECIPE,
+                                device=dev)
+            t = tvp.w12_encode(w)
+            alg.append(w12_algorithmic_bytes(n_out, k_in, t.n_esc))
+            copies.append(tvp.w12_pack(t))
+            if c == 0 and si == 0 and not args.no_cpu_baseline:
+                cpu = gemm_cpu_baseline(bf16_bits_numpy(w))
+            del t, w
+        torch.cuda.synchronize()
+        for m in GEMM_ROWS:
+            x = torch.randn(m, k_in, generator=make_generator(sub_seed(args.seed, 91, m))).to(torch.bfloat16).to(dev)
+            xp = tvp.w12_pack_x(x)
+            y = torch.empty(m, n_out, dtype=torch.bfloat16, device=dev)
+            epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_BF16, y=y.data_ptr(), ldy=n_out)
+            for c in range(n_copies):
+                tvp.w12_gemm_px(xp, m, copies[c], epi)
+            torch.cuda.synchronize()
+            iters = max(args.gemm_iters, 4 * n_copies)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+            for i in range(iters):
+                ev[i][0].record()
+                tvp.w12_gemm_px(xp, m, copies[i % n_copies], epi)
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            us = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1000.0
+            nbytes = float(np.mean(alg)) + m * k_in * 2 + m * n_out * 2
+            gbs = nbytes / (us * 1e-6) / 1e9
+            cases.append({"n_out": n_out, "k_in": k_in, "m": m, "us_per_launch": round(us, 2),
+                          "bytes_per_launch": int(nbytes), "achieved_gbs": round(gbs, 1),
+                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "probe_frac": round(gbs / probe, 4),
+                          "copies": n_copies})
+            log(f"bench: gemm {n_out}x{k_in} m={m}: {us:.2f} us, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f} of 8 TB/s)")
+        del copies
+        torch.cuda.empty_cache()
+    gm = float(np.exp(np.mean([np.log(c["achieved_gbs"]) for c in cases])))
+    line = {
+        "metric": "W12 skinny GEMM achieved HBM GB/s (27B-like shapes, M = 1/16/32), 1 GPU",
+        "value": round(gm, 1), "unit": "GB/s (geometric mean over shapes and M)", "n_gpus": 1,
+        "steps": max(args.gemm_iters, 1), "warmup": 1, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "read_probe_gbs": round(probe, 1),
+        "config": {"workload": "standalone W12 GEMM, weights [5120x17408], [17408x5120], [5120x6144] (K_in x N_out), "
+                               "M in {1,16,32}, X bf16 N(0,1), fp32 accumulation, bf16 out",
+                   "weights": "per-channel sigma log-uniform [0.005,0.05], 1% zeros, 0.05% outliers x1000",
+                   "rotation": ">= 512 MB of distinct encoded copies per shape"},
+        "cases": cases,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def gemm_cpu_baseline(w_bits):
+    """The oracle (untuned) on the 17408 x 5120 shape at 32 rows: exact W12
+    decode of the canonical tensor plus the fp64 product (the encode is the
+    offline conversion and is not timed)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import w12 as ow12
+    from oracle.bf16 import from_bits
+
+    t = ow12.encode(w_bits)
+    x = np.random.default_rng(0).standard_normal((32, w_bits.shape[1]))
+    t0 = time.perf_counter()
+    y = from_bits(ow12.decode(t)) @ x.T
+    dt = time.perf_counter() - t0
+    threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+    return {"value": round(1e6 * dt, 1), "unit": "us per GEMM (17408x5120, M=32)", "cores": threads,
+            "kind": "oracle", "sample": "one W12 decode + fp64 matmul of the 17408x5120 weight at M=32",
+            "checksum": float(np.abs(y).sum())}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -567,6 +669,8 @@ def main() -> int:
                     help="time the pass at 1, 8, 16 and 32 nodes instead and report c(N) = T(N)/T(1)")
     ap.add_argument("--batched", action="store_true",
                     help="time the batched pass instead (24 requests sharing a 192-node budget)")
+    ap.add_argument("--gemm", action="store_true",
+                    help="time the standalone W12 GEMM at the 27B-like shapes and M = 1, 16, 32 instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run three plain device copies of MIB MiB (calibrates HBM byte counters)")
     ap.add_argument("--rocprof-summary", metavar="DIR", default="",
@@ -602,6 +706,8 @@ def main() -> int:
     from synth.configs import CONFIGS
 
     cfg = CONFIGS[args.config]
+    if args.gemm:
+        return bench_gemm(args)
     if args.batched:
         return bench_batched(args, cfg)
     s_max = cfg.ctx_len + 64

@@ -213,6 +213,26 @@ int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed*
 int64_t w12_packed_x_elems(int64_t k_in);
 int w12_pack_x(const uint16_t* x, int64_t m, int64_t ldx, int64_t k_in, uint16_t* xp, hipStream_t stream);
 
+/* Projection + residual add + RMSNorm, the stage that follows the attention
+ * and the FFN in every layer of verify_step, in the same launch
+ * configuration (K split over workgroups, the slices' fp32 sums added in
+ * slice order by the fused residual + RMSNorm kernel).  The residual add
+ * follows from the decoder layer the pages' targets use; RMSNorm is the
+ * norm of the model configurations (eps given here).
+ *   xp     device bf16, packed activation layout of m rows x w->k_in
+ *   w      TVP_CHAN_PLAIN packed weight, w->k_in <= 32256
+ *   h      device bf16 [m][ldh] residual stream, updated in place:
+ *          h = bf16(h + xp . W^T)  (fp32 sum, one rounding)
+ *   gain   device bf16 [w->n_out]
+ *   yp     device bf16, packed layout of m rows x w->n_out:
+ *          bf16(h * (mean(h^2) + eps)^-1/2 * gain), fp32 inside
+ *   ws     device scratch of w12_gemm_resid_norm_workspace() bytes
+ * 1 <= m <= 32 (TVP_ERR_SHAPE otherwise); 16-byte aligned pointers.       */
+size_t w12_gemm_resid_norm_workspace(int64_t m, const tvp_w12_packed* w);
+int w12_gemm_resid_norm(const uint16_t* xp, int64_t m, const tvp_w12_packed* w, uint16_t* h, int64_t ldh,
+                        const uint16_t* gain, float eps, uint16_t* yp, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
 /* ------------------------------------------------------- tree attention
  * Attention of n draft-tree nodes over a committed context and their own
  * ancestors (SpecPilot summary, section 전제와 한계 names tree attention as

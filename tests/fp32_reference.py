@@ -12,9 +12,10 @@ noise, both computed from the oracle's definition alone:
   relative amount of at most ``eta`` (fp32-accumulation level) just before
   each bf16 rounding point.
 
-The end-to-end logit comparison allows max(2e-3, 1.5 x the larger envelope);
-the kernel-level parity tests, which see identical inputs, keep the plain
-bound.
+The end-to-end logit comparison is per row: row v may deviate by
+max(2e-3, 1.5 x row v's envelope), never more than ROW_TOL_CAP (see
+tests/parity.py); the kernel-level parity tests, which see identical inputs,
+keep the plain bound.
 """
 
 from __future__ import annotations
@@ -86,18 +87,14 @@ def noisy_oracle(m, cache, L, tokens, parents, seed: int, eta: float = 2.0 ** -1
         om.round_bf16 = orig
 
 
-def noise_envelope(m, cache, L, tokens, parents, ref_logits: np.ndarray, runs: int = 4) -> float:
-    """Largest row max-abs-rel deviation from the fp64 oracle over `runs` fp32
-    evaluations with different summation orders and `runs` noisy-rounding
-    oracle evaluations."""
+def noise_envelope_rows(m, cache, L, tokens, parents, ref_logits: np.ndarray, runs: int = 4) -> np.ndarray:
+    """Per logits row, the largest max-abs-rel deviation from the fp64 oracle
+    over `runs` fp32 evaluations with different summation orders and `runs`
+    noisy-rounding oracle evaluations."""
     from tests.parity import row_max_abs_rel
-    worst = 0.0
+    worst = np.zeros(ref_logits.shape[0])
     for s in range(runs):
         for g in (forward_fp32(m, cache, L, tokens, parents, seed=1000 + s),
                   noisy_oracle(m, cache, L, tokens, parents, seed=2000 + s)):
-            worst = max(worst, float(row_max_abs_rel(g, ref_logits).max()))
+            worst = np.maximum(worst, row_max_abs_rel(g, ref_logits))
     return worst
-
-
-def logit_tolerance(envelope: float, floor: float = 2e-3) -> float:
-    return max(floor, 1.5 * envelope)

@@ -2,12 +2,13 @@
 bench.py times: the 27B-like shapes (hidden 5120, 40 query / 8 KV heads of
 128, SwiGLU 17408, 4096-token context) and the 4B-like shapes (hidden 2560,
 32 / 8 heads of 128, SwiGLU 9728, 2048-token context), each with the full
-151936-token LM head and a 32-node best-first tree; and the batched pass at
-the 27B-like shapes (24 requests sharing a 192-node budget, trees of 4-16
-nodes, contexts uniform in [512, 8192]).  One decoder layer each (the
-oracle's fp64 cost of a whole model would not fit a test).  Logits are compared on every row within max(2e-3, 1.5 x the
-rounding-noise envelope of fp32 evaluations of the same definition, see
-tests/fp32_reference.py), greedy tokens on decidable rows, acceptance where
+151936-token LM head and a 32-node best-first tree: one decoder layer of
+each, and the whole 36-layer 4B-like target; and the batched pass at the
+27B-like shapes (24 requests sharing a 192-node budget, trees of 4-16 nodes,
+contexts uniform in [512, 8192]), every request compared.  Logits are
+compared row by row within max(2e-3, 1.5 x the row's rounding-noise envelope
+of fp32 evaluations of the same definition, see tests/fp32_reference.py),
+at most ROW_TOL_CAP; greedy tokens on decidable rows, acceptance where
 determined; the pass is bitwise reproducible."""
 
 import dataclasses
@@ -20,13 +21,13 @@ from oracle import model as om
 from oracle.accept import accept as oaccept
 from oracle.bf16 import from_bits
 from synth import best_first_topology
-from synth.configs import CONFIGS, gen_kv_context, gen_model
+from synth.configs import CONFIGS, gen_kv_context, gen_layer, gen_model
 from synth.trees import assign_tokens_by_depth
 from synth.weights import bf16_bits_numpy
-from tests.fp32_reference import logit_tolerance, noise_envelope
+from tests.fp32_reference import noise_envelope_rows
 from tests.gpu_util import to_i32
 from tests.helpers import oracle_topk_fn
-from tests.parity import acceptance_ok, check_logits
+from tests.parity import acceptance_ok, check_logits, row_report, row_tolerances
 
 pytestmark = pytest.mark.gpu
 
@@ -71,13 +72,12 @@ def test_verify_step_full_shapes_one_layer(cuda, cfg_name):
     torch.cuda.synchronize()
     g = res.logits.cpu().numpy().astype(np.float64)
     print("  rounding-noise envelope", flush=True)
-    env = noise_envelope(orc, cache, L, tokens, parents, ref["logits"], runs=2)
-    tol = logit_tolerance(env)
+    env = noise_envelope_rows(orc, cache, L, tokens, parents, ref["logits"], runs=3)
+    tol = row_tolerances(env)
     chk = check_logits(g, ref["logits"], tol=tol)
-    print(f"  logits max_abs_rel={chk['max_abs_rel']:.2e} fp32-envelope={env:.2e} tol={tol:.2e} "
-          f"undecidable={chk['undecidable_frac']:.3f} accepted={int(res.n_accepted.item())} "
+    print(f"  logits {row_report(chk, env, tol)} accepted={int(res.n_accepted.item())} "
           f"(oracle {ref['n_accepted']})", flush=True)
-    assert chk["logits_ok"], chk["max_abs_rel"]
+    assert chk["logits_ok"], (chk["bad_rows"], chk["max_abs_rel"])
     assert chk["argmax_ok"], chk["bad_argmax_rows"]
     am = res.argmax.cpu().numpy()
     assert np.array_equal(am, np.argmax(res.logits.cpu().numpy(), axis=1))
@@ -93,10 +93,10 @@ def test_verify_step_batched_27b_shapes_one_layer(cuda):
     topology) over contexts uniform in [512, 8192], in one batched pass at the
     27B-like shapes.  Every request: status OK, argmax equal to the argmax of
     its own logits, acceptance following from its own greedy tokens, and the
-    pass bitwise reproducible.  Six requests -- the shortest and longest
-    context, the smallest and largest tree, one whose drafts come from the
-    oracle's own top-4 and one more -- are compared with the oracle run on
-    that request alone."""
+    pass bitwise reproducible.  Every request is compared with the oracle run
+    on that request alone; two of them (the shortest and the longest
+    context) carry drafts from the oracle's own top-4, so some of their
+    drafts are accepted."""
     import tree_verification_pass_amd as tvp
     from synth.trees import batch_sizes
     from tree_verification_pass_amd.model import DeviceModel, Dims
@@ -128,14 +128,11 @@ def test_verify_step_batched_27b_shapes_one_layer(cuda):
         sl = slice(r * s_req, r * s_req + int(ctxs[r]))
         return om.KVCache.from_bits([bf16_bits_numpy(kc[:, sl])], [bf16_bits_numpy(vc[:, sl])])
 
-    sampled = sorted({int(np.argmin(ctxs)), int(np.argmax(ctxs)), int(np.argmin(sizes)), int(np.argmax(sizes))})
-    extra = [r for r in range(n_req) if r not in sampled]
-    drafted = extra[0]
-    sampled = sorted(set(sampled) | {drafted, extra[len(extra) // 2]})
+    drafted = {int(np.argmin(ctxs)), int(np.argmax(ctxs))}
     trees, toks = [], []
     for r in range(n_req):
         parents, rank, _ = best_first_topology(rng, int(sizes[r]))
-        if r == drafted:
+        if r in drafted:
             tokens = assign_tokens_by_depth(rng, parents, rank, int(rng.integers(cfg.vocab)), cfg.vocab,
                                             oracle_topk_fn(orc, cache_of(r), int(ctxs[r])), 0.7)
         else:
@@ -161,14 +158,102 @@ def test_verify_step_batched_27b_shapes_one_layer(cuda):
         assert int(res.status[r].item()) == 0
         assert int(res.n_accepted[r].item()) == a_own and int(res.bonus[r].item()) == b_own
         assert path_all[sl][: a_own + 1].tolist() == p_own
-    for r in sampled:
-        sl = slice(node_ptr[r], node_ptr[r + 1])
+    # the oracle and its rounding-noise envelope per request; one bound for the
+    # whole batch, from the envelope pooled over every request's rows
+    refs, envs = [], []
+    for r in range(n_req):
         cache = cache_of(r)
-        ref = om.verify(orc, cache, int(ctxs[r]), toks[r], trees[r])
-        env = noise_envelope(orc, cache, int(ctxs[r]), toks[r], trees[r], ref["logits"], runs=1)
-        chk = check_logits(lg_dev[sl].cpu().numpy().astype(np.float64), ref["logits"], tol=logit_tolerance(env))
-        print(f"  request {r}: {sizes[r]} nodes, ctx {ctxs[r]}: max_abs_rel={chk['max_abs_rel']:.2e} "
-              f"envelope={env:.2e} accepted={int(res.n_accepted[r].item())} (oracle {ref['n_accepted']})",
-              flush=True)
-        assert chk["logits_ok"] and chk["argmax_ok"], (r, chk["max_abs_rel"], env)
+        refs.append(om.verify(orc, cache, int(ctxs[r]), toks[r], trees[r]))
+        envs.append(noise_envelope_rows(orc, cache, int(ctxs[r]), toks[r], trees[r], refs[r]["logits"], runs=1))
+    tol_all = row_tolerances(np.concatenate(envs))
+    above = []
+    for r in range(n_req):
+        sl = slice(node_ptr[r], node_ptr[r + 1])
+        ref, env = refs[r], envs[r]
+        tol = tol_all[: len(env)]
+        chk = check_logits(lg_dev[sl].cpu().numpy().astype(np.float64), ref["logits"], tol=tol)
+        above.append(chk["row_err"] > 2e-3)
+        print(f"  request {r}: {sizes[r]} nodes, ctx {ctxs[r]}: {row_report(chk, env, tol)} "
+              f"accepted={int(res.n_accepted[r].item())} (oracle {ref['n_accepted']})", flush=True)
+        assert chk["logits_ok"] and chk["argmax_ok"], (r, chk["bad_rows"], chk["max_abs_rel"])
         assert acceptance_ok(am_all[sl], ref["argmax"], toks[r], trees[r], chk["decidable"])
+    print(f"  rows above 2e-3: {np.concatenate(above).mean():.3f} of {int(sizes.sum())}; "
+          f"batch bound {tol_all[0]:.2e}", flush=True)
+
+
+class _LazyLayers:
+    """Oracle weights of layer l converted from bf16 bits when the forward pass
+    reaches it (the whole 4B-like target in fp64 would hold 29 GB at once)."""
+
+    def __init__(self, cfg, seed: int):
+        self.cfg, self.seed = cfg, seed
+
+    def __len__(self):
+        return self.cfg.n_layers
+
+    def __getitem__(self, layer):
+        if not 0 <= layer < self.cfg.n_layers:
+            raise IndexError(layer)
+        return {k: from_bits(bf16_bits_numpy(v)) for k, v in gen_layer(self.cfg, self.seed, layer, "cpu",
+                                                                       "random").items()}
+
+    def __iter__(self):
+        return (self[i] for i in range(len(self)))
+
+
+def test_verify_step_4b_full_depth(cuda):
+    """The whole 36-layer 4B-like target, 2048-token context, full LM head, a
+    32-node best-first tree whose root's children carry the oracle's own top-4
+    tokens (the rest uniform): every row of the logits against the oracle
+    under the per-row rule, greedy tokens on decidable rows, acceptance where
+    determined, the path following from the pass's own greedy tokens."""
+    import tree_verification_pass_amd as tvp
+    from synth.configs import gen_embed, gen_final_norm, gen_lm_head
+    from tree_verification_pass_amd.model import DeviceModel, Dims
+
+    cfg = CONFIGS["4b"]
+    L, s_max, n, seed = cfg.ctx_len, cfg.ctx_len + 64, cfg.n_nodes, 12
+    print(f"[full depth] 4b: {cfg.n_layers} layers, ctx {L}, {n} nodes", flush=True)
+    kv = [gen_kv_context(cfg, seed, layer, L, s_max) for layer in range(cfg.n_layers)]
+    embed = gen_embed(cfg, seed, "cpu")
+    fnorm = gen_final_norm(cfg, seed, "cpu", "random")
+    lm = gen_lm_head(cfg, seed, "cpu")
+    dm = DeviceModel(Dims.of(cfg), embed.to(cuda), fnorm.to(cuda), lm.to(cuda),
+                     lambda l: {k: v.to(cuda) for k, v in gen_layer(cfg, seed, l, "cpu", "random").items()},
+                     lambda l: (kv[l][0].to(cuda), kv[l][1].to(cuda)), s_max=s_max, max_nodes=n)
+    orc = om.OracleModel(om.Dims.of(cfg), _Rows(bf16_bits_numpy(embed)), _LazyLayers(cfg, seed),
+                         from_bits(bf16_bits_numpy(fnorm)), from_bits(bf16_bits_numpy(lm)))
+    cache = om.KVCache.from_bits([bf16_bits_numpy(k) for k, _ in kv], [bf16_bits_numpy(v) for _, v in kv])
+    rng = np.random.default_rng(13)
+    parents, rank, _ = best_first_topology(rng, n)
+    root = int(rng.integers(cfg.vocab))
+    print("  oracle: root's top-4", flush=True)
+    lg0, _ = om.forward_tree(orc, cache, L, [root], [-1])
+    top = np.argsort(-lg0[0], kind="stable")[:4]
+    tokens = rng.integers(0, cfg.vocab, n).astype(np.int32)
+    tokens[0] = root
+    for i in range(1, n):
+        if parents[i] == 0 and rank[i] < 4:
+            tokens[i] = int(top[rank[i]])
+    print("  oracle forward", flush=True)
+    ref = om.verify(orc, cache, L, tokens, parents)
+    print("  gpu pass", flush=True)
+    res = tvp.verify_step(dm.plan, L, to_i32(tokens), to_i32(parents), commit=False, want_logits=True)
+    res2 = tvp.verify_step(dm.plan, L, to_i32(tokens), to_i32(parents), commit=False, want_logits=True)
+    torch.cuda.synchronize()
+    assert torch.equal(res.logits, res2.logits)
+    g = res.logits.cpu().numpy().astype(np.float64)
+    print("  rounding-noise envelope", flush=True)
+    env = noise_envelope_rows(orc, cache, L, tokens, parents, ref["logits"], runs=1)
+    tol = row_tolerances(env)
+    chk = check_logits(g, ref["logits"], tol=tol)
+    print(f"  logits {row_report(chk, env, tol)} accepted={int(res.n_accepted.item())} "
+          f"(oracle {ref['n_accepted']})", flush=True)
+    assert chk["logits_ok"], (chk["bad_rows"], chk["max_abs_rel"])
+    assert chk["argmax_ok"], chk["bad_argmax_rows"]
+    am = res.argmax.cpu().numpy()
+    assert np.array_equal(am, np.argmax(res.logits.cpu().numpy(), axis=1))
+    p_own, a_own, b_own = oaccept(am, tokens, parents)
+    assert int(res.n_accepted.item()) == a_own and int(res.bonus.item()) == b_own
+    assert res.path.cpu().numpy()[: a_own + 1].tolist() == p_own
+    assert acceptance_ok(am, ref["argmax"], tokens, parents, chk["decidable"])

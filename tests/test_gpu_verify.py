@@ -1,7 +1,7 @@
 """GPU parity of the whole verification pass (verify_step through the C ABI)
-against the CPU oracle: logits within max(2e-3, twice the rounding-noise
+against the CPU oracle: logits within max(2e-3, 1.5 x the row's own rounding-noise
 envelope of fp32 evaluations of the same definition -- see
-tests/fp32_reference.py), greedy tokens equal on decidable rows, acceptance
+tests/fp32_reference.py), at most 2e-2 per row, greedy tokens equal on decidable rows, acceptance
 equal where determined, commit moves exactly the accepted rows, a speculative
 loop reproduces the oracle's greedy stream, and a batch gives each request
 what the oracle gives that request alone."""
@@ -17,8 +17,8 @@ from synth.configs import CONFIGS
 from synth.trees import assign_tokens_by_depth
 from tests.gpu_util import build_pair, to_i32
 from tests.helpers import oracle_topk_fn
-from tests.fp32_reference import logit_tolerance, noise_envelope
-from tests.parity import acceptance_ok, check_logits
+from tests.fp32_reference import noise_envelope_rows
+from tests.parity import acceptance_ok, check_logits, row_report, row_tolerances
 
 pytestmark = pytest.mark.gpu
 
@@ -32,12 +32,11 @@ def _run(dm, ctx, tokens, parents, commit=False):
 
 def _compare(res, ref, tokens, parents, orc, cache, ctx, lg=None):
     g = res.logits.cpu().numpy().astype(np.float64) if lg is None else lg
-    env = noise_envelope(orc, cache, ctx, tokens, parents, ref["logits"])
-    tol = logit_tolerance(env)
+    env = noise_envelope_rows(orc, cache, ctx, tokens, parents, ref["logits"])
+    tol = row_tolerances(env)
     chk = check_logits(g, ref["logits"], tol=tol)
-    print(f"  logits max_abs_rel={chk['max_abs_rel']:.2e} fp32-envelope={env:.2e} tol={tol:.2e} "
-          f"undecidable={chk['undecidable_frac']:.3f}", flush=True)
-    assert chk["logits_ok"], (chk["max_abs_rel"], tol)
+    print(f"  logits {row_report(chk, env, tol)}", flush=True)
+    assert chk["logits_ok"], (chk["bad_rows"], chk["max_abs_rel"])
     am = res.argmax.cpu().numpy()
     assert np.array_equal(am, np.argmax(res.logits.cpu().numpy(), axis=1))
     assert chk["argmax_ok"], chk["bad_argmax_rows"]
@@ -178,10 +177,11 @@ def test_batched_equals_per_request(cuda):
     for r in range(n_req):
         ref = om.verify(orc, cache, ctxs[r], toks[r], trees[r])
         sl = slice(node_ptr[r], node_ptr[r + 1])
-        env = noise_envelope(orc, cache, ctxs[r], toks[r], trees[r], ref["logits"])
-        chk = check_logits(lg[sl], ref["logits"], tol=logit_tolerance(env))
-        print(f"  request {r}: max_abs_rel={chk['max_abs_rel']:.2e} envelope={env:.2e}", flush=True)
-        assert chk["logits_ok"] and chk["argmax_ok"], (r, chk["max_abs_rel"], env)
+        env = noise_envelope_rows(orc, cache, ctxs[r], toks[r], trees[r], ref["logits"])
+        tol = row_tolerances(env)
+        chk = check_logits(lg[sl], ref["logits"], tol=tol)
+        print(f"  request {r}: {row_report(chk, env, tol)}", flush=True)
+        assert chk["logits_ok"] and chk["argmax_ok"], (r, chk["bad_rows"], chk["max_abs_rel"])
         am = res.argmax.cpu().numpy()[sl]
         p_own, a_own, b_own = oaccept(am, toks[r], trees[r])
         assert int(res.n_accepted[r].item()) == a_own and int(res.bonus[r].item()) == b_own

@@ -105,6 +105,11 @@ _lib_w12_gemm_ex = _sig("w12_gemm_ex", ctypes.c_int,
                          c_vp, c_sz, c_vp])
 _lib_w12_packed_x_elems = _sig("w12_packed_x_elems", c_i64, [c_i64])
 _lib_w12_pack_x = _sig("w12_pack_x", ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp])
+_lib_w12_gemm_resid_norm_workspace = _sig("w12_gemm_resid_norm_workspace", c_sz,
+                                          [c_i64, ctypes.POINTER(TvpW12Packed)])
+_lib_w12_gemm_resid_norm = _sig("w12_gemm_resid_norm", ctypes.c_int,
+                                [c_vp, c_i64, ctypes.POINTER(TvpW12Packed), c_vp, c_i64, c_vp, ctypes.c_float, c_vp,
+                                 c_vp, c_sz, c_vp])
 _lib_tree_attention_workspace = _sig("tree_attention_workspace", c_sz, [c_i32, c_i32, c_i32, c_i32])
 _lib_tree_attention = _sig("tree_attention", ctypes.c_int,
                            [c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
@@ -123,7 +128,7 @@ _lib_tvp_read_probe = _sig("tvp_read_probe", ctypes.c_int, [c_vp, c_sz, c_vp, c_
 
 EXPORTED = ("tvp_status_string", "w12_encode_count", "w12_encode", "w12_decode", "w12_validate", "w12_pack_size",
             "w12_pack_workspace", "w12_pack", "w12_gemm_workspace", "w12_gemm", "w12_gemm_ex",
-            "w12_packed_x_elems", "w12_pack_x",
+            "w12_packed_x_elems", "w12_pack_x", "w12_gemm_resid_norm_workspace", "w12_gemm_resid_norm",
             "tree_attention_workspace", "tree_attention", "accept_path", "tvp_plan_create",
             "tvp_plan_destroy", "verify_step_workspace", "verify_step", "verify_step_batched",
             "tvp_read_probe")
@@ -345,6 +350,20 @@ def w12_gemm_px(xp: torch.Tensor, m: int, w: PackedW12, epi: TvpGemmEpilogue) ->
     ws = _ws_gemm.get(need, xp.device)
     _check(_lib_w12_gemm_ex(_ptr(xp), m, 0, ctypes.byref(w.desc), ctypes.byref(epi), _ptr(ws), ws.numel(),
                             _stream(xp.device)), "w12_gemm_ex")
+
+
+def w12_gemm_resid_norm(xp: torch.Tensor, m: int, w: PackedW12, h: torch.Tensor, gain: torch.Tensor,
+                        eps: float = 1e-6) -> torch.Tensor:
+    """The verify pass's projection + residual + RMSNorm stage: ``h`` (bf16
+    ``[m, n_out]``) is updated in place to ``bf16(h + x W^T)``; returns the
+    normed rows in the packed activation layout."""
+    _dev_check(xp, h, gain)
+    yp = torch.empty(max(w12_packed_x_elems(w.n_out), 8), dtype=torch.bfloat16, device=xp.device)
+    need = int(_lib_w12_gemm_resid_norm_workspace(m, ctypes.byref(w.desc)))
+    ws = _ws_gemm.get(need, xp.device)
+    _check(_lib_w12_gemm_resid_norm(_ptr(xp), m, ctypes.byref(w.desc), _ptr(h), h.stride(0), _ptr(gain), float(eps),
+                                    _ptr(yp), _ptr(ws), ws.numel(), _stream(xp.device)), "w12_gemm_resid_norm")
+    return yp
 
 
 # --------------------------------------------------------------- attention

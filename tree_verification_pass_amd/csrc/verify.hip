@@ -616,6 +616,47 @@ int verify_step_batched(tvp_plan* p, int32_t n_req, const int32_t* ctx_len, cons
   return run_pass(p, ri, s_req, tokens, parents, commit, out, ws, stream);
 }
 
+static size_t resid_norm_ws_layout(int64_t m, const tvp_w12_packed* w, size_t* off_gemm, size_t* gemm_bytes,
+                                   int* slices) {
+  int g;
+  gemm_requirements(m, w, &g, gemm_bytes, TVP_KSPLIT_MAX);
+  *slices = gemm_ksplits(m, w, TVP_KSPLIT_MAX);
+  *off_gemm = align_up((size_t)*slices * m * w->n_out * 4, 256);
+  return *off_gemm + align_up(*gemm_bytes, 256);
+}
+
+size_t w12_gemm_resid_norm_workspace(int64_t m, const tvp_w12_packed* w) {
+  if (!w || m < 1 || m > 32) return 0;
+  size_t og, gb;
+  int s;
+  return resid_norm_ws_layout(m, w, &og, &gb, &s);
+}
+
+int w12_gemm_resid_norm(const uint16_t* xp, int64_t m, const tvp_w12_packed* w, uint16_t* h, int64_t ldh,
+                        const uint16_t* gain, float eps, uint16_t* yp, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  if (!xp || !w || !w->blob || !h || !gain || !yp) return TVP_ERR_ARG;
+  if (m < 1 || m > 32 || w->n_out < 1) return TVP_ERR_SHAPE;
+  if (w->chan_map != TVP_CHAN_PLAIN || !gemm_is_skinny(m, w)) return TVP_ERR_SHAPE;
+  if (ldh < w->n_out || !(eps >= 0.0f)) return TVP_ERR_ARG;
+  if (((uintptr_t)xp | (uintptr_t)yp | (uintptr_t)h | (uintptr_t)gain) % 16) return TVP_ERR_ARG;
+  size_t off_g, gb;
+  int slices;
+  const size_t need = resid_norm_ws_layout(m, w, &off_g, &gb, &slices);
+  if (!ws || ws_bytes < need) return TVP_ERR_WORKSPACE;
+  float* part = (float*)ws;
+  tvp_gemm_epilogue e{};
+  e.mode = kEpiPartial;
+  e.y = part;
+  e.ldy = w->n_out;
+  int st = gemm_run(nullptr, xp, m, 0, w, &e, 0, (uint8_t*)ws + off_g, gb, stream, TVP_KSPLIT_MAX);
+  if (st != TVP_OK) return st;
+  launch_norm(part, slices, m * w->n_out, (int)w->n_out, h, (int)ldh, gain, (int)w->n_out, eps, yp, 0, 1, (int)m,
+              stream);
+  TVP_LAUNCH_CHECK();
+  return TVP_OK;
+}
+
 int accept_path(const int32_t* argmax, const int32_t* tokens, const int32_t* parents, int32_t n,
                 int32_t* path, int32_t* n_accepted, int32_t* bonus, int32_t* status, hipStream_t stream) {
   if (!argmax || !tokens || !parents || !path || !n_accepted || !bonus || !status) return TVP_ERR_ARG;
