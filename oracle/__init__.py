@@ -15,7 +15,11 @@ What it computes is written out from the pages' description of the method
                  one pass over every draft-tree node (section 무엇인가 /
                  "what it is": the target checks the drafter's tokens in one
                  forward pass), plus the definition-level per-path variant;
-* ``accept``  -- the matched path and bonus token (section 무엇과 다른가).
+* ``accept``  -- the matched path and bonus token (section 무엇과 다른가);
+* ``tlv``     -- two-level verification: a Q pass on the 8-bit leading view
+                 of the W12 records, then one exact pass over the matched
+                 path, the bonus token and a re-drafted subtree (section
+                 무엇과 다른가).
 
 Floating point is fp64 between the bf16 rounding points the method fixes
 (bf16 inputs and outputs of every op), so the oracle is at least as accurate
@@ -27,4 +31,4 @@ the structural ones listed there (library-routine equivalences, closed forms,
 special cases), which is stated where it matters.
 """
 
-from . import bf16, w12, accept, model  # noqa: F401
+from . import bf16, w12, accept, model, tlv  # noqa: F401

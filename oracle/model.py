@@ -80,10 +80,15 @@ class OracleModel:
                    None if lm_head is None else from_bits(lm_head))
 
     @classmethod
-    def from_w12(cls, dims: Dims, embed, layers, final_norm, lm_head) -> "OracleModel":
-        """From W12 tensors: every ``W12Tensor`` value is decoded exactly first."""
+    def from_w12(cls, dims: Dims, embed, layers, final_norm, lm_head, view: str = "exact") -> "OracleModel":
+        """From W12 tensors: every ``W12Tensor`` value is decoded exactly first
+        (``view="exact"``), or through the 8-bit leading view of its records
+        (``view="hi8"``, the Q pass of two-level verification, see
+        ``w12.decode_hi8``)."""
+        decode = {"exact": _w12.decode, "hi8": _w12.decode_hi8}[view]
+
         def dec(x):
-            return from_bits(_w12.decode(x) if isinstance(x, _w12.W12Tensor) else x)
+            return from_bits(decode(x) if isinstance(x, _w12.W12Tensor) else x)
         conv = [{k: dec(v) for k, v in layer.items()} for layer in layers]
         return cls(dims, from_bits(embed), conv, from_bits(final_norm),
                    None if lm_head is None else dec(lm_head))

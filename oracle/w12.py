@@ -126,3 +126,26 @@ def decode(t: W12Tensor) -> np.ndarray:
     rows = np.repeat(np.arange(t.n_out), counts)
     out[rows, t.esc_idx.astype(np.int64)] = t.esc_val
     return out
+
+
+def decode_hi8(t: W12Tensor) -> np.ndarray:
+    """The weights seen through the 8-bit leading view of each record, as bf16
+    bit patterns ``[n_out, k_in]`` (SpecPilot summary, section 무엇과 다른가:
+    two-level verification runs its Q pass on the 8-bit view of the front of
+    the W12 records).
+
+    Reading: the view is the ``hi`` plane, ``record >> 4`` (sign, exponent
+    offset and the top three mantissa bits); the weight it stands for is the
+    record with its low four mantissa bits cleared, decoded with the
+    channel's window, i.e. the bf16 value truncated toward zero to three
+    mantissa bits.  Escaped slots are not records: they keep their exact
+    values from the escape list, which is part of the format.
+    """
+    r = t.hi.astype(np.uint16) << 4
+    base = t.base.astype(np.uint16)[:, None]
+    exp = ((r >> 7) & 0xF) + base
+    out = ((((r >> 11) & 1) << 15) | (exp << 7) | (r & 0x7F)).astype(np.uint16)
+    counts = np.diff(t.esc_ptr.astype(np.int64))
+    rows = np.repeat(np.arange(t.n_out), counts)
+    out[rows, t.esc_idx.astype(np.int64)] = t.esc_val
+    return out
