@@ -201,6 +201,21 @@ typedef struct tvp_gemm_epilogue {
 int w12_gemm_ex(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
                 const tvp_gemm_epilogue* epi, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The same GEMM for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument; the scratch is a library-owned device array of
+ * TVP_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.  The call
+ * allocates nothing.  Shapes whose w12_gemm_workspace() exceeds that size
+ * return TVP_ERR_WORKSPACE (e.g. the wide path at many rows over large
+ * weights); every 27B-like projection and LM head at up to 32 rows fits.
+ * `stream` must belong to the current device (TVP_ERR_ARG otherwise).  All
+ * calls on one GPU share the array, so calls that overlap in time on one
+ * GPU (other streams, other threads) race; nothing in it needs to start at
+ * zero.  Arguments and results otherwise as w12_gemm_ex. */
+#define TVP_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int w12_gemm_ex_noalloc(const uint16_t* x, int64_t m, int64_t ldx, const tvp_w12_packed* w,
+                        const tvp_gemm_epilogue* epi, hipStream_t stream);
+
 /* Packed activation layout, the GEMM's input format for up to 32 rows (and
  * what verify_step produces internally; the pages leave the activation
  * layout open, so it is chosen for the GEMM's MFMA operand loads): bf16 element (row, k) lives at

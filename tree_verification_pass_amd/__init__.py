@@ -103,6 +103,9 @@ _lib_w12_gemm = _sig("w12_gemm", ctypes.c_int,
 _lib_w12_gemm_ex = _sig("w12_gemm_ex", ctypes.c_int,
                         [c_vp, c_i64, c_i64, ctypes.POINTER(TvpW12Packed), ctypes.POINTER(TvpGemmEpilogue),
                          c_vp, c_sz, c_vp])
+_lib_w12_gemm_ex_noalloc = _sig("w12_gemm_ex_noalloc", ctypes.c_int,
+                                [c_vp, c_i64, c_i64, ctypes.POINTER(TvpW12Packed), ctypes.POINTER(TvpGemmEpilogue),
+                                 c_vp])
 _lib_w12_packed_x_elems = _sig("w12_packed_x_elems", c_i64, [c_i64])
 _lib_w12_pack_x = _sig("w12_pack_x", ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp])
 _lib_w12_gemm_resid_norm_workspace = _sig("w12_gemm_resid_norm_workspace", c_sz,
@@ -127,7 +130,7 @@ _lib_verify_step_batched = _sig("verify_step_batched", ctypes.c_int,
 _lib_tvp_read_probe = _sig("tvp_read_probe", ctypes.c_int, [c_vp, c_sz, c_vp, c_vp])
 
 EXPORTED = ("tvp_status_string", "w12_encode_count", "w12_encode", "w12_decode", "w12_validate", "w12_pack_size",
-            "w12_pack_workspace", "w12_pack", "w12_gemm_workspace", "w12_gemm", "w12_gemm_ex",
+            "w12_pack_workspace", "w12_pack", "w12_gemm_workspace", "w12_gemm", "w12_gemm_ex", "w12_gemm_ex_noalloc",
             "w12_packed_x_elems", "w12_pack_x", "w12_gemm_resid_norm_workspace", "w12_gemm_resid_norm",
             "tree_attention_workspace", "tree_attention", "accept_path", "tvp_plan_create",
             "tvp_plan_destroy", "verify_step_workspace", "verify_step", "verify_step_batched",
@@ -325,6 +328,15 @@ def w12_gemm_ex(x: torch.Tensor, w: PackedW12, epi: TvpGemmEpilogue) -> None:
     ws = _ws_gemm.get(need, x.device)
     _check(_lib_w12_gemm_ex(_ptr(x), m, x.stride(0), ctypes.byref(w.desc), ctypes.byref(epi), _ptr(ws),
                             ws.numel(), _stream(x.device)), "w12_gemm_ex")
+
+
+def w12_gemm_ex_noalloc(x: torch.Tensor, m: int, w: PackedW12, epi: TvpGemmEpilogue) -> None:
+    """``w12_gemm_ex`` without a workspace: the library's own per-GPU scratch
+    array (``x`` row-major, or packed when ``epi.x_packed`` is set)."""
+    _dev_check(x)
+    ldx = 0 if epi.x_packed else x.stride(0)
+    _check(_lib_w12_gemm_ex_noalloc(_ptr(x), m, ldx, ctypes.byref(w.desc), ctypes.byref(epi), _stream(x.device)),
+           "w12_gemm_ex_noalloc")
 
 
 def w12_packed_x_elems(k_in: int) -> int:
