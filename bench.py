@@ -80,7 +80,7 @@ def w12_algorithmic_bytes(n_out: int, k_in: int, n_esc: int) -> int:
     return n_out * k_in + n_out * ((k_in + 1) // 2) + n_out + 4 * (n_out + 1) + 4 * n_esc
 
 
-def build_model(cfg, seed: int, s_max: int, max_nodes: int, kv_fn=None):
+def build_model(cfg, seed: int, s_max: int, max_nodes: int, kv_fn=None, with_hi8: bool = False):
     import torch
 
     from synth.configs import gen_embed, gen_final_norm, gen_kv_context, gen_layer, gen_lm_head
@@ -99,7 +99,8 @@ def build_model(cfg, seed: int, s_max: int, max_nodes: int, kv_fn=None):
 
     t0 = time.perf_counter()
     dm = DeviceModel(Dims.of(cfg), gen_embed(cfg, seed, dev), gen_final_norm(cfg, seed, dev),
-                     gen_lm_head(cfg, seed, dev), layer_fn, kv_fn, s_max=s_max, max_nodes=max_nodes)
+                     gen_lm_head(cfg, seed, dev), layer_fn, kv_fn, s_max=s_max, max_nodes=max_nodes,
+                     with_hi8=with_hi8)
     torch.cuda.synchronize()
     log(f"bench: model ready in {time.perf_counter() - t0:.1f} s")
     return dm
@@ -412,6 +413,94 @@ def bench_ar(args, cfg, dm) -> int:
     return 0
 
 
+def bench_tlv(args, cfg) -> int:
+    """Two-level verification on the 27B-like target: the Q pass (the 32-node
+    draft tree through the 8-bit leading views of the weights), the exact
+    pass alone, and whole TLV steps (Q pass, readback of its path and bonus,
+    a re-drafted subtree attached, one exact 32-node pass with commit) at a
+    fixed committed length.  Reports the Q pass's cost as a fraction of an
+    exact step, the bytes each pass streams, and the Q pass's top-1 agreement
+    with the exact pass on the same trees.  The synthetic drafter for the
+    subtree draws best-first trees with uniform tokens (random weights admit
+    no meaningful drafter)."""
+    import torch
+
+    import tree_verification_pass_amd as tvp
+    from synth import best_first_topology
+    from tree_verification_pass_amd.tlv import tlv_step
+
+    s_max = cfg.ctx_len + 64
+    dm = build_model(cfg, args.seed, s_max, cfg.n_nodes, with_hi8=True)
+    trees = make_trees(dm, cfg, args.trees, args.seed + 1)
+    dev = torch.device("cuda:0")
+    out_q = tvp._alloc_out(dm.q_plan, cfg.n_nodes, 1, False)
+    out_e = tvp._alloc_out(dm.plan, cfg.n_nodes, 1, False)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1000.0 / n
+
+    def q_pass(i):
+        tokens, parents = trees[i % len(trees)]
+        tvp.verify_step(dm.q_plan, cfg.ctx_len, tokens, parents, commit=False, out=out_q)
+        int(out_q.n_accepted.item())
+
+    def exact_pass(i):
+        tokens, parents = trees[i % len(trees)]
+        tvp.verify_step(dm.plan, cfg.ctx_len, tokens, parents, commit=False, out=out_e)
+        int(out_e.n_accepted.item())
+
+    rng = np.random.default_rng(args.seed + 7)
+
+    def redraft(q_path, q_bonus):
+        sp = best_first_topology(rng, cfg.n_nodes - len(q_path))[0]
+        st = rng.integers(0, cfg.vocab, len(sp))
+        st[0] = q_bonus
+        return sp, st
+
+    accepted = []
+
+    def tlv(i):
+        tokens, parents = trees[i % len(trees)]
+        r = tlv_step(dm, cfg.ctx_len, tokens, parents, redraft, commit=True)
+        accepted.append(int(r.exact.n_accepted.item()))
+
+    agree = []
+    for i in range(len(trees)):
+        q_pass(i)
+        exact_pass(i)
+        agree.append((out_q.argmax == out_e.argmax).float().mean().item())
+    for fn in (q_pass, exact_pass, tlv):
+        timed(fn, args.warmup)
+    accepted.clear()
+    log(f"bench: timing {args.steps} Q passes, exact passes and TLV steps")
+    ms_q = timed(q_pass, args.steps)
+    ms_e = timed(exact_pass, args.steps)
+    ms_t = timed(tlv, args.steps)
+    q_bytes = dm.stream_bytes(hi8=True)
+    e_bytes = dm.stream_bytes()
+    log(f"bench: Q pass {ms_q:.3f} ms, exact pass {ms_e:.3f} ms (Q / exact = {ms_q / ms_e:.3f}), TLV step "
+        f"{ms_t:.3f} ms; packed weights streamed: {q_bytes / 1e9:.2f} GB (8-bit views) vs {e_bytes / 1e9:.2f} GB")
+    line = {
+        "metric": "W12 two-level verification: Q-pass cost / exact step, TLV steps/s (27B-like, 32-node tree), 1 GPU",
+        "value": round(ms_q / ms_e, 4), "unit": "Q-pass ms / exact-pass ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "ms_q_pass": round(ms_q, 4), "ms_exact_pass": round(ms_e, 4), "ms_tlv_step": round(ms_t, 4),
+        "tlv_steps_per_s": round(1000.0 / ms_t, 3), "mean_accepted_tlv": round(float(np.mean(accepted)), 3),
+        "q_exact_top1_agreement": round(float(np.mean(agree)), 4),
+        "packed_bytes_hi8": int(q_bytes), "packed_bytes_w12": int(e_bytes),
+        "config": {"workload": f"{cfg.name}-like TLV step, {cfg.n_nodes}-node trees, ctx {cfg.ctx_len}",
+                   "drafter": "draft trees from the target's top-4 (p = 0.7); re-drafted subtrees uniform"},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_batched(args, cfg) -> int:
     """Batched verification: 24 requests share a 192-node budget (per-request
     trees of 4-16 nodes, best-first topology, drafts from the target's own
@@ -669,6 +758,8 @@ def main() -> int:
                     help="time the pass at 1, 8, 16 and 32 nodes instead and report c(N) = T(N)/T(1)")
     ap.add_argument("--batched", action="store_true",
                     help="time the batched pass instead (24 requests sharing a 192-node budget)")
+    ap.add_argument("--tlv", action="store_true",
+                    help="time two-level verification (Q pass on the 8-bit weight views + exact pass) instead")
     ap.add_argument("--gemm", action="store_true",
                     help="time the standalone W12 GEMM at the 27B-like shapes and M = 1, 16, 32 instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -708,6 +799,8 @@ def main() -> int:
     cfg = CONFIGS[args.config]
     if args.gemm:
         return bench_gemm(args)
+    if args.tlv:
+        return bench_tlv(args, cfg)
     if args.batched:
         return bench_batched(args, cfg)
     s_max = cfg.ctx_len + 64

@@ -128,16 +128,26 @@ int w12_validate(const uint8_t* base, const uint32_t* esc_ptr, const uint16_t* e
  *                    map_c = d; d % 32 == 0)                                  */
 enum { TVP_CHAN_PLAIN = 0, TVP_CHAN_GATEUP = 1, TVP_CHAN_QKV = 2 };
 
+/* Record format of a packed tensor.  TVP_FMT_W12: the full 12-bit records
+ * (3072-byte tile blocks).  TVP_FMT_HI8: only the 8-bit leading view of each
+ * record, record >> 4 (2048-byte tile blocks), for the Q pass of two-level
+ * verification (SpecPilot summary, section 무엇과 다른가: the Q pass runs on
+ * the 8-bit view of the front of the W12 records): an in-window weight is
+ * read with its low four mantissa bits cleared; escapes stay exact.         */
+enum { TVP_FMT_W12 = 0, TVP_FMT_HI8 = 1 };
+
 typedef struct tvp_w12_packed {
   int64_t n_out, k_in, n_esc;
   int32_t n_tiles, n_kb; /* ceil over 32 packed channels, ceil(k_in/64) */
   int32_t chan_map, map_a, map_b, map_c;
+  int32_t format;        /* TVP_FMT_W12 or TVP_FMT_HI8 */
   void* blob;            /* device, `bytes` long, caller-owned, 256-B aligned */
   size_t bytes;
   size_t off_rec, off_escoff, off_esc, off_b2, off_rowmap; /* offsets in blob */
 } tvp_w12_packed;
 
-/* Fills every field of *p except `blob` for the given shape and map. */
+/* Fills every field of *p except `blob` for the given shape and map
+ * (format TVP_FMT_W12). */
 int w12_pack_size(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, int32_t map_a,
                   int32_t map_b, int32_t map_c, tvp_w12_packed* p);
 
@@ -149,6 +159,14 @@ int w12_pack_size(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, 
  * launched), then the channel map is uploaded. */
 size_t w12_pack_workspace(int64_t n_out, int64_t k_in);
 int w12_pack(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The same two calls for the 8-bit leading view (format TVP_FMT_HI8): the
+ * tiles hold record >> 4 of every weight in the same lane order, the escape
+ * lists are the same.  The GEMM reads such a tensor at up to 32 rows
+ * (TVP_ERR_SHAPE above); w12_pack_workspace sizes the scratch of both. */
+int w12_pack_hi8_size(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, int32_t map_a,
+                      int32_t map_b, int32_t map_c, tvp_w12_packed* p);
+int w12_pack_hi8(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------ W12 GEMM
  * Y[m][n_out] = X[m][k_in] . W^T with bf16 inputs and fp32 accumulation, the

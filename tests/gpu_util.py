@@ -12,7 +12,7 @@ from synth.weights import bf16_bits_numpy
 
 
 def build_pair(cfg: ModelConfig, seed: int, s_max: int, max_nodes: int = 64, gains: str = "random",
-               device="cuda"):
+               device="cuda", with_hi8: bool = False):
     """Returns ``(device_model, oracle_model, oracle_cache)`` for ``cfg``."""
     from tree_verification_pass_amd.model import DeviceModel, Dims
     m = gen_model(cfg, seed, "cpu", gains)
@@ -20,7 +20,8 @@ def build_pair(cfg: ModelConfig, seed: int, s_max: int, max_nodes: int = 64, gai
     dev = torch.device(device)
     dm = DeviceModel(Dims.of(cfg), m.embed.to(dev), m.final_norm.to(dev), m.lm_head.to(dev),
                      lambda l: {k: v.to(dev) for k, v in m.layers[l].items()},
-                     lambda l: (kv[l][0].to(dev), kv[l][1].to(dev)), s_max=s_max, max_nodes=max_nodes)
+                     lambda l: (kv[l][0].to(dev), kv[l][1].to(dev)), s_max=s_max, max_nodes=max_nodes,
+                     with_hi8=with_hi8)
     layers = [{k: bf16_bits_numpy(v) for k, v in layer.items()} for layer in m.layers]
     orc = om.OracleModel.from_bits(om.Dims.of(cfg), bf16_bits_numpy(m.embed), layers,
                                    bf16_bits_numpy(m.final_norm), bf16_bits_numpy(m.lm_head))

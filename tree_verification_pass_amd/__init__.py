@@ -29,6 +29,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 TVP_OK, TVP_ERR_ARG, TVP_ERR_SHAPE, TVP_ERR_TREE = 0, 1, 2, 3
 TVP_ERR_CAPACITY, TVP_ERR_FORMAT, TVP_ERR_WORKSPACE, TVP_ERR_HIP = 4, 5, 6, 7
 TVP_CHAN_PLAIN, TVP_CHAN_GATEUP, TVP_CHAN_QKV = 0, 1, 2
+TVP_FMT_W12, TVP_FMT_HI8 = 0, 1
 TVP_EPI_F32, TVP_EPI_BF16, TVP_EPI_RESID, TVP_EPI_SWIGLU, TVP_EPI_QKV, TVP_EPI_ARGMAX = range(6)
 
 c_i32, c_i64, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
@@ -48,7 +49,7 @@ class TvpW12(ctypes.Structure):
 
 class TvpW12Packed(ctypes.Structure):
     _fields_ = [("n_out", c_i64), ("k_in", c_i64), ("n_esc", c_i64), ("n_tiles", c_i32), ("n_kb", c_i32),
-                ("chan_map", c_i32), ("map_a", c_i32), ("map_b", c_i32), ("map_c", c_i32),
+                ("chan_map", c_i32), ("map_a", c_i32), ("map_b", c_i32), ("map_c", c_i32), ("format", c_i32),
                 ("blob", c_vp), ("bytes", c_sz), ("off_rec", c_sz), ("off_escoff", c_sz),
                 ("off_esc", c_sz), ("off_b2", c_sz), ("off_rowmap", c_sz)]
 
@@ -93,6 +94,10 @@ _lib_w12_decode = _sig("w12_decode", ctypes.c_int, [ctypes.POINTER(TvpW12), c_vp
 _lib_w12_validate = _sig("w12_validate", ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64])
 _lib_w12_pack_size = _sig("w12_pack_size", ctypes.c_int,
                           [c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(TvpW12Packed)])
+_lib_w12_pack_hi8_size = _sig("w12_pack_hi8_size", ctypes.c_int,
+                              [c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(TvpW12Packed)])
+_lib_w12_pack_hi8 = _sig("w12_pack_hi8", ctypes.c_int,
+                         [ctypes.POINTER(TvpW12), ctypes.POINTER(TvpW12Packed), c_vp, c_sz, c_vp])
 _lib_w12_pack_workspace = _sig("w12_pack_workspace", c_sz, [c_i64, c_i64])
 _lib_w12_pack = _sig("w12_pack", ctypes.c_int,
                      [ctypes.POINTER(TvpW12), ctypes.POINTER(TvpW12Packed), c_vp, c_sz, c_vp])
@@ -130,7 +135,7 @@ _lib_verify_step_batched = _sig("verify_step_batched", ctypes.c_int,
 _lib_tvp_read_probe = _sig("tvp_read_probe", ctypes.c_int, [c_vp, c_sz, c_vp, c_vp])
 
 EXPORTED = ("tvp_status_string", "w12_encode_count", "w12_encode", "w12_decode", "w12_validate", "w12_pack_size",
-            "w12_pack_workspace", "w12_pack", "w12_gemm_workspace", "w12_gemm", "w12_gemm_ex", "w12_gemm_ex_noalloc",
+            "w12_pack_workspace", "w12_pack", "w12_pack_hi8_size", "w12_pack_hi8", "w12_gemm_workspace", "w12_gemm", "w12_gemm_ex", "w12_gemm_ex_noalloc",
             "w12_packed_x_elems", "w12_pack_x", "w12_gemm_resid_norm_workspace", "w12_gemm_resid_norm",
             "tree_attention_workspace", "tree_attention", "accept_path", "tvp_plan_create",
             "tvp_plan_destroy", "verify_step_workspace", "verify_step", "verify_step_batched",
@@ -288,15 +293,20 @@ def w12_pack_size(n_out: int, k_in: int, n_esc: int, chan_map: int = TVP_CHAN_PL
 
 
 def w12_pack(t: W12Tensor, chan_map: int = TVP_CHAN_PLAIN, map_a: int = 0, map_b: int = 0,
-             map_c: int = 0) -> PackedW12:
+             map_c: int = 0, fmt: int = TVP_FMT_W12) -> PackedW12:
+    """Tiled GPU copy of ``t``: the full records (TVP_FMT_W12) or only their
+    8-bit leading view (TVP_FMT_HI8, the Q pass of two-level verification)."""
     dev = t.hi.device
-    p = w12_pack_size(t.n_out, t.k_in, t.n_esc, chan_map, map_a, map_b, map_c)
+    p = TvpW12Packed()
+    size_fn, pack_fn = ((_lib_w12_pack_size, _lib_w12_pack) if fmt == TVP_FMT_W12
+                        else (_lib_w12_pack_hi8_size, _lib_w12_pack_hi8))
+    _check(size_fn(t.n_out, t.k_in, t.n_esc, chan_map, map_a, map_b, map_c, ctypes.byref(p)), "w12_pack_size")
     blob = torch.empty(int(p.bytes), dtype=torch.uint8, device=dev)
     p.blob = blob.data_ptr()
     need = _lib_w12_pack_workspace(t.n_out, t.k_in)
     ws = torch.empty(int(need), dtype=torch.uint8, device=dev)
     s = t.struct()
-    _check(_lib_w12_pack(ctypes.byref(s), ctypes.byref(p), _ptr(ws), need, _stream(dev)), "w12_pack")
+    _check(pack_fn(ctypes.byref(s), ctypes.byref(p), _ptr(ws), need, _stream(dev)), "w12_pack")
     torch.cuda.current_stream(dev).synchronize()
     return PackedW12(p, blob)
 

@@ -27,6 +27,10 @@ namespace tvp {
 constexpr int kTileN = 32;      // channels per packed tile
 constexpr int kBlockK = 64;     // k per packed block
 constexpr int kBlockBytes = 3072;  // 32 x 64 x 12 bits
+constexpr int kBlockBytesHi8 = 2048;  // 32 x 64 x 8 bits: the 8-bit leading view of the records
+
+// Bytes of one packed tile block in the tensor's format.
+__host__ __device__ inline int block_bytes(int32_t format) { return format == TVP_FMT_HI8 ? kBlockBytesHi8 : kBlockBytes; }
 
 // Record block (tile t, k-block j) of a packed weight, k-block-major.
 __host__ __device__ inline int64_t rec_block(int64_t t, int64_t j, int64_t n_tiles) { return j * n_tiles + t; }

@@ -208,6 +208,13 @@ __global__ __launch_bounds__(64) void pack_count_kernel(const uint32_t* __restri
   if (c == 0) counts[unit] = cnt;
 }
 
+// HI8 (the 8-bit leading view): each lane owns 32 bytes, dwords D[0..7] at
+// byte offsets s*1024 + l*16 + 4*i (s = i / 4), D[2s+q] holding the hi bytes
+// (record >> 4) of w[s][4q..4q+3] in the same byte order (4q, 4q+2, 4q+1,
+// 4q+3), so masking with 0x00FF00FF (after a shift by 8 for the odd pair)
+// spreads a pair into two halfwords.  Decode of such a pair x:
+//   (((x & 0x007F007F) << 4) + (base<<7)*0x10001) | ((x & 0x00800080) << 8).
+template <bool HI8>
 __global__ __launch_bounds__(64) void pack_write_kernel(const uint8_t* __restrict__ hi,
                                                         const uint8_t* __restrict__ lo,
                                                         const uint8_t* __restrict__ base,
@@ -257,9 +264,28 @@ __global__ __launch_bounds__(64) void pack_write_kernel(const uint8_t* __restric
     D[8 + s] = hn;
   }
   const int64_t n_tiles = (int64_t)gridDim.x / n_kb;  // one workgroup per (tile, k-block)
-  uint4* blk = (uint4*)(rec_out + rec_block(t, j, n_tiles) * (int64_t)kBlockBytes);
+  if constexpr (HI8) {
+    uint32_t Q[8];
 #pragma unroll
-  for (int s = 0; s < 3; ++s) blk[s * 64 + l] = make_uint4(D[4 * s], D[4 * s + 1], D[4 * s + 2], D[4 * s + 3]);
+    for (int s = 0; s < 4; ++s) {
+      uint32_t h8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t k = 64LL * j + 16 * s + 8 * h + i;
+        h8[i] = (r >= 0 && k < k_in) ? (uint32_t)hi[(int64_t)r * k_in + k] : 0u;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        Q[2 * s + q] = h8[4 * q] | (h8[4 * q + 2] << 8) | (h8[4 * q + 1] << 16) | (h8[4 * q + 3] << 24);
+    }
+    uint4* blk = (uint4*)(rec_out + rec_block(t, j, n_tiles) * (int64_t)kBlockBytesHi8);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) blk[s * 64 + l] = make_uint4(Q[4 * s], Q[4 * s + 1], Q[4 * s + 2], Q[4 * s + 3]);
+  } else {
+    uint4* blk = (uint4*)(rec_out + rec_block(t, j, n_tiles) * (int64_t)kBlockBytes);
+#pragma unroll
+    for (int s = 0; s < 3; ++s) blk[s * 64 + l] = make_uint4(D[4 * s], D[4 * s + 1], D[4 * s + 2], D[4 * s + 3]);
+  }
 
   // escape entries, channel by channel in packed order, ascending column
   uint32_t lo0 = 0, lo1 = 0;
@@ -410,8 +436,8 @@ int w12_validate(const uint8_t* base, const uint32_t* esc_ptr, const uint16_t* e
   return TVP_OK;
 }
 
-int w12_pack_size(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, int32_t map_a,
-                  int32_t map_b, int32_t map_c, tvp_w12_packed* p) {
+static int pack_size_fmt(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, int32_t map_a,
+                         int32_t map_b, int32_t map_c, int32_t format, tvp_w12_packed* p) {
   if (!p || n_out < 1 || k_in < 0 || n_esc < 0) return TVP_ERR_ARG;
   if (k_in > 65536) return TVP_ERR_SHAPE;
   int64_t n_tiles;
@@ -439,9 +465,10 @@ int w12_pack_size(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, 
   p->map_a = map_a;
   p->map_b = map_b;
   p->map_c = map_c;
+  p->format = format;
   size_t off = 0;
   p->off_rec = off;
-  off = align_up(off + (size_t)units * kBlockBytes, 256);
+  off = align_up(off + (size_t)units * block_bytes(format), 256);
   p->off_escoff = off;
   off = align_up(off + (size_t)(units + 1) * 4, 256);
   p->off_esc = off;
@@ -454,14 +481,26 @@ int w12_pack_size(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, 
   return TVP_OK;
 }
 
+int w12_pack_size(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, int32_t map_a,
+                  int32_t map_b, int32_t map_c, tvp_w12_packed* p) {
+  return pack_size_fmt(n_out, k_in, n_esc, chan_map, map_a, map_b, map_c, TVP_FMT_W12, p);
+}
+
+int w12_pack_hi8_size(int64_t n_out, int64_t k_in, int64_t n_esc, int32_t chan_map, int32_t map_a,
+                      int32_t map_b, int32_t map_c, tvp_w12_packed* p) {
+  return pack_size_fmt(n_out, k_in, n_esc, chan_map, map_a, map_b, map_c, TVP_FMT_HI8, p);
+}
+
 size_t w12_pack_workspace(int64_t n_out, int64_t k_in) {
   // per-unit escape counts for the worst map (GATEUP/QKV add at most a few tiles)
   const int64_t tiles = ceil_div(n_out, 16) + 64;
   return align_up((size_t)(tiles * ceil_div(k_in, kBlockK) + 1) * 4, 256);
 }
 
-int w12_pack(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int pack_fmt(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hipStream_t stream,
+                    int32_t format) {
   if (!t || !p || !p->blob) return TVP_ERR_ARG;
+  if (p->format != format) return TVP_ERR_FORMAT;
   if (t->n_out != p->n_out || t->k_in != p->k_in || t->n_esc != p->n_esc) return TVP_ERR_SHAPE;
   const int64_t units = (int64_t)p->n_tiles * p->n_kb;
   if (!ws || ws_bytes < (size_t)(units + 1) * 4 || ws_bytes < w12_pack_workspace(t->n_out, t->k_in))
@@ -504,11 +543,24 @@ int w12_pack(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hip
   TVP_LAUNCH_CHECK();
   scan_u32_kernel<<<1, 1024, 0, stream>>>(counts, units, escoff);
   TVP_LAUNCH_CHECK();
-  pack_write_kernel<<<dim3((unsigned)units), dim3(64), 0, stream>>>(
-      t->hi, t->lo, t->base, t->esc_ptr, t->esc_idx, t->esc_val, rowmap, t->k_in, p->n_kb, escoff,
-      blob + p->off_rec, (uint32_t*)(blob + p->off_esc));
+  if (format == TVP_FMT_HI8)
+    pack_write_kernel<true><<<dim3((unsigned)units), dim3(64), 0, stream>>>(
+        t->hi, t->lo, t->base, t->esc_ptr, t->esc_idx, t->esc_val, rowmap, t->k_in, p->n_kb, escoff,
+        blob + p->off_rec, (uint32_t*)(blob + p->off_esc));
+  else
+    pack_write_kernel<false><<<dim3((unsigned)units), dim3(64), 0, stream>>>(
+        t->hi, t->lo, t->base, t->esc_ptr, t->esc_idx, t->esc_val, rowmap, t->k_in, p->n_kb, escoff,
+        blob + p->off_rec, (uint32_t*)(blob + p->off_esc));
   TVP_LAUNCH_CHECK();
   return TVP_OK;
+}
+
+int w12_pack(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return pack_fmt(t, p, ws, ws_bytes, stream, TVP_FMT_W12);
+}
+
+int w12_pack_hi8(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return pack_fmt(t, p, ws, ws_bytes, stream, TVP_FMT_HI8);
 }
 
 }  // extern "C"

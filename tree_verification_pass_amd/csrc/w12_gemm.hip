@@ -48,6 +48,7 @@ struct GemmArgs {
   unsigned long long* keys;  // ARGMAX: [slot][m] packed (value, -id) maxima, one slot per workgroup that
                              // applies the epilogue (every slot written, no zeroing)
   int key_slots;
+  int hi8;  // records are the 8-bit leading view (TVP_FMT_HI8): 2048-byte tile blocks
   int mode;
   void* y;
   int64_t ldy;
@@ -106,6 +107,23 @@ __device__ inline void decode_block(const uint4 (&r)[3], uint32_t b2, uint32_t (
       const uint32_t L = lb[2 * s + q];
       o[4 * s + 2 * q] = (rotl32(hn[s], 8 * q) & 0x87008700u) + (L & 0x00FF00FFu) + b2;
       o[4 * s + 2 * q + 1] = (rotl32(hn[s], 8 * q + 4) & 0x87008700u) + ((L >> 8) & 0x00FF00FFu) + b2;
+    }
+  }
+}
+
+// The 8-bit leading view (record >> 4 per weight): 8 dwords of one lane ->
+// 16 bf16-pair dwords, the low four mantissa bits zero.  Each dword holds the
+// bytes of weights (4q, 4q+2, 4q+1, 4q+3); sign to bit 15 of each halfword,
+// offset and top mantissa bits shifted into place, plus the window base.
+__device__ inline void decode_block_hi8(const uint4 (&r)[3], uint32_t b2, uint32_t (&o)[16]) {
+  const uint32_t D[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t d = D[2 * s + q];
+      o[4 * s + 2 * q] = (((d & 0x007F007Fu) << 4) + b2) | ((d & 0x00800080u) << 8);
+      o[4 * s + 2 * q + 1] = (((d >> 4) & 0x07F007F0u) + b2) | (d & 0x80008000u);
     }
   }
 }
@@ -300,8 +318,10 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned lon
 // with readlane, so no load in the loop depends on another.  At the end the
 // waves' fp32 partial tiles meet in LDS and are summed in wave order: no
 // global partial sums, no atomics, no device-scope fences.
-template <int MT, int TPW, int RD, int MODE>
+template <int MT, int TPW, int RD, int MODE, bool HI8>
 __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
+  constexpr int NQ = HI8 ? 2 : 3;  // 16-byte pieces per lane of one tile block
+  constexpr int BB = HI8 ? kBlockBytesHi8 : kBlockBytes;
   constexpr int NACC = MT == 32 ? 16 : 4;
   constexpr int NCH = MT == 32 ? 1 : 2;
   constexpr int KS = MT == 32 ? 4 : 2;  // MFMA K-steps per 64-column block
@@ -372,7 +392,7 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
   const bool ragged_tail = nblk > 0 && kb1 == a.n_kb && (a.k_in & 63) != 0;
   const int nfast = nblk - (ragged_tail ? 1 : 0);
 
-  uint4 R[RD][TPW][3];
+  uint4 R[RD][TPW][3] = {};  // HI8 fills two of the three pieces
   uint4 A[RD][KS];
   uint32_t E[RD][TPW];
 
@@ -380,9 +400,9 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
     const int j = kb0 + i;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const uint4* blk = (const uint4*)(a.rec + rec_block(tt[t], j, a.n_tiles) * kBlockBytes);
+      const uint4* blk = (const uint4*)(a.rec + rec_block(tt[t], j, a.n_tiles) * BB);
 #pragma unroll
-      for (int q = 0; q < 3; ++q) R[slot][t][q] = load_nt(blk + q * 64 + lane);
+      for (int q = 0; q < NQ; ++q) R[slot][t][q] = load_nt(blk + q * 64 + lane);
     }
   };
   auto issue_esc = [&](int i, int slot) {
@@ -430,7 +450,8 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       uint32_t o[16];
-      decode_block(R[slot][t], b2v[t], o);
+      if constexpr (HI8) decode_block_hi8(R[slot][t], b2v[t], o);
+      else decode_block(R[slot][t], b2v[t], o);
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         scr[wave][t][64 * s + lane] = make_uint4(o[4 * s], o[4 * s + 1], o[4 * s + 2], o[4 * s + 3]);
@@ -1060,19 +1081,25 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
   return p;
 }
 
-template <int MT, int TPW, int RD>
-static void launch_skinny(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
+template <int MT, int TPW, int RD, bool HI8>
+static void launch_skinny_fmt(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.grid), block((unsigned)(p.KW * 64));
   const size_t lds = (size_t)p.KW * TPW * 4096;
   switch (a.mode) {
-    case TVP_EPI_F32: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_F32><<<grid, block, lds, stream>>>(a); break;
-    case TVP_EPI_BF16: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_BF16><<<grid, block, lds, stream>>>(a); break;
-    case TVP_EPI_RESID: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_RESID><<<grid, block, lds, stream>>>(a); break;
-    case TVP_EPI_SWIGLU: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_SWIGLU><<<grid, block, lds, stream>>>(a); break;
-    case TVP_EPI_QKV: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_QKV><<<grid, block, lds, stream>>>(a); break;
-    case kEpiPartial: w12_skinny_kernel<MT, TPW, RD, kEpiPartial><<<grid, block, lds, stream>>>(a); break;
-    default: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_ARGMAX><<<grid, block, lds, stream>>>(a); break;
+    case TVP_EPI_F32: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_F32, HI8><<<grid, block, lds, stream>>>(a); break;
+    case TVP_EPI_BF16: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_BF16, HI8><<<grid, block, lds, stream>>>(a); break;
+    case TVP_EPI_RESID: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_RESID, HI8><<<grid, block, lds, stream>>>(a); break;
+    case TVP_EPI_SWIGLU: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_SWIGLU, HI8><<<grid, block, lds, stream>>>(a); break;
+    case TVP_EPI_QKV: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_QKV, HI8><<<grid, block, lds, stream>>>(a); break;
+    case kEpiPartial: w12_skinny_kernel<MT, TPW, RD, kEpiPartial, HI8><<<grid, block, lds, stream>>>(a); break;
+    default: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_ARGMAX, HI8><<<grid, block, lds, stream>>>(a); break;
   }
+}
+
+template <int MT, int TPW, int RD>
+static void launch_skinny(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
+  if (a.hi8) launch_skinny_fmt<MT, TPW, RD, true>(a, p, stream);
+  else launch_skinny_fmt<MT, TPW, RD, false>(a, p, stream);
   if (p.rem_groups > 0) {  // launch errors of both are read by the caller's check
     const dim3 fgrid((unsigned)(a.n_tiles - p.full_groups * TPW));
     switch (a.mode) {
@@ -1158,6 +1185,8 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
   if (ksplit > 1 && epi->mode != kEpiPartial) return TVP_ERR_ARG;
   const GemmPlan p = make_plan(m, w, ksplit, epi->mode != TVP_EPI_ARGMAX);
+  if (w->format != TVP_FMT_W12 && w->format != TVP_FMT_HI8) return TVP_ERR_FORMAT;
+  if (w->format == TVP_FMT_HI8 && !p.skinny) return TVP_ERR_SHAPE;  // the 8-bit view: up to 32 rows
   if (xp) {
     if (!p.skinny || ((uintptr_t)xp) % 16 != 0) return TVP_ERR_ARG;
   } else if (w->k_in > 0) {
@@ -1176,6 +1205,7 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
     TVP_LAUNCH_CHECK();
     xp = dst;
   }
+  a.hi8 = w->format == TVP_FMT_HI8 ? 1 : 0;
   a.x = x;
   a.xp = xp;
   a.y_packed = y_packed;

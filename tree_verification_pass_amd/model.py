@@ -15,8 +15,8 @@ from typing import Callable, Dict, List, Optional
 
 import torch
 
-from . import (TVP_CHAN_GATEUP, TVP_CHAN_PLAIN, TVP_CHAN_QKV, PackedW12, Plan, TvpLayer, TvpModelDesc,
-               W12Tensor, tvp_plan_create, w12_encode, w12_pack)
+from . import (TVP_CHAN_GATEUP, TVP_CHAN_PLAIN, TVP_CHAN_QKV, TVP_FMT_HI8, TVP_FMT_W12, PackedW12, Plan,
+               TvpLayer, TvpModelDesc, W12Tensor, tvp_plan_create, w12_encode, w12_pack)
 
 
 @dataclass(frozen=True)
@@ -48,20 +48,28 @@ class DeviceLayer:
     k_cache: torch.Tensor
     v_cache: torch.Tensor
     canonical: Dict[str, W12Tensor] = field(default_factory=dict)
+    hi8: Dict[str, PackedW12] = field(default_factory=dict)  # 8-bit leading views (Q pass), when built
 
 
-def pack_linear(w: torch.Tensor, name: str, dims: Dims, keep: Optional[Dict[str, W12Tensor]] = None
-                ) -> PackedW12:
+def _pack(t: W12Tensor, name: str, dims: Dims, fmt: int) -> PackedW12:
+    if name == "wqkv":
+        return w12_pack(t, TVP_CHAN_QKV, dims.n_heads, dims.n_kv_heads, dims.head_dim, fmt=fmt)
+    if name == "wgu":
+        return w12_pack(t, TVP_CHAN_GATEUP, dims.ffn, fmt=fmt)
+    return w12_pack(t, TVP_CHAN_PLAIN, fmt=fmt)
+
+
+def pack_linear(w: torch.Tensor, name: str, dims: Dims, keep: Optional[Dict[str, W12Tensor]] = None,
+                hi8: Optional[Dict[str, PackedW12]] = None) -> PackedW12:
     """W12-encode one bf16 ``[out, in]`` weight on the device and pack it with the
-    channel map its fused epilogue needs."""
+    channel map its fused epilogue needs (and, when ``hi8`` is given, a packed
+    copy of its 8-bit leading view under the same name)."""
     t = w12_encode(w.contiguous())
     if keep is not None:
         keep[name] = t
-    if name == "wqkv":
-        return w12_pack(t, TVP_CHAN_QKV, dims.n_heads, dims.n_kv_heads, dims.head_dim)
-    if name == "wgu":
-        return w12_pack(t, TVP_CHAN_GATEUP, dims.ffn)
-    return w12_pack(t, TVP_CHAN_PLAIN)
+    if hi8 is not None:
+        hi8[name] = _pack(t, name, dims, TVP_FMT_HI8)
+    return _pack(t, name, dims, TVP_FMT_W12)
 
 
 class DeviceModel:
@@ -70,49 +78,62 @@ class DeviceModel:
     ``layer_fn(l)`` returns the bf16 tensors of layer ``l`` (``wqkv, wo, wgu,
     wdown, attn_norm, ffn_norm``) on the device; ``kv_fn(l)`` returns that
     layer's K and V caches ``[n_kv_heads, s_max, head_dim]`` (context filled).
+    With ``with_hi8`` every weight also gets a packed copy of its 8-bit leading
+    view, and ``q_plan`` is the plan of the Q pass of two-level verification
+    (same embedding, norms and KV caches; up to 32 nodes).
     """
 
     def __init__(self, dims: Dims, embed: torch.Tensor, final_norm: torch.Tensor, lm_head: torch.Tensor,
                  layer_fn: Callable[[int], Dict[str, torch.Tensor]],
                  kv_fn: Callable[[int], tuple], s_max: int, max_nodes: int = 32,
-                 keep_canonical: bool = False):
+                 keep_canonical: bool = False, with_hi8: bool = False):
         self.dims = dims
         self.s_max = s_max
         self.device = embed.device
         self.embed = embed.contiguous()
         self.final_norm = final_norm.contiguous()
         self.canonical_lm: Dict[str, W12Tensor] = {}
-        self.lm_head = pack_linear(lm_head, "lm_head", dims, self.canonical_lm if keep_canonical else None)
+        self.hi8_lm: Dict[str, PackedW12] = {}
+        self.lm_head = pack_linear(lm_head, "lm_head", dims, self.canonical_lm if keep_canonical else None,
+                                   self.hi8_lm if with_hi8 else None)
         self.layers: List[DeviceLayer] = []
         for layer in range(dims.n_layers):
             src = layer_fn(layer)
             keep: Dict[str, W12Tensor] = {}
-            packed = {k: pack_linear(src[k], k, dims, keep if keep_canonical else None)
+            hi8: Dict[str, PackedW12] = {}
+            packed = {k: pack_linear(src[k], k, dims, keep if keep_canonical else None, hi8 if with_hi8 else None)
                       for k in ("wqkv", "wo", "wgu", "wdown")}
             kc, vc = kv_fn(layer)
             self.layers.append(DeviceLayer(packed["wqkv"], packed["wo"], packed["wgu"], packed["wdown"],
                                            src["attn_norm"].contiguous(), src["ffn_norm"].contiguous(),
-                                           kc.contiguous(), vc.contiguous(), keep))
+                                           kc.contiguous(), vc.contiguous(), keep, hi8))
             del src
         self.plan = self._make_plan(max_nodes)
+        self.q_plan = self._make_plan(min(max_nodes, 32), hi8=True) if with_hi8 else None
 
-    def _make_plan(self, max_nodes: int) -> Plan:
+    def _make_plan(self, max_nodes: int, hi8: bool = False) -> Plan:
         d = self.dims
         arr = (TvpLayer * d.n_layers)()
-        keep = [self.embed, self.final_norm, self.lm_head.blob]
+        lm = self.hi8_lm["lm_head"] if hi8 else self.lm_head
+        keep = [self.embed, self.final_norm, lm.blob]
         for i, L in enumerate(self.layers):
-            arr[i] = TvpLayer(L.wqkv.desc, L.wo.desc, L.wgu.desc, L.wdown.desc, L.attn_norm.data_ptr(),
+            w = L.hi8 if hi8 else {"wqkv": L.wqkv, "wo": L.wo, "wgu": L.wgu, "wdown": L.wdown}
+            arr[i] = TvpLayer(w["wqkv"].desc, w["wo"].desc, w["wgu"].desc, w["wdown"].desc, L.attn_norm.data_ptr(),
                               L.ffn_norm.data_ptr(), L.k_cache.data_ptr(), L.v_cache.data_ptr())
-            keep += [L.wqkv.blob, L.wo.blob, L.wgu.blob, L.wdown.blob, L.attn_norm, L.ffn_norm, L.k_cache,
-                     L.v_cache]
+            keep += [w["wqkv"].blob, w["wo"].blob, w["wgu"].blob, w["wdown"].blob, L.attn_norm, L.ffn_norm,
+                     L.k_cache, L.v_cache]
         desc = TvpModelDesc(d.n_layers, d.hidden, d.n_heads, d.n_kv_heads, d.head_dim, d.ffn, d.vocab,
                             d.rope_theta, d.norm_eps, self.s_max, self.embed.data_ptr(),
-                            self.final_norm.data_ptr(), self.lm_head.desc,
+                            self.final_norm.data_ptr(), lm.desc,
                             ctypes.cast(arr, ctypes.POINTER(TvpLayer)))
         return tvp_plan_create(desc, arr, max_nodes, keep)
 
-    def stream_bytes(self) -> int:
-        """W12 bytes one pass streams (packed records, escapes and per-channel data)."""
+    def stream_bytes(self, hi8: bool = False) -> int:
+        """Packed bytes one pass streams (records, escapes and per-channel data),
+        of the W12 copies or of the 8-bit views."""
+        if hi8:
+            return self.hi8_lm["lm_head"].stream_bytes() + sum(p.stream_bytes() for L in self.layers
+                                                                for p in L.hi8.values())
         total = self.lm_head.stream_bytes()
         for L in self.layers:
             total += L.wqkv.stream_bytes() + L.wo.stream_bytes() + L.wgu.stream_bytes() + L.wdown.stream_bytes()
