@@ -16,6 +16,9 @@ What it computes is written out from the pages' description of the method
                  "what it is": the target checks the drafter's tokens in one
                  forward pass), plus the definition-level per-path variant;
 * ``accept``  -- the matched path and bonus token (section 무엇과 다른가);
+* ``lmhead_i8`` -- the LM head on INT8 weights with a Cauchy-Schwarz
+                 certified candidate filter, exact argmax kept (section
+                 무엇과 다른가);
 * ``tlv``     -- two-level verification: a Q pass on the 8-bit leading view
                  of the W12 records, then one exact pass over the matched
                  path, the bonus token and a re-drafted subtree (section
@@ -31,4 +34,4 @@ the structural ones listed there (library-routine equivalences, closed forms,
 special cases), which is stated where it matters.
 """
 
-from . import bf16, w12, accept, model, tlv  # noqa: F401
+from . import bf16, w12, accept, model, tlv, lmhead_i8  # noqa: F401
