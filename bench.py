@@ -722,6 +722,77 @@ def bench_gemm(args) -> int:
     return 0
 
 
+def bench_lmhead(args) -> int:
+    """The 27B-like LM head (151936 x 5120) at 32 and 1 rows: the W12 head
+    (skinny GEMM with the argmax epilogue, plus its finalize) against the
+    INT8 head with the Cauchy-Schwarz certified candidate filter (norms,
+    GEMM on the int8 tiles with the approximate-logit epilogue, threshold,
+    candidate scan with exact rescoring from the canonical W12 rows, result).
+    Each call is timed with HIP events on its stream (median of the timed
+    calls); both return the exact greedy token of every row."""
+    import torch
+
+    import tree_verification_pass_amd as tvp
+    from synth import gen_linear_bf16, make_generator
+    from synth.configs import CONFIGS, LARGE_RECIPE
+    from synth.weights import sub_seed
+
+    cfg = CONFIGS["27b"]
+    V, H = cfg.vocab, cfg.hidden
+    dev = torch.device("cuda:0")
+    w = gen_linear_bf16(make_generator(sub_seed(args.seed, 95), dev), V, H, LARGE_RECIPE, device=dev)
+    exact = tvp.w12_encode(w)
+    pw = tvp.w12_pack(exact)
+    head = tvp.lmhead_i8_encode(w)
+    del w
+    torch.cuda.synchronize()
+    rows = {}
+    for m in (32, 1):
+        x = torch.randn(m, H, generator=make_generator(sub_seed(args.seed, 96, m))).to(torch.bfloat16).to(dev)
+        xp = tvp.w12_pack_x(x)
+        am = torch.zeros(m, dtype=torch.int32, device=dev)
+        epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_ARGMAX, argmax=am.data_ptr())
+
+        def w12_call():
+            tvp.w12_gemm_px(xp, m, pw, epi)
+
+        def i8_call():
+            return tvp.lmhead_i8_argmax(xp, m, head, exact)
+
+        res = {}
+        for name, fn in (("w12", w12_call), ("i8", i8_call)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+            for s, e in ev:
+                s.record()
+                fn()
+                e.record()
+            torch.cuda.synchronize()
+            res[name] = float(np.median([s.elapsed_time(e) for s, e in ev])) * 1000.0
+        a8, nc, _ = i8_call()
+        w12_call()
+        torch.cuda.synchronize()
+        rows[m] = {"us_w12_head": round(res["w12"], 1), "us_i8_head": round(res["i8"], 1),
+                   "i8_over_w12": round(res["i8"] / res["w12"], 3),
+                   "same_argmax_rows": int((a8 == am).sum().item()),
+                   "candidates_mean": round(float(nc.float().mean().item()), 2), "candidates_max": int(nc.max().item())}
+        log(f"bench: LM head m={m}: W12 {res['w12']:.1f} us, INT8 certified {res['i8']:.1f} us, "
+            f"candidates mean {rows[m]['candidates_mean']}, same argmax on {rows[m]['same_argmax_rows']}/{m} rows")
+    line = {
+        "metric": "LM head (151936x5120) greedy token: W12 head vs INT8 head with certified candidate filter, 1 GPU",
+        "value": rows[32]["us_i8_head"], "unit": "us per call (INT8 certified head, 32 rows)", "n_gpus": 1,
+        "steps": 20, "warmup": 3, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "bytes_w12_head": int(pw.stream_bytes()), "bytes_i8_head": int(head.stream_bytes()),
+        "rows": {str(k): v for k, v in rows.items()},
+        "config": {"workload": "27B-like LM head, 151936 x 5120, large-recipe weights, X bf16 N(0,1)"},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def gemm_cpu_baseline(w_bits):
     """The oracle (untuned) on the 17408 x 5120 shape at 32 rows: exact W12
     decode of the canonical tensor plus the fp64 product (the encode is the
@@ -758,6 +829,8 @@ def main() -> int:
                     help="time the pass at 1, 8, 16 and 32 nodes instead and report c(N) = T(N)/T(1)")
     ap.add_argument("--batched", action="store_true",
                     help="time the batched pass instead (24 requests sharing a 192-node budget)")
+    ap.add_argument("--lmhead", action="store_true",
+                    help="time the W12 LM head against the INT8 head with the certified candidate filter instead")
     ap.add_argument("--tlv", action="store_true",
                     help="time two-level verification (Q pass on the 8-bit weight views + exact pass) instead")
     ap.add_argument("--gemm", action="store_true",
@@ -801,6 +874,8 @@ def main() -> int:
         return bench_gemm(args)
     if args.tlv:
         return bench_tlv(args, cfg)
+    if args.lmhead:
+        return bench_lmhead(args)
     if args.batched:
         return bench_batched(args, cfg)
     s_max = cfg.ctx_len + 64

@@ -266,6 +266,50 @@ int w12_gemm_resid_norm(const uint16_t* xp, int64_t m, const tvp_w12_packed* w, 
                         const uint16_t* gain, float eps, uint16_t* yp, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* ------------------------------------------------ INT8 certified LM head
+ * SpecPilot summary, section 무엇과 다른가: the LM head can filter candidate
+ * tokens with INT8 weights and a Cauchy-Schwarz error bound while keeping the
+ * exact argmax.  Per vocabulary row v: the 8 largest magnitudes (ties to the
+ * smaller column) are escapes, carried as bf16(w / s_v); the rest are
+ * q = clip(rint(fp32(w) / s_v), -127, 127) with s_v = fp32(t_v / 127), t_v the
+ * largest remaining magnitude (1 when it is 0); r_v = ||W_v - s_v B_v||_2 (B_v:
+ * the int8 values with the escapes in place) rounded up to fp32, and r_eff_v
+ * = r_v plus a bound of the fp32 accumulation error of the approximate logit.
+ * The argmax computes a_v = f . s_v B_v (bf16 MFMA on the int8 values, fp32
+ * accumulation), tau = max_v (a_v - ||f|| r_eff_v), and exact logits -- from
+ * the canonical W12 rows of the same weights -- only for the v with
+ * a_v + ||f|| r_eff_v >= tau, a set that always holds the exact argmax.
+ * Keeping the largest magnitudes out of the scale follows W12's escapes: on
+ * weights with rare large outliers, a scale set by the outliers would leave
+ * a large share of the vocabulary as candidates.                            */
+typedef struct tvp_lmhead_i8 {
+  int64_t vocab, k_in;  /* k_in <= 16384 */
+  int8_t* q;            /* device [vocab][k_in], 0 at the escaped columns */
+  float* scale;         /* device [vocab] */
+  uint16_t* esc_col;    /* device [vocab][8], ascending */
+  uint16_t* esc_val;    /* device [vocab][8], bf16 of w / scale */
+  float* r;             /* device [vocab] */
+  float* r_eff;         /* device [vocab] */
+  tvp_w12_packed tiles; /* the int8 values in the GEMM's tiled layout (blob caller-owned) */
+} tvp_lmhead_i8;
+
+/* Sizes the tiles (every field of *p but `blob`). */
+int lmhead_i8_tiles_size(int64_t vocab, int64_t k_in, tvp_w12_packed* p);
+/* Encodes device bf16 `w` [vocab][k_in] into every array of *h and packs the
+ * tiles (h->tiles from lmhead_i8_tiles_size, its blob set).  Device scratch
+ * of lmhead_i8_encode_workspace() bytes.  Synchronises `stream` (offline
+ * conversion, like w12_pack). */
+size_t lmhead_i8_encode_workspace(int64_t vocab, int64_t k_in);
+int lmhead_i8_encode(const uint16_t* w, tvp_lmhead_i8* h, void* ws, size_t ws_bytes, hipStream_t stream);
+/* Greedy token of every row of the packed activations xp (m <= 32 rows of
+ * k_in): argmax (int32 [m], ties to the smallest id) and the number of
+ * certified candidates per row (int32 [m]); `approx` (optional fp32
+ * [m][vocab]) receives the approximate logits.  `exact` is the canonical W12
+ * tensor of the same weights.  Scratch: lmhead_i8_argmax_workspace() bytes. */
+size_t lmhead_i8_argmax_workspace(int64_t m, const tvp_lmhead_i8* h);
+int lmhead_i8_argmax(const uint16_t* xp, int64_t m, const tvp_lmhead_i8* h, const tvp_w12* exact, int32_t* argmax,
+                     int32_t* n_cand, float* approx, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------- tree attention
  * Attention of n draft-tree nodes over a committed context and their own
  * ancestors (SpecPilot summary, section 전제와 한계 names tree attention as

@@ -54,6 +54,11 @@ class TvpW12Packed(ctypes.Structure):
                 ("off_esc", c_sz), ("off_b2", c_sz), ("off_rowmap", c_sz)]
 
 
+class TvpLmheadI8(ctypes.Structure):
+    _fields_ = [("vocab", c_i64), ("k_in", c_i64), ("q", c_vp), ("scale", c_vp), ("esc_col", c_vp),
+                ("esc_val", c_vp), ("r", c_vp), ("r_eff", c_vp), ("tiles", TvpW12Packed)]
+
+
 class TvpGemmEpilogue(ctypes.Structure):
     _fields_ = [("mode", c_i32), ("y", c_vp), ("ldy", c_i64), ("resid", c_vp), ("ldr", c_i64),
                 ("pos", c_vp), ("slot", c_vp), ("k_cache", c_vp), ("v_cache", c_vp), ("s_stride", c_i64),
@@ -118,6 +123,13 @@ _lib_w12_gemm_resid_norm_workspace = _sig("w12_gemm_resid_norm_workspace", c_sz,
 _lib_w12_gemm_resid_norm = _sig("w12_gemm_resid_norm", ctypes.c_int,
                                 [c_vp, c_i64, ctypes.POINTER(TvpW12Packed), c_vp, c_i64, c_vp, ctypes.c_float, c_vp,
                                  c_vp, c_sz, c_vp])
+_lib_lmhead_i8_tiles_size = _sig("lmhead_i8_tiles_size", ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(TvpW12Packed)])
+_lib_lmhead_i8_encode_workspace = _sig("lmhead_i8_encode_workspace", c_sz, [c_i64, c_i64])
+_lib_lmhead_i8_encode = _sig("lmhead_i8_encode", ctypes.c_int, [c_vp, ctypes.POINTER(TvpLmheadI8), c_vp, c_sz, c_vp])
+_lib_lmhead_i8_argmax_workspace = _sig("lmhead_i8_argmax_workspace", c_sz, [c_i64, ctypes.POINTER(TvpLmheadI8)])
+_lib_lmhead_i8_argmax = _sig("lmhead_i8_argmax", ctypes.c_int,
+                             [c_vp, c_i64, ctypes.POINTER(TvpLmheadI8), ctypes.POINTER(TvpW12), c_vp, c_vp, c_vp,
+                              c_vp, c_sz, c_vp])
 _lib_tree_attention_workspace = _sig("tree_attention_workspace", c_sz, [c_i32, c_i32, c_i32, c_i32])
 _lib_tree_attention = _sig("tree_attention", ctypes.c_int,
                            [c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
@@ -137,6 +149,8 @@ _lib_tvp_read_probe = _sig("tvp_read_probe", ctypes.c_int, [c_vp, c_sz, c_vp, c_
 EXPORTED = ("tvp_status_string", "w12_encode_count", "w12_encode", "w12_decode", "w12_validate", "w12_pack_size",
             "w12_pack_workspace", "w12_pack", "w12_pack_hi8_size", "w12_pack_hi8", "w12_gemm_workspace", "w12_gemm", "w12_gemm_ex", "w12_gemm_ex_noalloc",
             "w12_packed_x_elems", "w12_pack_x", "w12_gemm_resid_norm_workspace", "w12_gemm_resid_norm",
+            "lmhead_i8_tiles_size", "lmhead_i8_encode_workspace", "lmhead_i8_encode",
+            "lmhead_i8_argmax_workspace", "lmhead_i8_argmax",
             "tree_attention_workspace", "tree_attention", "accept_path", "tvp_plan_create",
             "tvp_plan_destroy", "verify_step_workspace", "verify_step", "verify_step_batched",
             "tvp_read_probe")
@@ -386,6 +400,64 @@ def w12_gemm_resid_norm(xp: torch.Tensor, m: int, w: PackedW12, h: torch.Tensor,
     _check(_lib_w12_gemm_resid_norm(_ptr(xp), m, ctypes.byref(w.desc), _ptr(h), h.stride(0), _ptr(gain), float(eps),
                                     _ptr(yp), _ptr(ws), ws.numel(), _stream(xp.device)), "w12_gemm_resid_norm")
     return yp
+
+
+# ------------------------------------------------------- INT8 certified head
+@dataclass
+class LmheadI8:
+    """Device INT8 LM head (see ``tvp_lmhead_i8``); the tensors own the memory."""
+
+    desc: TvpLmheadI8
+    q: torch.Tensor
+    scale: torch.Tensor
+    esc_col: torch.Tensor
+    esc_val: torch.Tensor
+    r: torch.Tensor
+    r_eff: torch.Tensor
+    tiles: torch.Tensor
+
+    def stream_bytes(self) -> int:
+        """Bytes the approximate pass streams: tiles, escapes, scales and radii."""
+        return int(self.desc.tiles.bytes) + 8 * int(self.desc.vocab)
+
+
+def lmhead_i8_encode(w: torch.Tensor) -> LmheadI8:
+    """INT8 head of device bf16 ``w [vocab, k_in]``."""
+    _dev_check(w)
+    V, k = w.shape
+    dev = w.device
+    tp = TvpW12Packed()
+    _check(_lib_lmhead_i8_tiles_size(V, k, ctypes.byref(tp)), "lmhead_i8_tiles_size")
+    t = dict(q=torch.empty((V, k), dtype=torch.int8, device=dev), scale=torch.empty(V, dtype=torch.float32, device=dev),
+             esc_col=torch.empty((V, 8), dtype=torch.int16, device=dev),
+             esc_val=torch.empty((V, 8), dtype=torch.int16, device=dev),
+             r=torch.empty(V, dtype=torch.float32, device=dev), r_eff=torch.empty(V, dtype=torch.float32, device=dev),
+             tiles=torch.empty(int(tp.bytes), dtype=torch.uint8, device=dev))
+    tp.blob = t["tiles"].data_ptr()
+    d = TvpLmheadI8(V, k, t["q"].data_ptr(), t["scale"].data_ptr(), t["esc_col"].data_ptr(), t["esc_val"].data_ptr(),
+                    t["r"].data_ptr(), t["r_eff"].data_ptr(), tp)
+    need = int(_lib_lmhead_i8_encode_workspace(V, k))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(_lib_lmhead_i8_encode(_ptr(w), ctypes.byref(d), _ptr(ws), need, _stream(dev)), "lmhead_i8_encode")
+    torch.cuda.current_stream(dev).synchronize()
+    return LmheadI8(d, **t)
+
+
+def lmhead_i8_argmax(xp: torch.Tensor, m: int, head: LmheadI8, exact: W12Tensor, want_approx: bool = False):
+    """Greedy tokens of the ``m`` rows of packed activations ``xp``: returns
+    ``(argmax [m], candidates per row [m], approximate logits [m, vocab] or None)``."""
+    _dev_check(xp)
+    dev = xp.device
+    V = int(head.desc.vocab)
+    am = torch.empty(m, dtype=torch.int32, device=dev)
+    nc = torch.empty(m, dtype=torch.int32, device=dev)
+    apx = torch.empty((m, V), dtype=torch.float32, device=dev) if want_approx else None
+    need = int(_lib_lmhead_i8_argmax_workspace(m, ctypes.byref(head.desc)))
+    ws = _ws_gemm.get(need, dev)
+    s = exact.struct()
+    _check(_lib_lmhead_i8_argmax(_ptr(xp), m, ctypes.byref(head.desc), ctypes.byref(s), _ptr(am), _ptr(nc), _ptr(apx),
+                                 _ptr(ws), ws.numel(), _stream(dev)), "lmhead_i8_argmax")
+    return am, nc, apx
 
 
 # --------------------------------------------------------------- attention

@@ -564,3 +564,12 @@ int w12_pack_hi8(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes,
 }
 
 }  // extern "C"
+
+namespace tvp {
+// The packer for other entry points of the library (the INT8 head packs its
+// int8 values as the 8-bit tile layout).
+int pack_tiles(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hipStream_t stream,
+               int32_t layout) {
+  return pack_fmt(t, p, ws, ws_bytes, stream, layout);
+}
+}  // namespace tvp

@@ -48,7 +48,11 @@ struct GemmArgs {
   unsigned long long* keys;  // ARGMAX: [slot][m] packed (value, -id) maxima, one slot per workgroup that
                              // applies the epilogue (every slot written, no zeroing)
   int key_slots;
-  int hi8;  // records are the 8-bit leading view (TVP_FMT_HI8): 2048-byte tile blocks
+  int fmt;  // TVP_FMT_W12, TVP_FMT_HI8 (the 8-bit leading view) or kFmtI8 (int8 values): see decode_*
+  // INT8 head (kEpiI8Approx): per-channel scale and bound radius, per-row ||f||_2
+  const float* i8_scale;
+  const float* i8_r;
+  const float* i8_fnorm;
   int mode;
   void* y;
   int64_t ldy;
@@ -124,6 +128,24 @@ __device__ inline void decode_block_hi8(const uint4 (&r)[3], uint32_t b2, uint32
       const uint32_t d = D[2 * s + q];
       o[4 * s + 2 * q] = (((d & 0x007F007Fu) << 4) + b2) | ((d & 0x00800080u) << 8);
       o[4 * s + 2 * q + 1] = (((d >> 4) & 0x07F007F0u) + b2) | (d & 0x80008000u);
+    }
+  }
+}
+
+// Int8 values (the INT8 LM head): 8 dwords of one lane -> 16 bf16-pair
+// dwords, each value converted exactly (|q| <= 127 fits bf16's significand).
+// Byte order as above: (4q, 4q+2, 4q+1, 4q+3).
+__device__ inline void decode_block_i8(const uint4 (&r)[3], uint32_t (&o)[16]) {
+  const uint32_t D[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int32_t d = (int32_t)D[2 * s + q];
+      const float f0 = (float)((d << 24) >> 24), f2 = (float)((d << 16) >> 24);
+      const float f1 = (float)((d << 8) >> 24), f3 = (float)(d >> 24);
+      o[4 * s + 2 * q] = pack_bf16x2(f0, f1);
+      o[4 * s + 2 * q + 1] = pack_bf16x2(f2, f3);
     }
   }
 }
@@ -255,6 +277,35 @@ __device__ inline void epilogue(const GemmArgs& a, int c0, int nc, int M, int ti
         a.vc[((int64_t)kh * a.s_stride + a.slot[row]) * d + dim] = (uint16_t)f32_to_bf16(V(row, col));
       }
     }
+  } else if constexpr (MODE == kEpiI8Approx) {
+    // INT8 head: approximate logit a = scale * acc of every channel to
+    // logits [row][ldl], and per row the largest a - ||f|| r of this
+    // workgroup (the certificate threshold's share) to its key slot
+    __shared__ unsigned long long red_i8[8][32];
+    for (int row = 0; row < M; ++row) {
+      unsigned long long best = 0ull;
+      const float fn = a.i8_fnorm[row];
+      for (int cc = tid; cc < nc; cc += nthr) {
+        const int col = c0 + cc;
+        const int32_t r = rowmap_of(col);
+        if (r < 0) continue;
+        const float v = V(row, col) * a.i8_scale[r];
+        a.logits[row * a.ldl + r] = v;
+        const unsigned long long k = argmax_key(v - fn * a.i8_r[r], r);
+        best = k > best ? k : best;
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(best, off);
+        best = o > best ? o : best;
+      }
+      if ((tid & 63) == 0) red_i8[tid >> 6][row] = best;
+    }
+    __syncthreads();
+    for (int row = tid; row < M; row += nthr) {
+      unsigned long long best = 0ull;
+      for (int w = 0; w < (nthr >> 6); ++w) best = red_i8[w][row] > best ? red_i8[w][row] : best;
+      a.keys[(int64_t)key_slot * M + row] = best;
+    }
   } else {  // ARGMAX: per row the best (value, smallest id) of this workgroup, to its key slot
     __shared__ unsigned long long red[8][kArgmaxMaxRows];
     for (int row = 0; row < M; ++row) {
@@ -318,10 +369,11 @@ __global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned lon
 // with readlane, so no load in the loop depends on another.  At the end the
 // waves' fp32 partial tiles meet in LDS and are summed in wave order: no
 // global partial sums, no atomics, no device-scope fences.
-template <int MT, int TPW, int RD, int MODE, bool HI8>
+template <int MT, int TPW, int RD, int MODE, int FMT>
 __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
-  constexpr int NQ = HI8 ? 2 : 3;  // 16-byte pieces per lane of one tile block
-  constexpr int BB = HI8 ? kBlockBytesHi8 : kBlockBytes;
+  constexpr bool W12 = FMT == TVP_FMT_W12;
+  constexpr int NQ = W12 ? 3 : 2;  // 16-byte pieces per lane of one tile block
+  constexpr int BB = W12 ? kBlockBytes : kBlockBytesHi8;
   constexpr int NACC = MT == 32 ? 16 : 4;
   constexpr int NCH = MT == 32 ? 1 : 2;
   constexpr int KS = MT == 32 ? 4 : 2;  // MFMA K-steps per 64-column block
@@ -450,7 +502,8 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       uint32_t o[16];
-      if constexpr (HI8) decode_block_hi8(R[slot][t], b2v[t], o);
+      if constexpr (FMT == TVP_FMT_HI8) decode_block_hi8(R[slot][t], b2v[t], o);
+      else if constexpr (FMT == kFmtI8) decode_block_i8(R[slot][t], o);
       else decode_block(R[slot][t], b2v[t], o);
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -1081,10 +1134,14 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
   return p;
 }
 
-template <int MT, int TPW, int RD, bool HI8>
+template <int MT, int TPW, int RD, int HI8>
 static void launch_skinny_fmt(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.grid), block((unsigned)(p.KW * 64));
   const size_t lds = (size_t)p.KW * TPW * 4096;
+  if (a.fmt == kFmtI8) {  // the INT8 head: one epilogue
+    w12_skinny_kernel<MT, TPW, RD, kEpiI8Approx, kFmtI8><<<grid, block, lds, stream>>>(a);
+    return;
+  }
   switch (a.mode) {
     case TVP_EPI_F32: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_F32, HI8><<<grid, block, lds, stream>>>(a); break;
     case TVP_EPI_BF16: w12_skinny_kernel<MT, TPW, RD, TVP_EPI_BF16, HI8><<<grid, block, lds, stream>>>(a); break;
@@ -1098,8 +1155,8 @@ static void launch_skinny_fmt(const GemmArgs& a, const GemmPlan& p, hipStream_t 
 
 template <int MT, int TPW, int RD>
 static void launch_skinny(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
-  if (a.hi8) launch_skinny_fmt<MT, TPW, RD, true>(a, p, stream);
-  else launch_skinny_fmt<MT, TPW, RD, false>(a, p, stream);
+  if (a.fmt == TVP_FMT_W12) launch_skinny_fmt<MT, TPW, RD, TVP_FMT_W12>(a, p, stream);
+  else launch_skinny_fmt<MT, TPW, RD, TVP_FMT_HI8>(a, p, stream);
   if (p.rem_groups > 0) {  // launch errors of both are read by the caller's check
     const dim3 fgrid((unsigned)(a.n_tiles - p.full_groups * TPW));
     switch (a.mode) {
@@ -1167,6 +1224,9 @@ int launch_rope_table(const int32_t* pos, int n, int d, double theta, float* rop
 
 bool gemm_is_skinny(int64_t m, const tvp_w12_packed* w) { return make_plan(m, w).skinny; }
 
+int gemm_key_slots(int64_t m, const tvp_w12_packed* w) { return make_plan(m, w, 1, false).key_slots; }
+size_t gemm_keys_offset(int64_t m, const tvp_w12_packed* w) { return make_plan(m, w, 1, false).keys_off; }
+
 int gemm_ksplits(int64_t m, const tvp_w12_packed* w, int ksplit) {
   const GemmPlan p = make_plan(m, w, ksplit);
   return p.splits;
@@ -1180,13 +1240,14 @@ void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* 
 
 int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
              const tvp_gemm_epilogue* epi, int y_packed, void* scratch, size_t scratch_bytes,
-             hipStream_t stream, int ksplit, const float* rope_cs) {
+             hipStream_t stream, int ksplit, const float* rope_cs, const I8EpiArgs* i8) {
   if (!w || !epi || !w->blob) return TVP_ERR_ARG;
   if (m < 1 || m > 192) return TVP_ERR_SHAPE;
   if (ksplit > 1 && epi->mode != kEpiPartial) return TVP_ERR_ARG;
-  const GemmPlan p = make_plan(m, w, ksplit, epi->mode != TVP_EPI_ARGMAX);
-  if (w->format != TVP_FMT_W12 && w->format != TVP_FMT_HI8) return TVP_ERR_FORMAT;
-  if (w->format == TVP_FMT_HI8 && !p.skinny) return TVP_ERR_SHAPE;  // the 8-bit view: up to 32 rows
+  const GemmPlan p = make_plan(m, w, ksplit, epi->mode != TVP_EPI_ARGMAX && epi->mode != kEpiI8Approx);
+  if (w->format != TVP_FMT_W12 && w->format != TVP_FMT_HI8 && w->format != kFmtI8) return TVP_ERR_FORMAT;
+  if (w->format != TVP_FMT_W12 && !p.skinny) return TVP_ERR_SHAPE;  // 8-bit tiles: up to 32 rows
+  if ((w->format == kFmtI8) != (epi->mode == kEpiI8Approx)) return TVP_ERR_ARG;
   if (xp) {
     if (!p.skinny || ((uintptr_t)xp) % 16 != 0) return TVP_ERR_ARG;
   } else if (w->k_in > 0) {
@@ -1205,7 +1266,7 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
     TVP_LAUNCH_CHECK();
     xp = dst;
   }
-  a.hi8 = w->format == TVP_FMT_HI8 ? 1 : 0;
+  a.fmt = w->format;
   a.x = x;
   a.xp = xp;
   a.y_packed = y_packed;
@@ -1275,6 +1336,13 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
     case TVP_EPI_ARGMAX:
       if (!epi->argmax) return TVP_ERR_ARG;
       if (epi->logits && epi->ldl < w->n_out) return TVP_ERR_ARG;
+      break;
+    case kEpiI8Approx:
+      if (!epi->logits || epi->ldl < w->n_out || !i8 || !i8->scale || !i8->r || !i8->fnorm || m > 32)
+        return TVP_ERR_ARG;
+      a.i8_scale = i8->scale;
+      a.i8_r = i8->r;
+      a.i8_fnorm = i8->fnorm;
       break;
     case kEpiPartial:
       // skinny: slices to y [slice][row][ldy]; wide: the split sums stay in
