@@ -266,7 +266,7 @@ def pass_roles(trace_csv: str) -> dict:
     rows.sort()
 
     def kind(name):
-        m = re.search(r"w12_skinny_kernel<\d+, \d+, \d+, (\d+)>", name)
+        m = re.search(r"w12_skinny_kernel<\d+, \d+, \d+, (\d+)(?:, \d+)?>", name)
         if m:
             return {"3": "gateup", "4": "qkv", "5": "lmhead", "16": "partial"}.get(m.group(1), "gemm")
         for key, lab in (("rem_fixup", "fixup"), ("wide_fixup", "wfix"), ("w12_wide_kernel", "wide"),

@@ -19,6 +19,10 @@ What it computes is written out from the pages' description of the method
 * ``lmhead_i8`` -- the LM head on INT8 weights with a Cauchy-Schwarz
                  certified candidate filter, exact argmax kept (section
                  무엇과 다른가);
+* ``gdn``     -- Gated DeltaNet layers of a hybrid target over a draft tree:
+                 every node's output with the state recomputed along its
+                 root path, and the state after the accepted path (section
+                 무엇과 다른가);
 * ``tlv``     -- two-level verification: a Q pass on the 8-bit leading view
                  of the W12 records, then one exact pass over the matched
                  path, the bonus token and a re-drafted subtree (section
@@ -34,4 +38,4 @@ the structural ones listed there (library-routine equivalences, closed forms,
 special cases), which is stated where it matters.
 """
 
-from . import bf16, w12, accept, model, tlv, lmhead_i8  # noqa: F401
+from . import bf16, w12, accept, model, tlv, lmhead_i8, gdn  # noqa: F401
