@@ -793,6 +793,133 @@ def bench_lmhead(args) -> int:
     return 0
 
 
+def gdn_bytes(n: int, hk: int, hv: int, dk: int, dv: int) -> int:
+    """Algorithmic bytes of one Gated DeltaNet tree verify: the fp32 state
+    once, q, k, v, g, beta of the n nodes once, the bf16 outputs once."""
+    return hv * dv * dk * 4 + 2 * n * hk * dk * 2 + n * hv * dv * 2 + 2 * n * hv * 4 + n * hv * dv * 2
+
+
+def bench_gdn(args) -> int:
+    """The Gated DeltaNet layers of the 27B-hybrid-like stand-in (48
+    recurrent layers of 8 key heads and 40 value heads x 128) over a 32-node
+    best-first tree: per layer the WY-form verify and the path verify (one
+    launch each per layer, every layer's own state and inputs, the 48
+    launches captured in a HIP graph and replayed between two events), then
+    one commit launch for all 48 layers along an accepted path of up to 4
+    nodes (events around each launch, median).  The WY verify's achieved
+    bytes (fp32 state, inputs and outputs once) are set against 8 TB/s."""
+    import torch
+
+    import tree_verification_pass_amd as tvp
+    from synth import best_first_topology
+    from synth.gdn import GDN_LAYERS_27B_HYBRID, GDN_SHAPES, gen_gdn_inputs
+
+    shape = GDN_SHAPES["27b_hybrid"]
+    L, n = GDN_LAYERS_27B_HYBRID, 32
+    dev = torch.device("cuda:0")
+    parents_np = np.asarray(best_first_topology(np.random.default_rng(args.seed + 5), n)[0], dtype=np.int32)
+    parents = torch.as_tensor(parents_np, device=dev)
+    inps = [gen_gdn_inputs(args.seed, l, n, shape) for l in range(L)]
+    state = torch.stack([i.state for i in inps]).to(dev).contiguous()
+    q = torch.stack([i.q for i in inps]).to(dev).contiguous()
+    k = torch.stack([i.k for i in inps]).to(dev).contiguous()
+    v = torch.stack([i.v for i in inps]).to(dev).contiguous()
+    g = torch.stack([i.g for i in inps]).to(dev).contiguous()
+    beta = torch.stack([i.beta for i in inps]).to(dev).contiguous()
+    out = torch.empty(L, n, shape.hv, shape.dv, dtype=torch.bfloat16, device=dev)
+    status = torch.zeros(L, dtype=torch.int32, device=dev)
+    res = {}
+    steps = max(args.steps // 10, 5)
+    for name, fn in (("wy", tvp.gdn_tree_verify), ("path", tvp.gdn_path_verify)):
+        def all_layers(fn=fn):
+            for l in range(L):
+                fn(q[l], k[l], v[l], g[l], beta[l], state[l], parents, out=out[l], status=status[l:l + 1])
+        all_layers()
+        torch.cuda.synchronize()
+        eager = out.clone()
+        # the 48 launches of a pass, captured once and replayed: the host's
+        # per-call cost stays out of the timed region
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            all_layers()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out.view(torch.int16), eager.view(torch.int16)) or int(status.abs().sum()) != 0:
+            raise RuntimeError(f"GDN {name} verify: graph replay differs from the eager launches")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_layer = e0.elapsed_time(e1) * 1000.0 / (steps * L)
+        res[name] = (per_layer, per_layer * L)
+        log(f"bench: GDN {name} verify: {per_layer:.2f} us per layer ({L} launches replayed from a graph)")
+        del graph
+    # commit of a 4-node accepted path into all layers (in place on a copy)
+    path_np = [0]
+    for i in range(1, n):
+        if parents_np[i] == path_np[-1] and len(path_np) < 4:
+            path_np.append(i)
+    pbuf = torch.full((n,), -1, dtype=torch.int32, device=dev)
+    pbuf[:len(path_np)] = torch.as_tensor(path_np, dtype=torch.int32)
+    na = torch.tensor([len(path_np) - 1], dtype=torch.int32, device=dev)
+    ok = torch.zeros(1, dtype=torch.int32, device=dev)
+    work = state.clone()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        work.copy_(state)
+        a.record()
+        tvp.gdn_commit(work, k, v, g, beta, pbuf, na, ok)
+        b.record()
+    torch.cuda.synchronize()
+    commit_us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1000.0
+    commit_bytes = 2 * L * shape.hv * shape.dv * shape.dk * 4
+    log(f"bench: GDN commit ({len(path_np)} nodes, {L} layers): {commit_us:.1f} us, "
+        f"{commit_bytes / commit_us / 1e3:.0f} GB/s")
+    nbytes = gdn_bytes(n, shape.hk, shape.hv, shape.dk, shape.dv)
+    gbs = nbytes / (res["wy"][0] * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import gdn as ogdn
+        from threadpoolctl import threadpool_info
+        heads = 4  # a bounded sample: 4 of the 40 value heads of one layer
+        i0 = inps[0]
+        S = i0.state.double().numpy()[:heads]
+        args_np = [S] + [t.double().numpy() for t in (i0.q, i0.k)] + \
+                  [i0.v.double().numpy()[:, :heads], i0.g.double().numpy()[:, :heads],
+                   i0.beta.double().numpy()[:, :heads]]
+        hk_s = 1
+        args_np[1], args_np[2] = args_np[1][:, :hk_s], args_np[2][:, :hk_s]
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0 or reps == 0:
+            ogdn.tree_outputs(*args_np, parents_np)
+            reps += 1
+        per_layer_s = (time.perf_counter() - t0) / reps * (shape.hv / heads)
+        threads = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
+        cpu = {"value": round(per_layer_s * 1e6, 1), "unit": "us per GDN layer verify (32 nodes, 40 value heads)",
+               "cores": threads, "kind": "oracle",
+               "sample": f"{reps} oracle runs over 4 of 40 value heads of one layer, scaled x10"}
+    line = {
+        "metric": "Gated DeltaNet tree verify (27B-hybrid-like, 48 recurrent layers, 32-node tree), 1 GPU",
+        "value": round(res["wy"][0], 2), "unit": "us per layer (WY-form verify, 48 launches replayed)", "n_gpus": 1,
+        "steps": steps, "warmup": 1, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32 state, bf16 io", "data": "synthetic",
+        "us_per_layer": {"wy_verify": round(res["wy"][0], 2), "path_verify": round(res["path"][0], 2)},
+        "us_all_layers": {"wy_verify": round(res["wy"][1], 1), "path_verify": round(res["path"][1], 1)},
+        "commit_us_48_layers": round(commit_us, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gdn_wy_kernel", "bytes_per_launch": int(nbytes)},
+        "config": {"workload": "27B-hybrid-like Gated DeltaNet layers: 48 layers, 8 key / 40 value heads x 128, "
+                               "fp32 state, 32-node best-first tree (branching <= 4, depth <= 8)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def gemm_cpu_baseline(w_bits):
     """The oracle (untuned) on the 17408 x 5120 shape at 32 rows: exact W12
     decode of the canonical tensor plus the fp64 product (the encode is the
@@ -833,6 +960,8 @@ def main() -> int:
                     help="time the W12 LM head against the INT8 head with the certified candidate filter instead")
     ap.add_argument("--tlv", action="store_true",
                     help="time two-level verification (Q pass on the 8-bit weight views + exact pass) instead")
+    ap.add_argument("--gdn", action="store_true",
+                    help="time the Gated DeltaNet tree verify (WY form, path form) and commit of a hybrid target")
     ap.add_argument("--gemm", action="store_true",
                     help="time the standalone W12 GEMM at the 27B-like shapes and M = 1, 16, 32 instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -872,6 +1001,8 @@ def main() -> int:
     cfg = CONFIGS[args.config]
     if args.gemm:
         return bench_gemm(args)
+    if args.gdn:
+        return bench_gdn(args)
     if args.tlv:
         return bench_tlv(args, cfg)
     if args.lmhead:

@@ -428,6 +428,51 @@ int verify_step_batched(tvp_plan* plan, int32_t n_req, const int32_t* ctx_len,
                         const int32_t* parents, int32_t commit, const tvp_verify_out* out,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------- Gated DeltaNet layers (hybrid targets)
+ * SpecPilot summary, section 무엇과 다른가: for a target whose recurrent
+ * layers are Gated DeltaNet, verification takes each node's recurrent state
+ * along its own root path (recomputed, not stored per node); a WY-form
+ * verify solves all paths at once with matrix products, the fp32 state split
+ * into three bf16 pieces that hold its 24-bit significand exactly; after
+ * acceptance the accepted path is replayed into every recurrent layer.  The
+ * recurrence (gated delta rule, Gated DeltaNet, Yang, Kautz and Hatamizadeh,
+ * ICLR 2025), per value head with state S [dv][dk]:
+ *   S <- exp(g) S + beta (v - exp(g) S k) k^T,   o = S q
+ * for every new token in root-first order; value head h reads q and k of key
+ * head h / (hv / hk).  q and k arrive as the recurrence consumes them (after
+ * the layer's projections, convolution and normalisation).
+ *
+ * gdn_tree_verify (WY form) and gdn_path_verify (each leaf's root path
+ * replayed from the committed state) compute the same outputs:
+ *   q, k     device bf16 [n][hk][dk]       v  device bf16 [n][hv][dv]
+ *   g, beta  device fp32 [n][hv] (log decay <= 0, write strength)
+ *   state    device fp32 [hv][dv][dk], the committed state (read only)
+ *   parents  device int32 [n], parents[0] = -1, 0 <= parents[i] < i
+ *   out      device bf16 [n][hv][dv] (caller-owned; every element written)
+ *   status   device int32 [1]: TVP_OK, or TVP_ERR_TREE for a malformed tree
+ *            (the outputs are then unspecified)
+ * Limits: 1 <= n <= 32, dk = dv = 128, hv a multiple of hk; q, k, v and
+ * state 16-byte aligned.  TVP_ERR_ARG / TVP_ERR_SHAPE before any launch.  No
+ * workspace.  Deterministic: the same inputs give the same bits.           */
+int gdn_tree_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
+                    const float* state, const int32_t* parents, int32_t n, int32_t hk, int32_t hv, int32_t dk,
+                    int32_t dv, uint16_t* out, int32_t* status, hipStream_t stream);
+int gdn_path_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
+                    const float* state, const int32_t* parents, int32_t n, int32_t hk, int32_t hv, int32_t dk,
+                    int32_t dv, uint16_t* out, int32_t* status, hipStream_t stream);
+
+/* Commit of the accepted path into n_layers recurrent layers at once:
+ * state [n_layers][hv][dv][dk] (device fp32, updated in place) gets the
+ * updates of nodes path[0 .. *n_accepted] in that order, with each layer's
+ * k [n_layers][n][hk][dk], v [n_layers][n][hv][dv] (bf16) and
+ * g, beta [n_layers][n][hv] (fp32).  path, n_accepted and status are device
+ * int32 as accept_path writes them; nothing is changed unless *status is
+ * TVP_OK, 0 <= *n_accepted < n and every path entry is in [0, n).  Limits as
+ * above (n_layers <= 1024; state, k and v 16-byte aligned).               */
+int gdn_commit(float* state, const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
+               int32_t n_layers, int32_t n, int32_t hk, int32_t hv, int32_t dk, int32_t dv, const int32_t* path,
+               const int32_t* n_accepted, const int32_t* status, hipStream_t stream);
+
 /* ------------------------------------------------------- measurement
  * Streaming-read probe: the HBM read rate a plain sequential stream reaches
  * on this GPU, the practical ceiling the weight stream of the pass (SpecPilot

@@ -145,6 +145,12 @@ _lib_verify_step_batched = _sig("verify_step_batched", ctypes.c_int,
                                 [c_vp, c_i32, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32), c_i32, c_vp, c_vp,
                                  c_i32, ctypes.POINTER(TvpVerifyOut), c_vp, c_sz, c_vp])
 _lib_tvp_read_probe = _sig("tvp_read_probe", ctypes.c_int, [c_vp, c_sz, c_vp, c_vp])
+_GDN_VERIFY_ARGS = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
+_lib_gdn_tree_verify = _sig("gdn_tree_verify", ctypes.c_int, _GDN_VERIFY_ARGS)
+_lib_gdn_path_verify = _sig("gdn_path_verify", ctypes.c_int, _GDN_VERIFY_ARGS)
+_lib_gdn_commit = _sig("gdn_commit", ctypes.c_int,
+                       [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
+                        c_vp])
 
 EXPORTED = ("tvp_status_string", "w12_encode_count", "w12_encode", "w12_decode", "w12_validate", "w12_pack_size",
             "w12_pack_workspace", "w12_pack", "w12_pack_hi8_size", "w12_pack_hi8", "w12_gemm_workspace", "w12_gemm", "w12_gemm_ex", "w12_gemm_ex_noalloc",
@@ -153,7 +159,7 @@ EXPORTED = ("tvp_status_string", "w12_encode_count", "w12_encode", "w12_decode",
             "lmhead_i8_argmax_workspace", "lmhead_i8_argmax",
             "tree_attention_workspace", "tree_attention", "accept_path", "tvp_plan_create",
             "tvp_plan_destroy", "verify_step_workspace", "verify_step", "verify_step_batched",
-            "tvp_read_probe")
+            "tvp_read_probe", "gdn_tree_verify", "gdn_path_verify", "gdn_commit")
 
 
 # ------------------------------------------------------------------ helpers
@@ -477,6 +483,46 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                                _ptr(out), _ptr(status), _ptr(ws), ws.numel(), _stream(q.device)),
            "tree_attention")
     return out, status
+
+
+def _gdn_verify(fn, name, q, k, v, g, beta, state, parents, out=None, status=None):
+    _dev_check(q, k, v, g, beta, state, parents)
+    n, hk, dk = q.shape
+    hv, dv, _ = state.shape
+    if out is None:
+        out = torch.empty(n, hv, dv, dtype=torch.bfloat16, device=q.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=q.device)
+    _dev_check(out, status)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(parents), n, hk, hv, dk, dv,
+              _ptr(out), _ptr(status), _stream(q.device)), name)
+    return out, status
+
+
+def gdn_tree_verify(q, k, v, g, beta, state, parents, out=None, status=None):
+    """Gated DeltaNet layer over a draft tree, WY form (one solve for all
+    paths).  ``q, k [n, hk, dk]`` and ``v [n, hv, dv]`` bf16, ``g, beta
+    [n, hv]`` fp32, ``state [hv, dv, dk]`` fp32 (not modified), ``parents
+    [n]`` int32.  Returns ``(out [n, hv, dv] bf16, status [1])`` (both may be
+    passed in)."""
+    return _gdn_verify(_lib_gdn_tree_verify, "gdn_tree_verify", q, k, v, g, beta, state, parents, out, status)
+
+
+def gdn_path_verify(q, k, v, g, beta, state, parents, out=None, status=None):
+    """The same outputs as ``gdn_tree_verify``, each leaf's root path replayed
+    from the committed state."""
+    return _gdn_verify(_lib_gdn_path_verify, "gdn_path_verify", q, k, v, g, beta, state, parents, out, status)
+
+
+def gdn_commit(state, k, v, g, beta, path, n_accepted, status) -> None:
+    """Replays ``path[0 .. n_accepted]`` into ``state [L, hv, dv, dk]`` (in
+    place) for every layer; ``k [L, n, hk, dk]``, ``v [L, n, hv, dv]``,
+    ``g, beta [L, n, hv]``.  Nothing changes unless ``status`` is TVP_OK."""
+    _dev_check(state, k, v, g, beta, path, n_accepted, status)
+    L, hv, dv, dk = state.shape
+    _, n, hk, _ = k.shape
+    _check(_lib_gdn_commit(_ptr(state), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), L, n, hk, hv, dk, dv, _ptr(path),
+                           _ptr(n_accepted), _ptr(status), _stream(state.device)), "gdn_commit")
 
 
 def accept_path(argmax: torch.Tensor, tokens: torch.Tensor, parents: torch.Tensor):
