@@ -512,10 +512,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
 
 // Key splits are sized so that one launch has about this many workgroups
 // (one per compute unit).
-#ifndef TVP_ATTN_TARGET_GROUPS
-#define TVP_ATTN_TARGET_GROUPS 256
-#endif
-constexpr int kAttnTargetGroups = TVP_ATTN_TARGET_GROUPS;
+constexpr int kAttnTargetGroups = 256;
 // Blocks of 32 keys per wavefront kept in flight (including the one in LDS).
 constexpr int kAttnStages = 2;
 

@@ -20,9 +20,7 @@ namespace tvp {
 
 constexpr int kMaxLayers = 120;
 
-#ifndef TVP_KSPLIT_MAX
-#define TVP_KSPLIT_MAX 16  // most K slices of the O and down projections (packed path)
-#endif
+constexpr int kKsplitMax = 16;  // most K slices of the O and down projections (packed path)
 
 // ------------------------------------------------------------ small kernels
 
@@ -362,7 +360,7 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
       gmax = std::max(gmax, g);
       gscr = std::max(gscr, b);
       if (sliced && m <= 32) {  // the O and down projections' K-sliced launches
-        gemm_requirements(m, &w, &g, &b, TVP_KSPLIT_MAX);
+        gemm_requirements(m, &w, &g, &b, kKsplitMax);
         gmax = std::max(gmax, g);
         gscr = std::max(gscr, b);
       }
@@ -411,8 +409,8 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   p->ks_down = 1;
   if (p->pack_ok) {  // the largest slice counts any layer uses (they size the partial buffer)
     for (int l = 0; l < d->n_layers; ++l) {
-      p->ks_o = std::max(p->ks_o, gemm_ksplits(32, &p->layers[l].wo, TVP_KSPLIT_MAX));
-      p->ks_down = std::max(p->ks_down, gemm_ksplits(32, &p->layers[l].wdown, TVP_KSPLIT_MAX));
+      p->ks_o = std::max(p->ks_o, gemm_ksplits(32, &p->layers[l].wo, kKsplitMax));
+      p->ks_down = std::max(p->ks_down, gemm_ksplits(32, &p->layers[l].wdown, kKsplitMax));
     }
   }
   p->off_part = off;
@@ -506,9 +504,9 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
       e.y = part;
       e.ldy = H;
       if ((st = gemm_run(o, o, n_total, p->ld_q, &L.wo, &e, 0, gscr, p->gscr_bytes, stream,
-                         TVP_KSPLIT_MAX)))
+                         kKsplitMax)))
         return st;
-      launch_norm(part, gemm_ksplits(n_total, &L.wo, TVP_KSPLIT_MAX), pstride, H, h, p->ld_h, L.ffn_norm, H,
+      launch_norm(part, gemm_ksplits(n_total, &L.wo, kKsplitMax), pstride, H, h, p->ld_h, L.ffn_norm, H,
                   d.norm_eps, a, p->ld_h, 1, n_total, stream);
     } else {  // wide kernel: its split sums stay in the GEMM scratch and the norm adds them in split order
       e.mode = kEpiPartial;
@@ -533,9 +531,9 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
       e.y = part;
       e.ldy = H;
       if ((st = gemm_run(u, u, n_total, p->ld_u, &L.wdown, &e, 0, gscr, p->gscr_bytes, stream,
-                         TVP_KSPLIT_MAX)))
+                         kKsplitMax)))
         return st;
-      launch_norm(part, gemm_ksplits(n_total, &L.wdown, TVP_KSPLIT_MAX), pstride, H, h, p->ld_h, next_norm, H,
+      launch_norm(part, gemm_ksplits(n_total, &L.wdown, kKsplitMax), pstride, H, h, p->ld_h, next_norm, H,
                   d.norm_eps, a, p->ld_h, 1, n_total, stream);
     } else {
       e.mode = kEpiPartial;
@@ -619,8 +617,8 @@ int verify_step_batched(tvp_plan* p, int32_t n_req, const int32_t* ctx_len, cons
 static size_t resid_norm_ws_layout(int64_t m, const tvp_w12_packed* w, size_t* off_gemm, size_t* gemm_bytes,
                                    int* slices) {
   int g;
-  gemm_requirements(m, w, &g, gemm_bytes, TVP_KSPLIT_MAX);
-  *slices = gemm_ksplits(m, w, TVP_KSPLIT_MAX);
+  gemm_requirements(m, w, &g, gemm_bytes, kKsplitMax);
+  *slices = gemm_ksplits(m, w, kKsplitMax);
   *off_gemm = align_up((size_t)*slices * m * w->n_out * 4, 256);
   return *off_gemm + align_up(*gemm_bytes, 256);
 }
@@ -649,7 +647,7 @@ int w12_gemm_resid_norm(const uint16_t* xp, int64_t m, const tvp_w12_packed* w, 
   e.mode = kEpiPartial;
   e.y = part;
   e.ldy = w->n_out;
-  int st = gemm_run(nullptr, xp, m, 0, w, &e, 0, (uint8_t*)ws + off_g, gb, stream, TVP_KSPLIT_MAX);
+  int st = gemm_run(nullptr, xp, m, 0, w, &e, 0, (uint8_t*)ws + off_g, gb, stream, kKsplitMax);
   if (st != TVP_OK) return st;
   launch_norm(part, slices, m * w->n_out, (int)w->n_out, h, (int)ldh, gain, (int)w->n_out, eps, yp, 0, 1, (int)m,
               stream);

@@ -972,44 +972,25 @@ struct GemmPlan {
 // workgroups of 4 x kWideTPW tiles sharing X through LDS, split K over
 // workgroups (the splits finished by the next launch).
 constexpr int kWideMaxSplits = 32;
-#ifndef TVP_WIDE_SUM_WEIGHT
-#define TVP_WIDE_SUM_WEIGHT 0.5
-#endif
 // Cost of a split-sum byte against a record byte: the sums are written and
 // read back within microseconds, mostly from the caches (measured: 0.5 beat
 // 1 by 3.5% on the batched 27B-like step, 0.25 by 2%, 0 lost 50%).
-constexpr double kWideSumWeight = TVP_WIDE_SUM_WEIGHT;
-#ifndef TVP_WIDE_TPW
-#define TVP_WIDE_TPW 1
-#endif
-#ifndef TVP_WIDE_RD
-#define TVP_WIDE_RD 4
-#endif
-constexpr int kWideTPW = TVP_WIDE_TPW;  // wide kernel: tiles per wavefront (a workgroup owns 4 x kWideTPW)
-#ifndef TVP_WIDE_RD_BIG
-#define TVP_WIDE_RD_BIG 3  // measured: 3 beat 4 by 1.1% per batched step (2 within noise)
-#endif
-constexpr int kWideRD = TVP_WIDE_RD;    // wide kernel: register-ring depth
-constexpr int kWideRDBig = TVP_WIDE_RD_BIG;  // ... above 128 rows (one tile per wavefront, two wavefronts per SIMD)
-#ifndef TVP_TPW2_MIN_TILES
-#define TVP_TPW2_MIN_TILES 1024  // tiles from which a workgroup takes two tiles
-#endif
-#ifndef TVP_WAVES_PER_CU
-#define TVP_WAVES_PER_CU 12
-#endif
-constexpr int kWavesPerCU = TVP_WAVES_PER_CU;  // skinny kernel: three wavefronts per SIMD (136-156 VGPRs)
-#ifndef TVP_KW_ONE_ROUND
-#define TVP_KW_ONE_ROUND 8  // waves per workgroup when every workgroup has a CU to itself (4 measured 0.9% slower per verify step)
-#endif
-#ifndef TVP_RD1
-#define TVP_RD1 2  // register-ring depth, one tile per workgroup (106 VGPRs; 3 measured 1.4% slower per verify step)
-#endif
-#ifndef TVP_RD1_16
-#define TVP_RD1_16 TVP_RD1  // the same, 16-row MFMA tiles (m <= 16)
-#endif
-#ifndef TVP_RD2
-#define TVP_RD2 2  // register-ring depth, two tiles per workgroup
-#endif
+constexpr double kWideSumWeight = 0.5;
+constexpr int kWideTPW = 1;    // wide kernel: tiles per wavefront (a workgroup owns 4 x kWideTPW)
+constexpr int kWideRD = 4;     // wide kernel: register-ring depth
+constexpr int kWideRDBig = 3;  // ... above 128 rows (one tile per wavefront, two wavefronts per SIMD;
+                               // measured: 3 beat 4 by 1.1% per batched step, 2 within noise)
+constexpr int kTpw2MinTiles = 1024;  // tiles from which a workgroup takes two tiles
+constexpr int kWavesPerCU = 12;      // skinny kernel: three wavefronts per SIMD (136-156 VGPRs)
+// Waves per workgroup when every workgroup has a CU to itself (4 measured
+// 0.8% slower per verify step).
+constexpr int kKwOneRound = 8;
+// Register-ring depth with one tile per workgroup (106 VGPRs; 3 measured
+// 1.5% slower per verify step), the same with 16-row MFMA tiles, and with
+// two tiles per workgroup.
+constexpr int kRd1 = 2;
+constexpr int kRd1M16 = kRd1;
+constexpr int kRd2 = 2;
 
 // Compute units the skinny decomposition balances over (MI355X: 256).
 constexpr int kNumCUs = 256;
@@ -1017,16 +998,12 @@ constexpr int kNumCUs = 256;
 // Per-CU cost, in K blocks, of `gsplit` groups cut into `s` K slices of
 // `kps` blocks (partial-sum epilogue): the busiest CU's blocks plus a fixed
 // cost per workgroup; a CU holding a single workgroup streams slower.
-#ifndef TVP_SLICE_FIXED
-#define TVP_SLICE_FIXED 4.0  // measured: 4 (down in 3 slices) beat 2 (8 slices) by 0.35% per verify step, 1 lost 1%
-#endif
-#ifndef TVP_SLICE_SINGLE
-#define TVP_SLICE_SINGLE 1.5
-#endif
+constexpr double kSliceFixed = 4.0;   // measured: 4 (down in 3 slices) beat 2 (8 slices) by 0.35% per verify step, 1 lost 1%
+constexpr double kSliceSingle = 1.5;
 static double slice_cost(int gsplit, int s, int kps) {
   const int per_cu = (int)ceil_div((int64_t)gsplit * s, kNumCUs);
-  const double cost = (double)per_cu * kps + TVP_SLICE_FIXED * per_cu;
-  return per_cu <= 1 ? TVP_SLICE_SINGLE * cost : cost;
+  const double cost = (double)per_cu * kps + kSliceFixed * per_cu;
+  return per_cu <= 1 ? kSliceSingle * cost : cost;
 }
 
 // rem_ok: the epilogue can be finished by w12_rem_fixup_kernel (not argmax,
@@ -1040,8 +1017,8 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
   p.RB = (int)ceil_div(m, p.MT);
   p.skinny = m <= 32 && nkb <= 8 * 63;
   if (p.skinny) {
-    p.TPW = w->n_tiles >= TVP_TPW2_MIN_TILES ? 2 : 1;
-    p.RD = p.TPW == 2 ? TVP_RD2 : (p.MT == 16 ? TVP_RD1_16 : TVP_RD1);
+    p.TPW = w->n_tiles >= kTpw2MinTiles ? 2 : 1;
+    p.RD = p.TPW == 2 ? kRd2 : (p.MT == 16 ? kRd1M16 : kRd1);
     p.TG = p.TPW;
     p.groups = (int)ceil_div(w->n_tiles, p.TPW);
     p.splits = 1;
@@ -1066,7 +1043,7 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
     // of a CU's workgroups stream together instead of in two rounds; more
     // when a wave would exceed 63 blocks.
     p.KW = (int)ceil_div(nwg, kNumCUs) * 4 > kWavesPerCU ? 2 : 4;
-    if (nwg <= kNumCUs) p.KW = TVP_KW_ONE_ROUND;  // one workgroup per CU at most
+    if (nwg <= kNumCUs) p.KW = kKwOneRound;  // one workgroup per CU at most
     while (p.KW < 8 && ceil_div(krange, p.KW) > 63) p.KW *= 2;
     p.KW = std::max(1, std::min(p.KW, std::max(krange, 1)));
     p.kbs = nkb > 0 ? (int)ceil_div(nkb, p.KW) : 0;
@@ -1187,11 +1164,11 @@ static int dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
   if (p.grid > 0) {
     if (p.skinny) {
       if (p.MT == 16) {
-        if (p.TPW == 2) launch_skinny<16, 2, TVP_RD2>(a, p, stream);
-        else launch_skinny<16, 1, TVP_RD1_16>(a, p, stream);
+        if (p.TPW == 2) launch_skinny<16, 2, kRd2>(a, p, stream);
+        else launch_skinny<16, 1, kRd1M16>(a, p, stream);
       } else {
-        if (p.TPW == 2) launch_skinny<32, 2, TVP_RD2>(a, p, stream);
-        else launch_skinny<32, 1, TVP_RD1>(a, p, stream);
+        if (p.TPW == 2) launch_skinny<32, 2, kRd2>(a, p, stream);
+        else launch_skinny<32, 1, kRd1>(a, p, stream);
       }
     } else {
       switch ((int)ceil_div(a.m, 32)) {  // 32-row blocks
