@@ -226,20 +226,30 @@ def cpu_baseline(dm, cfg, seed: int, tree):
     vc = bf16_bits_numpy(dm.layers[0].v_cache[:, : cfg.ctx_len])
     dims = om.Dims.of(cfg)
     from oracle.bf16 import from_bits
-    t0 = time.perf_counter()
-    model = om.OracleModel.from_w12(dims, np.zeros((1, cfg.hidden), np.uint16), [enc], bits["attn_norm"][:1],
-                                    None)
-    h = from_bits(h_bits)
-    pos = cfg.ctx_len + om._accept.depths(parents)
-    om.layer_forward(model, 0, h, pos, from_bits(kc), from_bits(vc), om.ancestor_mask(parents))
-    t_layer = time.perf_counter() - t0
+    from threadpoolctl import threadpool_limits
+
+    def one_layer() -> float:
+        t0 = time.perf_counter()
+        model = om.OracleModel.from_w12(dims, np.zeros((1, cfg.hidden), np.uint16), [enc], bits["attn_norm"][:1],
+                                        None)
+        h = from_bits(h_bits)
+        pos = cfg.ctx_len + om._accept.depths(parents)
+        om.layer_forward(model, 0, h, pos, from_bits(kc), from_bits(vc), om.ancestor_mask(parents))
+        return time.perf_counter() - t0
+
+    t_layer = one_layer()
+    with threadpool_limits(limits=1):
+        t_layer_1 = one_layer()
     w_layer = sum(a * b for a, b in cfg.linear_shapes().values())
-    est = t_layer * cfg.streamed_params() / w_layer
+    scale = cfg.streamed_params() / w_layer
+    est, est_1 = t_layer * scale, t_layer_1 * scale
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": 1.0 / est, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"1 of {cfg.n_layers} decoder layers of one {len(tokens)}-node verify step (W12 decode of its 4 "
                        f"weights + fp64 forward, ctx {cfg.ctx_len}): {t_layer:.2f} s, scaled by streamed "
-                       f"weights ({cfg.streamed_params() / w_layer:.2f}x) to a whole step of {est:.1f} s")}
+                       f"weights ({scale:.2f}x) to a whole step of {est:.1f} s"),
+            "one_thread": {"value": 1.0 / est_1, "unit": "steps/s", "cores": 1,
+                           "sample": f"the same layer on 1 thread: {t_layer_1:.2f} s, a whole step of {est_1:.1f} s"}}
 
 
 # once-per-pass kernels, by the name they carry in a trace
