@@ -55,9 +55,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic():
+def recorded_traffic(alg_bytes: int):
     """Bytes per launch from the committed counter summary, if it was taken on
-    the current sources; else None."""
+    the current sources and on this launch (the same algorithmic bytes, i.e.
+    the same weight shape and rows); else None."""
     try:
         text = open(TRAFFIC_PROFILE).read()
     except OSError:
@@ -68,6 +69,8 @@ def recorded_traffic():
             k, v = line.strip()[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
     if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    if fields.get("algorithmic_bytes_per_launch") != str(int(alg_bytes)):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -176,6 +179,35 @@ def time_gateup(dm, cfg, iters: int):
     nbytes = (sum(w12_algorithmic_bytes(L.wgu.n_out, L.wgu.k_in, int(L.wgu.desc.n_esc)) for L in layers)
               / len(layers) + n * H * 2 + n * F * 2)
     return ms, nbytes, p
+
+
+def time_gateup_rows(dm, cfg, m: int, iters: int):
+    """The fused gate/up W12 GEMM at m rows in row-major layout (the batched
+    pass's wide kernel and its fix-up), rotated over the layers' distinct
+    weights, timed with HIP events around each launch on its stream."""
+    import torch
+
+    import tree_verification_pass_amd as tvp
+
+    dev = torch.device("cuda:0")
+    H, F = cfg.hidden, cfg.ffn
+    x = torch.randn(m, H, device=dev).to(torch.bfloat16)
+    u = torch.empty(m, F, dtype=torch.bfloat16, device=dev)
+    epi = tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=u.data_ptr(), ldy=F)
+    layers = dm.layers
+    for i in range(len(layers)):
+        tvp.w12_gemm_ex(x, layers[i].wgu, epi)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record()
+        tvp.w12_gemm_ex(x, layers[i % len(layers)].wgu, epi)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / iters
+    nbytes = (sum(w12_algorithmic_bytes(L.wgu.n_out, L.wgu.k_in, int(L.wgu.desc.n_esc)) for L in layers)
+              / len(layers) + m * H * 2 + m * F * 2)
+    return ms, nbytes
 
 
 def read_probe_gbs(gib: int = 4, iters: int = 5) -> float:
@@ -592,6 +624,9 @@ def bench_batched(args, cfg) -> int:
     nbytes = w + cfg.n_layers * (kv_read + kv_write + commit) + total * cfg.hidden * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"bench: {ms:.3f} ms/step, {1000.0 / ms:.2f} steps/s, {emitted * 1000.0 / ms:.0f} tokens/s, {gbs:.0f} GB/s")
+    g_ms, g_bytes = time_gateup_rows(dm, cfg, total, max(args.gemm_iters, 2 * cfg.n_layers))
+    g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
+    log(f"bench: gate/up W12 GEMM at {total} rows {g_ms * 1000.0:.1f} us/launch, {g_gbs:.0f} GB/s")
     line = {
         "metric": "W12 batched tree-verify steps/s (27B-like, 24 requests sharing a 192-node budget), 1 GPU",
         "value": round(1000.0 / ms, 3), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
@@ -599,6 +634,14 @@ def bench_batched(args, cfg) -> int:
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "tokens_per_s": round(emitted * 1000.0 / ms, 2), "mean_emitted_per_step": round(emitted, 2),
         "achieved_hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": int(nbytes),
+        "roofline": {"kernel": (f"w12_wide_kernel + w12_wide_fixup_kernel (fused gate/up SwiGLU, "
+                                f"{2 * cfg.ffn}x{cfg.hidden}, {total} rows)"),
+                     "bound": "hbm", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "us_per_launch": round(g_ms * 1000.0, 2), "bytes_per_launch": int(g_bytes),
+                     "note": (f"{2 * total * 2 * cfg.ffn * cfg.hidden / g_bytes:.0f} flop per byte: the bf16 MFMA "
+                              f"bound ({2 * total * 2 * cfg.ffn * cfg.hidden / 2.5e15 * 1e6:.1f} us) is below the "
+                              f"HBM bound ({g_bytes / 8e12 * 1e6:.1f} us)")},
         "config": {"workload": (f"{cfg.name}-like batched verify step, {n_req} requests, {total} nodes "
                                 f"(trees of {int(sizes.min())}-{int(sizes.max())}), ctx {int(ctxs.min())}-"
                                 f"{int(ctxs.max())} (mean {float(ctxs.mean()):.0f})"),
@@ -1108,7 +1151,7 @@ def main() -> int:
                                 f"(fused gate/up, {2 * cfg.ffn}x{cfg.hidden})"), "bound": "hbm",
                      "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(g_gbs / HBM_PEAK_GBS, 4), "probe_frac": round(g_gbs / probe, 4),
-                     "traffic": recorded_traffic(),
+                     "traffic": recorded_traffic(g_bytes),
                      "us_per_launch": round(g_ms * 1000.0, 2), "bytes_per_launch": int(g_bytes)},
         "cpu_baseline": cpu,
     }
