@@ -54,8 +54,10 @@ __device__ inline bool gdn_tree_masks(const int32_t* __restrict__ parents, int n
                                       uint32_t* anc, int* ok_flag) {
   const int tid = threadIdx.x;
   if (tid < 64) {
-    int p = -2;
-    if (tid < n) p = parents[tid];
+    // loads stay unconditional (clamped index): a load inside a branch is
+    // waited for at the branch's end
+    const int pl = parents[min(tid, n - 1)];
+    const int p = tid < n ? pl : -2;
     const bool ok = tid >= n || (tid == 0 ? p == -1 : (p >= 0 && p < tid));
     const bool all_ok = __all(ok);
     if (tid < kGdnMaxNodes) par[tid] = (tid < n && all_ok && tid > 0) ? p : -1;
@@ -142,6 +144,36 @@ __device__ inline void load_half(const float* src, float* S) {
   }
 }
 
+// u along the root path of node i (mask mk, root first) at value dimension c,
+// and o_i's path sum: for path position p (node x), u_x = B_x - sum over
+// earlier path positions q of A[x][path q] u_q, then o += E[i][x] u_x.  Fully
+// unrolled to P positions with no branch: positions past the path take node 0
+// with zero coefficients, so they add nothing.
+template <int P>
+__device__ inline float wy_path(uint32_t mk, int i, int c, const float (*Am)[33], const float (*Em)[33],
+                                const float (*Bm)[33]) {
+  int pn[P];
+  bool on[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    on[p] = mk != 0;
+    pn[p] = on[p] ? __ffs(mk) - 1 : 0;
+    mk &= mk - 1;
+  }
+  float u[P];
+  float o = 0.0f;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int x = pn[p];
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < p; ++q) s = fmaf(Am[x][pn[q]], u[q], s);
+    u[p] = on[p] ? Bm[x][c] - s : 0.0f;
+    o = fmaf(on[p] ? Em[i][x] : 0.0f, u[p], o);
+  }
+  return o;
+}
+
 // ------------------------------------------------------------- WY verify
 
 constexpr int kWyCols = 32;     // value dimensions per workgroup
@@ -177,13 +209,11 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(GdnArgs a) {
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int i = slot + NS * m;
-    vreg[m] = i < n ? __uint_as_float((uint32_t)a.v[((int64_t)i * a.hv + h) * D + c0 + c] << 16) : 0.0f;
+    // unconditional, clamped: nodes past n read node n - 1 and are never used
+    vreg[m] = __uint_as_float((uint32_t)a.v[((int64_t)min(i, n - 1) * a.hv + h) * D + c0 + c] << 16);
   }
-  float gv = 0.0f, bv = 0.0f;
-  if (tid < n) {
-    gv = a.g[tid * a.hv + h];
-    bv = a.beta[tid * a.hv + h];
-  }
+  const int tn = min(tid, n - 1);
+  const float gv = a.g[tn * a.hv + h], bv = a.beta[tn * a.hv + h];  // lanes past n: never used
   // product operands (wavefronts 0-3): lane holds row lane % 32 (a node,
   // or a state row of the block) and k values 8 (lane / 32) .. +7 of each
   // 16-wide step; rows past n read node 0 and are zeroed
@@ -213,7 +243,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(GdnArgs a) {
   const bool ok = gdn_tree_masks(a.parents, n, par, anc, &ok_flag);
   if (blockIdx.x == 0 && tid == 0) *a.status = ok ? TVP_OK : TVP_ERR_TREE;
   if (tid < 64) {  // G_i over the root path in node order (lane j holds g_j); beta_i
-    const uint32_t m = tid < kGdnMaxNodes ? anc[tid] : 0u;
+    const uint32_t m = tid < kGdnMaxNodes ? anc[tid] : 0u;  // bits only below n
     float s = 0.0f;
     for (int j = 0; j < kGdnMaxNodes; ++j) {
       const float gj = __shfl(gv, j);
@@ -221,7 +251,7 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(GdnArgs a) {
     }
     if (tid < kGdnMaxNodes) {
       Gs[tid] = s;
-      bs[tid] = bv;
+      bs[tid] = tid < n ? bv : 0.0f;
     }
   }
   if (wave < 4) {
@@ -259,33 +289,19 @@ __global__ __launch_bounds__(kWyThreads) void gdn_wy_kernel(GdnArgs a) {
     Bm[i][c] = i < n ? bs[i] * (vreg[m] - expf(Gs[i]) * prod[2][i][c]) : 0.0f;
   }
   __syncthreads();
-  // ---- solve along the root path and output, thread (node i, column c)
+  // ---- solve along the root path and output, thread (node i, column c),
+  // unrolled to the tree's longest root path
+  int maxlen = 1;
+  for (int i = 0; i < n; ++i) maxlen = max(maxlen, __popc(anc[i]));
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int i = slot + NS * m;
     if (i >= n) continue;
-    uint32_t mk = anc[i];
-    const int len = __popc(mk);
-    int pn[kGdnMaxNodes];  // path nodes, root first
-    float u[kGdnMaxNodes];
-#pragma unroll
-    for (int p = 0; p < kGdnMaxNodes; ++p) {
-      pn[p] = mk ? __ffs(mk) - 1 : 0;
-      mk &= mk - 1;
-    }
-    float o = expf(Gs[i]) * prod[3][i][c];
-#pragma unroll
-    for (int p = 0; p < kGdnMaxNodes; ++p) {
-      if (p < len) {
-        const int x = pn[p];
-        float s = 0.0f;
-#pragma unroll
-        for (int q = 0; q < p; ++q) s = fmaf(Am[x][pn[q]], u[q], s);
-        u[p] = Bm[x][c] - s;
-        o = fmaf(Em[i][x], u[p], o);
-      }
-    }
-    a.out[((int64_t)i * a.hv + h) * D + c0 + c] = (uint16_t)f32_to_bf16(o);
+    float o;
+    if (maxlen <= 9) o = wy_path<9>(anc[i], i, c, Am, Em, Bm);
+    else if (maxlen <= 16) o = wy_path<16>(anc[i], i, c, Am, Em, Bm);
+    else o = wy_path<kGdnMaxNodes>(anc[i], i, c, Am, Em, Bm);
+    a.out[((int64_t)i * a.hv + h) * D + c0 + c] = (uint16_t)f32_to_bf16(o + expf(Gs[i]) * prod[3][i][c]);
   }
 }
 
@@ -324,21 +340,31 @@ __global__ __launch_bounds__(kPairThreads) void gdn_path_kernel(GdnArgs a) {
   // (16-byte loads), decay and strength, all loads in flight together
   float S[kHalf];
   load_half(a.state + ((int64_t)h * D + row) * D + hf, S);
+  // (loads unconditional with clamped indices, stores guarded: a load inside
+  // a branch is waited for at the branch's end)
+  constexpr int NIT = kGdnMaxNodes * C8 / kPairThreads;
+  uint4 kx[NIT], qx[NIT], vx[NIT];
 #pragma unroll
-  for (int it = 0; it < kGdnMaxNodes * C8 / kPairThreads; ++it) {
+  for (int it = 0; it < NIT; ++it) {
+    const int e = tid + kPairThreads * it, j = min(e / C8, n - 1), c8 = e % C8;
+    kx[it] = *(const uint4*)(a.k + ((int64_t)j * a.hk + kh) * D + 8 * c8);
+    qx[it] = *(const uint4*)(a.q + ((int64_t)j * a.hk + kh) * D + 8 * c8);
+    vx[it] = *(const uint4*)(a.v + ((int64_t)j * a.hv + h) * D + 8 * c8);
+  }
+  const int tn = min(tid, n - 1);
+  const float gval = a.g[tn * a.hv + h], bval = a.beta[tn * a.hv + h];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
     const int e = tid + kPairThreads * it, j = e / C8, c8 = e % C8;
     if (j < n) {
-      const uint4 kx = *(const uint4*)(a.k + ((int64_t)j * a.hk + kh) * D + 8 * c8);
-      const uint4 qx = *(const uint4*)(a.q + ((int64_t)j * a.hk + kh) * D + 8 * c8);
-      const uint4 vx = *(const uint4*)(a.v + ((int64_t)j * a.hv + h) * D + 8 * c8);
-      unpack8(kx, &ks[j][8 * c8]);
-      unpack8(qx, &qs[j][8 * c8]);
-      unpack8(vx, &vs[j][8 * c8]);
+      unpack8(kx[it], &ks[j][8 * c8]);
+      unpack8(qx[it], &qs[j][8 * c8]);
+      unpack8(vx[it], &vs[j][8 * c8]);
     }
   }
   if (tid < n) {
-    gl[tid] = expf(a.g[tid * a.hv + h]);
-    bl[tid] = a.beta[tid * a.hv + h];
+    gl[tid] = expf(gval);
+    bl[tid] = bval;
   }
   if (tid < kGdnMaxNodes) {  // the first leaf below each node writes its output
     int o = kGdnMaxNodes;
@@ -401,18 +427,28 @@ __global__ __launch_bounds__(kPairThreads) void gdn_commit_kernel(GdnCommitArgs 
   float* dst = a.state + (((int64_t)layer * a.hv + h) * D + row) * D + hf;
   float S[kHalf];
   load_half(dst, S);
+  // (loads unconditional with clamped indices, stores guarded)
+  constexpr int NIT = kGdnMaxNodes * C8 / kPairThreads;
+  uint4 kx[NIT], vx[NIT];
 #pragma unroll
-  for (int it = 0; it < kGdnMaxNodes * C8 / kPairThreads; ++it) {
+  for (int it = 0; it < NIT; ++it) {
+    const int e = tid + kPairThreads * it, j = pj[min(e / C8, m - 1)], c8 = e % C8;
+    kx[it] = *(const uint4*)(a.k + lk + ((int64_t)j * a.hk + kh) * D + 8 * c8);
+    vx[it] = *(const uint4*)(a.v + lv + ((int64_t)j * a.hv + h) * D + 8 * c8);
+  }
+  const int jt = pj[min(tid, m - 1)];
+  const float gval = a.g[lg + jt * a.hv + h], bval = a.beta[lg + jt * a.hv + h];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
     const int e = tid + kPairThreads * it, i = e / C8, c8 = e % C8;
     if (i < m) {
-      const int j = pj[i];
-      unpack8(*(const uint4*)(a.k + lk + ((int64_t)j * a.hk + kh) * D + 8 * c8), &ks[i][8 * c8]);
-      unpack8(*(const uint4*)(a.v + lv + ((int64_t)j * a.hv + h) * D + 8 * c8), &vs[i][8 * c8]);
+      unpack8(kx[it], &ks[i][8 * c8]);
+      unpack8(vx[it], &vs[i][8 * c8]);
     }
   }
   if (tid < m) {
-    gl[tid] = expf(a.g[lg + pj[tid] * a.hv + h]);
-    bl[tid] = a.beta[lg + pj[tid] * a.hv + h];
+    gl[tid] = expf(gval);
+    bl[tid] = bval;
   }
   __syncthreads();
   for (int i = 0; i < m; ++i) pair_update(S, ks[i] + hf, gl[i], bl[i], vs[i][row]);
