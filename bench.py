@@ -235,53 +235,62 @@ def read_probe_gbs(gib: int = 4, iters: int = 5) -> float:
     return rate
 
 
-def cpu_baseline(dm, cfg, seed: int, tree):
-    """The oracle (untuned) on one of the 64 decoder layers of one step: W12
-    decode of the layer's four weights plus the layer's forward over the 32
-    nodes; the step estimate scales that by total/layer streamed weights."""
+def cpu_baseline(dm, cfg, seed: int, tree, n_sample: int = 4):
+    """The oracle (untuned) on ``n_sample`` of the decoder layers of one step:
+    W12 decode of each layer's four weights plus the layer's forward over the
+    nodes; the step estimate scales that by total / sampled streamed weights.
+    The first sampled layer is also timed on one thread."""
     import torch
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import model as om
     from oracle import w12 as ow12
+    from oracle.bf16 import from_bits
     from synth.configs import gen_layer
     from synth.weights import bf16_bits_numpy
 
     dev = torch.device("cuda:0")
-    layer = gen_layer(cfg, seed, 0, device=dev, gains="ones")
-    bits = {k: bf16_bits_numpy(v) for k, v in layer.items()}
-    del layer
-    enc = {k: (ow12.encode(v) if k in ("wqkv", "wo", "wgu", "wdown") else v) for k, v in bits.items()}
     tokens, parents = (t.cpu().numpy() for t in tree)
     h_bits = bf16_bits_numpy(dm.embed[torch.as_tensor(tokens.astype(np.int64), device=dev)])
-    kc = bf16_bits_numpy(dm.layers[0].k_cache[:, : cfg.ctx_len])
-    vc = bf16_bits_numpy(dm.layers[0].v_cache[:, : cfg.ctx_len])
     dims = om.Dims.of(cfg)
-    from oracle.bf16 import from_bits
-    from threadpoolctl import threadpool_limits
+    n_sample = max(1, min(n_sample, cfg.n_layers))
 
-    def one_layer() -> float:
+    def layer_inputs(li):  # weight generation and W12 encoding are not timed
+        layer = gen_layer(cfg, seed, li, device=dev, gains="ones")
+        bits = {k: bf16_bits_numpy(v) for k, v in layer.items()}
+        del layer
+        enc = {k: (ow12.encode(v) if k in ("wqkv", "wo", "wgu", "wdown") else v) for k, v in bits.items()}
+        kc = bf16_bits_numpy(dm.layers[li].k_cache[:, : cfg.ctx_len])
+        vc = bf16_bits_numpy(dm.layers[li].v_cache[:, : cfg.ctx_len])
+        return enc, bits["attn_norm"][:1], kc, vc
+
+    def one_layer(enc, norm, kc, vc) -> float:
         t0 = time.perf_counter()
-        model = om.OracleModel.from_w12(dims, np.zeros((1, cfg.hidden), np.uint16), [enc], bits["attn_norm"][:1],
-                                        None)
+        model = om.OracleModel.from_w12(dims, np.zeros((1, cfg.hidden), np.uint16), [enc], norm, None)
         h = from_bits(h_bits)
         pos = cfg.ctx_len + om._accept.depths(parents)
         om.layer_forward(model, 0, h, pos, from_bits(kc), from_bits(vc), om.ancestor_mask(parents))
         return time.perf_counter() - t0
 
-    t_layer = one_layer()
-    with threadpool_limits(limits=1):
-        t_layer_1 = one_layer()
+    t_sample, t_one = 0.0, 0.0
+    for li in range(n_sample):
+        inp = layer_inputs(li)
+        t_sample += one_layer(*inp)
+        if li == 0:
+            with threadpool_limits(limits=1):
+                t_one = one_layer(*inp)
+        del inp
     w_layer = sum(a * b for a, b in cfg.linear_shapes().values())
-    scale = cfg.streamed_params() / w_layer
-    est, est_1 = t_layer * scale, t_layer_1 * scale
+    scale = cfg.streamed_params() / (w_layer * n_sample)
+    est, est_1 = t_sample * scale, t_one * scale * n_sample
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": 1.0 / est, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"1 of {cfg.n_layers} decoder layers of one {len(tokens)}-node verify step (W12 decode of its 4 "
-                       f"weights + fp64 forward, ctx {cfg.ctx_len}): {t_layer:.2f} s, scaled by streamed "
-                       f"weights ({scale:.2f}x) to a whole step of {est:.1f} s"),
+            "sample": (f"{n_sample} of {cfg.n_layers} decoder layers of one {len(tokens)}-node verify step (W12 "
+                       f"decode of their weights + fp64 forward, ctx {cfg.ctx_len}): {t_sample:.2f} s, scaled by "
+                       f"streamed weights ({scale:.2f}x) to a whole step of {est:.1f} s"),
             "one_thread": {"value": 1.0 / est_1, "unit": "steps/s", "cores": 1,
-                           "sample": f"the same layer on 1 thread: {t_layer_1:.2f} s, a whole step of {est_1:.1f} s"}}
+                           "sample": (f"the first sampled layer on 1 thread: {t_one:.2f} s, a whole step of "
+                                      f"{est_1:.1f} s")}}
 
 
 # once-per-pass kernels, by the name they carry in a trace

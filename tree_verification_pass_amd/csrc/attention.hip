@@ -86,7 +86,9 @@ struct AttnArgs {
   float* pm;
   float* pl;
   int row_blocks;  // merge: 32-row blocks per (request, kv head)
-  int8_t order[kMaxReq];  // request of each unit slot: longest key range first (batched passes)
+  // request of each unit slot: longest key range first (batched passes);
+  // 32-bit entries, so a uniform index reads one with a scalar load
+  int32_t order[kMaxReq];
   int grouped;            // block order: units in groups of 8, row blocks inner (batched passes)
   PartRows pr;
   uint16_t* out;
@@ -592,8 +594,8 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
   // Workgroups start in index order and run for a time proportional to
   // their request's key range, so the longest requests go first (the tail of
   // the launch is then the shortest work).  Ties keep request order.
-  for (int i = 0; i < n_req; ++i) a.order[i] = (int8_t)i;
-  std::stable_sort(a.order, a.order + n_req, [&](int8_t x, int8_t y) {
+  for (int i = 0; i < n_req; ++i) a.order[i] = i;
+  std::stable_sort(a.order, a.order + n_req, [&](int32_t x, int32_t y) {
     return ri.ctx_len[x] + (ri.node_ptr[x + 1] - ri.node_ptr[x]) > ri.ctx_len[y] + (ri.node_ptr[y + 1] - ri.node_ptr[y]);
   });
   a.grouped = n_req > 1 ? 1 : 0;
