@@ -81,6 +81,8 @@ struct GemmArgs {
 };
 
 constexpr int kArgmaxMaxRows = 192;
+// Compute units the skinny decomposition balances over (MI355X: 256).
+constexpr int kNumCUs = 256;
 constexpr int kRemMaxSplits = 16;  // K slices of a remaining group (whole-K epilogues)
 
 // Row-major x [m][ldx] -> packed (rows >= m and columns >= k_in are zero).
@@ -388,7 +390,16 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
   // range, or, with the partial-sum epilogue, one per (group, K slice).
   // With a whole-K epilogue, workgroups past full_groups take one K slice of
   // a remaining group (so every CU gets the same share of the stream).
-  const int b = blockIdx.x;
+  // Workgroups b, b + 256, b + 512, ... start on one CU, one per CU per
+  // dispatch round; when whole groups fill several rounds they take
+  // consecutive groups, so one CU reads neighbouring tiles of each k block
+  // (measured: verify steps at the 27B-like shapes 0.9% faster, with 2 and 9
+  // rounds in the gate/up and LM-head launches).
+  int b = blockIdx.x;
+  if (MODE != kEpiPartial) {
+    const int rounds = a.full_groups / kNumCUs;
+    if (rounds >= 2 && b < rounds * kNumCUs) b = rounds * (b % kNumCUs) + b / kNumCUs;
+  }
   const bool rem = MODE != kEpiPartial && b >= a.full_groups;
   int grp, slice, ks0, ks1, kbs;  // ks0 .. ks1: this workgroup's K range
   if (MODE == kEpiPartial) {
@@ -991,9 +1002,6 @@ constexpr int kKwOneRound = 8;
 constexpr int kRd1 = 2;
 constexpr int kRd1M16 = kRd1;
 constexpr int kRd2 = 2;
-
-// Compute units the skinny decomposition balances over (MI355X: 256).
-constexpr int kNumCUs = 256;
 
 // Per-CU cost, in K blocks, of `gsplit` groups cut into `s` K slices of
 // `kps` blocks (partial-sum epilogue): the busiest CU's blocks plus a fixed
