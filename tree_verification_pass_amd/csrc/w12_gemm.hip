@@ -394,9 +394,10 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
   // dispatch round; when whole groups fill several rounds they take
   // consecutive groups, so one CU reads neighbouring tiles of each k block
   // (measured: verify steps at the 27B-like shapes 0.9% faster, with 2 and 9
-  // rounds in the gate/up and LM-head launches).
+  // rounds in the gate/up and LM-head launches; the int8 head's 2 KB blocks
+  // lost 7% that way and keep the dispatch order).
   int b = blockIdx.x;
-  if (MODE != kEpiPartial) {
+  if (MODE != kEpiPartial && FMT != kFmtI8) {
     const int rounds = a.full_groups / kNumCUs;
     if (rounds >= 2 && b < rounds * kNumCUs) b = rounds * (b % kNumCUs) + b / kNumCUs;
   }
