@@ -312,7 +312,10 @@ def _attn_ref(parents, q, kc, vc, L):
 
 @pytest.mark.parametrize("n,hq,hkv,d,L", [(32, 40, 8, 128, 4096), (32, 32, 8, 128, 2048), (8, 8, 8, 64, 256),
                                           (13, 6, 2, 64, 300), (1, 4, 4, 128, 0), (64, 4, 1, 64, 700),
-                                          (5, 10, 2, 128, 513)])
+                                          (5, 10, 2, 128, 513),
+                                          # two 32-row blocks per workgroup: three blocks (one pair
+                                          # half empty), one pair with a single split, four blocks
+                                          (13, 5, 1, 128, 300), (32, 8, 4, 128, 100), (20, 12, 2, 128, 1500)])
 def test_tree_attention_matches_oracle(tvp, cuda, n, hq, hkv, d, L):
     print(f"[tree_attention] n={n} hq={hq} hkv={hkv} d={d} L={L}", flush=True)
     parents, q, kc, vc = _attn_case(cuda, n, hq, hkv, d, L, seed=n + L)
