@@ -303,7 +303,7 @@ def pass_roles(trace_csv: str) -> dict:
     """Durations (us) of the pass's launches by role, from a rocprofv3 kernel
     trace: the library's dispatches in start order, each named by its kernel
     and, where one kernel serves two roles, by the launch before it (the O
-    projection follows the attention merge, the down projection the gate/up
+    projection follows tree attention, the down projection the gate/up
     fix-up; each residual + RMSNorm is named for the projection it follows).
     Gate/up launches outside the pass (bench.py's own timing leg) follow
     another gate/up launch and are left out."""
@@ -321,7 +321,7 @@ def pass_roles(trace_csv: str) -> dict:
         if m:
             return {"3": "gateup", "4": "qkv", "5": "lmhead", "16": "partial"}.get(m.group(1), "gemm")
         for key, lab in (("rem_fixup", "fixup"), ("wide_fixup", "wfix"), ("w12_wide_kernel", "wide"),
-                         ("tree_attn_merge", "merge"), ("tree_attn_kernel", "attn"), ("resid_norm", "norm")):
+                         ("tree_attn_kernel", "attn"), ("resid_norm", "norm")):
             if key in name:
                 return lab
         for key, lab in SMALL_ROLES:
@@ -339,10 +339,8 @@ def pass_roles(trace_csv: str) -> dict:
             role = "QKV GEMM + RoPE + KV write"
         elif k == "attn":
             role = "tree attention"
-        elif k == "merge":
-            role = "attention merge"
         elif k == "partial":
-            role = {"attention merge": "O GEMM (K slices)", "gate/up fix-up": "down GEMM (K slices)"}.get(prev)
+            role = {"tree attention": "O GEMM (K slices)", "gate/up fix-up": "down GEMM (K slices)"}.get(prev)
         elif k == "norm":
             role = {"O GEMM (K slices)": "residual + norm after O", "wide O GEMM (split sums)": "residual + norm after O",
                     "down GEMM (K slices)": "residual + norm after down",
@@ -355,7 +353,7 @@ def pass_roles(trace_csv: str) -> dict:
             role = "LM head + argmax"
         elif k == "wide":  # more than 32 rows: named by the launch before it
             role = {"norm (first or final)": "wide QKV GEMM", "residual + norm after down": "wide QKV GEMM",
-                    "tree attention": "wide O GEMM (split sums)", "attention merge": "wide O GEMM (split sums)",
+                    "tree attention": "wide O GEMM (split sums)",
                     "residual + norm after O": "wide gate/up GEMM",
                     "wide gate/up fix-up (SwiGLU)": "wide down GEMM (split sums)"}.get(prev)
             if role == "wide QKV GEMM" and i + 2 < len(kinds) and kinds[i + 2] == "LM-head argmax finalize":
@@ -369,7 +367,7 @@ def pass_roles(trace_csv: str) -> dict:
         if role:
             out.setdefault(role, []).append((rows[i][1] - rows[i][0]) / 1e3)
     order = ["QKV GEMM + RoPE + KV write", "wide QKV GEMM", "wide QKV fix-up (RoPE, KV write)", "tree attention",
-             "attention merge", "O GEMM (K slices)", "wide O GEMM (split sums)", "residual + norm after O",
+             "O GEMM (K slices)", "wide O GEMM (split sums)", "residual + norm after O",
              "gate/up GEMM", "gate/up fix-up", "wide gate/up GEMM", "wide gate/up fix-up (SwiGLU)",
              "down GEMM (K slices)", "wide down GEMM (split sums)", "residual + norm after down",
              "norm (first or final)", "LM head + argmax", "wide LM head", "wide LM-head fix-up (argmax keys)"] + \

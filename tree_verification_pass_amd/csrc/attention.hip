@@ -19,8 +19,9 @@
 // applied as a sum of two bf16 pieces.  The wavefronts' (max, sum, O)
 // are combined in LDS in a fixed order; with several splits, each split's
 // (max, sum, O) goes out in the accumulator's register layout (coalesced
-// 256-byte stores) and a separate merge launch sums them in split order, so
-// the result is deterministic.
+// 256-byte stores, written through to the device's coherence point) and the
+// last split of a row block to arrive, counted on a device-scope atomic,
+// sums them all in split order, so the result is deterministic.
 #include <math.h>
 
 #include <algorithm>
@@ -36,9 +37,13 @@ __global__ __launch_bounds__(64) void tree_prep_kernel(const int32_t* __restrict
                                                        int32_t s_req, uint64_t* __restrict__ anc,
                                                        int32_t* __restrict__ pos,
                                                        int32_t* __restrict__ slot,
-                                                       int32_t* __restrict__ status) {
+                                                       int32_t* __restrict__ status,
+                                                       uint32_t* __restrict__ cnt, int ncnt) {
   __shared__ int32_t par[64];
   const int r = blockIdx.x, i = threadIdx.x;
+  // the attention's arrival counters start every pass at zero (each launch
+  // leaves them at zero again)
+  for (int c = r * 64 + i; c < ncnt; c += gridDim.x * 64) cnt[c] = 0u;
   const int nb = ri.node_ptr[r], n = ri.node_ptr[r + 1] - nb;
   const int L = ri.ctx_len[r];
   int p = -2;
@@ -85,7 +90,10 @@ struct AttnArgs {
   float* po;
   float* pm;
   float* pl;
-  int row_blocks;  // merge: 32-row blocks per (request, kv head)
+  // arrival counters of the key splits, [request][kv head][kAttnRowBlocks]:
+  // zero before the launch, and left at zero by the split that merges
+  uint32_t* cnt;
+  int row_blocks;  // 32-row blocks per (request, kv head)
   // request of each unit slot: longest key range first (batched passes);
   // 32-bit entries, so a uniform index reads one with a scalar load
   int32_t order[kMaxReq];
@@ -136,6 +144,22 @@ __device__ inline void lds_fence() {
 
 // Wavefronts per attention workgroup (two per SIMD).
 constexpr int kAttnWaves = 8;
+
+// Device-scope stores and loads (cache-scope bits of the agent scope): a
+// store is written through to the device's coherence point before it
+// counts as complete, and a load is served from there, never from a stale
+// line of this XCD's L2.  The split partials travel this way, so the split
+// that merges them may run on any XCD without a write-back or invalidate of
+// a whole L2 (which a device-scope fence costs on this part).
+__device__ inline void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt with vmcnt 0 (expcnt and lgkmcnt at their maxima): every vector
+// memory access of this wavefront, stores included, has completed.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // One workgroup per (request, kv head, 32-row block, key split); its NW
 // wavefronts stream disjoint 32-key blocks of the split (wavefront w takes
@@ -416,98 +440,79 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
         a.out[attn_out_index<D>(a, nb + nd, (kh * a.G + g2) * D + dd)] = (uint16_t)f32_to_bf16(acc * inv);
       }
     } else {  // partial rows [kv head][split][padded rows], accumulator layout
-      a.po[pbase * D + e] = acc;
+      st_dev(a.po + pbase * D + e, acc);
       if (dv == 0 && ln < 32) {  // the exponent base is a raw score (unscaled)
-        a.pm[pbase + rw] = mx;
-        a.pl[pbase + rw] = den;
+        st_dev(a.pm + pbase + rw, mx);
+        st_dev(a.pl + pbase + rw, den);
       }
     }
   }
-}
+  if (nsplit == 1) return;
 
-// Merge of the key splits (a separate launch: the kernel boundary makes every
-// split's partials visible).  One workgroup per (request, kv head, 32-row
-// block, quarter of the block's D*32 elements).  Each row's split weights
-// come from 8 lanes with a fixed shuffle-tree order; every output element
-// sums its splits in split order, so the result is deterministic.
-template <int D>
-__global__ __launch_bounds__(256) void tree_attn_merge_kernel(AttnArgs a) {
-  __shared__ float wts[32 * 64];  // [row][split], normalised merge weights
-  const int qt = blockIdx.x & 3;
-  const int rb = (blockIdx.x >> 2) % a.row_blocks;
-  const int kh = ((blockIdx.x >> 2) / a.row_blocks) % a.hkv;
-  const int r = (blockIdx.x >> 2) / (a.row_blocks * a.hkv);
-  const int L = a.ri.ctx_len[r], nb = a.ri.node_ptr[r], n = a.ri.node_ptr[r + 1] - nb;
-  const int R = a.G * n;
-  const int nsplit = (L + n + a.kr - 1) / a.kr;  // <= 64
-  if (nsplit <= 1 || rb * 32 >= R) return;
-  const int tid = threadIdx.x;
-  // row block base of split 0; split sp adds sp * rows_total
-  const int64_t hb = (int64_t)kh * a.max_splits * a.rows_total + a.pr.prow[r] + rb * 32;
-  {
-    const int lr = tid >> 3, s0 = tid & 7;  // 8 lanes per row
-    float pm[8], pl[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int sp = s0 + 8 * j;
-      const bool ok = sp < nsplit;
-      const int64_t pr = hb + (int64_t)sp * a.rows_total + lr;
-      pm[j] = ok ? a.pm[pr] : -INFINITY;
-      pl[j] = ok ? a.pl[pr] : 0.0f;
-    }
-    float mx = pm[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, pm[j]);
-#pragma unroll
-    for (int off = 4; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    const float bse = mx == -INFINITY ? 0.0f : mx;
-    float w[8], den = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      w[j] = pm[j] == -INFINITY ? 0.0f : exp2f((pm[j] - bse) * a.scale_log2);  // maxima are raw scores
-      den += pl[j] * w[j];
-    }
-#pragma unroll
-    for (int off = 4; off > 0; off >>= 1) den += __shfl_xor(den, off);
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) wts[lr * 64 + s0 + 8 * j] = w[j] * inv;
+  // Arrival: once every wavefront's partial stores are complete, one
+  // device-scope atomic counts this split in; the split that brings the
+  // count to nsplit merges the row block (and resets its counter).  No
+  // workgroup waits for another.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  __shared__ int s_last;
+  if (tid == 0) {
+    uint32_t* c = a.cnt + ((int64_t)r * a.hkv + kh) * kAttnRowBlocks + rb;
+    const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == (uint32_t)(nsplit - 1);
+    if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
   }
   __syncthreads();
-  const int64_t sstride = (int64_t)a.rows_total * D;
-  const float* src = a.po + hb * D;
-  constexpr int NE = D / 32;  // elements per thread
-  int pe[NE];
-  float acc[NE];
+  if (!s_last) return;
+
+  // Merge of the row block's splits, in split order with a running exponent
+  // base (one pass, so the loads of up to 8 splits are in flight together).
+  // This thread's elements are the ones it stored above, all of row rw;
+  // every value is read back from the partials, this split's included, so the
+  // result does not depend on which split merges.
+  const int64_t hb = (int64_t)kh * a.max_splits * a.rows_total + a.pr.prow[r] + rb * 32;  // split 0
+  constexpr int NE = NACC / NW;  // elements per thread
+  float gb = -INFINITY, gden = 0.0f, macc[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) macc[i] = 0.0f;
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float pmv[8], plv[8], pv[8][NE];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // past the last split: its loads repeated, weight zero
+      const int64_t sb = hb + (int64_t)min(s0 + j, nsplit - 1) * a.rows_total;
+      const float m = ld_dev(a.pm + sb + rw);
+      pmv[j] = s0 + j < nsplit ? m : -INFINITY;
+      plv[j] = ld_dev(a.pl + sb + rw);
+#pragma unroll
+      for (int i = 0; i < NE; ++i) pv[j][i] = ld_dev(a.po + sb * D + (wave + NW * i) * 64 + ln);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (pmv[j] == -INFINITY) continue;  // no visible key of this row in the split
+      if (pmv[j] > gb) {  // raise the base (maxima are raw scores)
+        const float f = gb == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((gb - pmv[j]) * a.scale_log2);
+        gden *= f;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) macc[i] *= f;
+        gb = pmv[j];
+      }
+      const float wj = __builtin_amdgcn_exp2f((pmv[j] - gb) * a.scale_log2);
+      gden += plv[j] * wj;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) macc[i] += pv[j][i] * wj;
+    }
+  }
+  const float ginv = gden > 0.0f ? 1.0f / gden : 0.0f;
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
-    pe[i] = qt * (8 * D) + i * 256 + tid;  // element of the block in accumulator layout
-    acc[i] = 0.0f;
-  }
-  int sp = 0;
-  for (; sp + 4 <= nsplit; sp += 4) {  // 4 * NE independent loads in flight
-    float v[4][NE];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < NE; ++i) v[j][i] = src[(sp + j) * sstride + pe[i]];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < NE; ++i) acc[i] += v[j][i] * wts[(pe[i] & 31) * 64 + sp + j];
-  }
-  for (; sp < nsplit; ++sp)
-#pragma unroll
-    for (int i = 0; i < NE; ++i) acc[i] += src[sp * sstride + pe[i]] * wts[(pe[i] & 31) * 64 + sp];
-#pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    const int ln = pe[i] & 63, dv = pe[i] >> 6;  // lane, db * 16 + v
-    const int rr = rb * 32 + (ln & 31);
+    const int dv = wave + NW * i;
+    const int rr = rb * 32 + rw;
     if (rr < R) {
       const int db = dv >> 4, v = dv & 15;
       const int dd = db * 32 + 8 * (v >> 2) + 4 * (ln >> 5) + (v & 3);
       const int g2 = rr / n, nd = rr % n;
-      a.out[attn_out_index<D>(a, nb + nd, (kh * a.G + g2) * D + dd)] = (uint16_t)f32_to_bf16(acc[i]);
+      a.out[attn_out_index<D>(a, nb + nd, (kh * a.G + g2) * D + dd)] = (uint16_t)f32_to_bf16(macc[i] * ginv);
     }
   }
 }
@@ -520,7 +525,7 @@ constexpr int kAttnStages = 2;
 
 struct AttnPlan {
   int kr, max_splits, rows_total, row_blocks;
-  size_t off_po, off_pm, off_pl, bytes;
+  size_t off_cnt, off_po, off_pm, off_pl, bytes;
 };
 
 // max_keys: largest ctx_len + n over the requests; r_max: largest G * n;
@@ -538,6 +543,8 @@ static AttnPlan attn_plan(int hkv, int d, int r_max, int rows_total, int max_key
   p.rows_total = rows_total;
   const size_t rows = (size_t)hkv * p.max_splits * p.rows_total;
   size_t off = 0;
+  p.off_cnt = off;  // the arrival counters come first: tree preparation clears them
+  off = align_up(off + (size_t)attention_counters(n_req, hkv) * 4, 256);
   p.off_po = off;
   off = align_up(off + rows * d * 4, 256);
   p.off_pm = off;
@@ -549,8 +556,11 @@ static AttnPlan attn_plan(int hkv, int d, int r_max, int rows_total, int max_key
 }
 
 int launch_tree_prep(const int32_t* parents, const ReqInfo& ri, int32_t s_req, uint64_t* anc,
-                     int32_t* pos, int32_t* slot, int32_t* status, hipStream_t stream) {
-  tree_prep_kernel<<<dim3(ri.n_req), dim3(64), 0, stream>>>(parents, ri, s_req, anc, pos, slot, status);
+                     int32_t* pos, int32_t* slot, int32_t* status, void* attn_scratch, int hkv,
+                     hipStream_t stream) {
+  tree_prep_kernel<<<dim3(ri.n_req), dim3(64), 0, stream>>>(parents, ri, s_req, anc, pos, slot, status,
+                                                            (uint32_t*)attn_scratch,
+                                                            attention_counters(ri.n_req, hkv));
   TVP_LAUNCH_CHECK();
   return TVP_OK;
 }
@@ -585,6 +595,7 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
   a.kr = p.kr;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
   uint8_t* sb = (uint8_t*)scratch;
+  a.cnt = (uint32_t*)(sb + p.off_cnt);
   a.po = (float*)(sb + p.off_po);
   a.pm = (float*)(sb + p.off_pm);
   a.pl = (float*)(sb + p.off_pl);
@@ -602,13 +613,10 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
   a.units = n_req * hkv * p.max_splits;
   a.units8 = (int)align_up((size_t)a.units, 8);
   const dim3 grid((unsigned)(a.units8 * p.row_blocks));
-  const dim3 mgrid((unsigned)(n_req * hkv * a.row_blocks * 4));
   if (d == 128) {
     tree_attn_kernel<128, kAttnStages><<<grid, dim3(kAttnWaves * 64), 0, stream>>>(a);
-    if (p.max_splits > 1) tree_attn_merge_kernel<128><<<mgrid, dim3(256), 0, stream>>>(a);
   } else if (d == 64) {
     tree_attn_kernel<64, kAttnStages><<<grid, dim3(kAttnWaves * 64), 0, stream>>>(a);
-    if (p.max_splits > 1) tree_attn_merge_kernel<64><<<mgrid, dim3(256), 0, stream>>>(a);
   } else {
     return TVP_ERR_SHAPE;
   }
@@ -675,7 +683,7 @@ int tree_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v
   ri.ctx_len[0] = ctx_len;
   ri.node_ptr[0] = 0;
   ri.node_ptr[1] = n;
-  int st = launch_tree_prep(parents, ri, 0, anc, pos, slot, status, stream);
+  int st = launch_tree_prep(parents, ri, 0, anc, pos, slot, status, w + offp, hkv, stream);
   if (st != TVP_OK) return st;
   return launch_tree_attention(q, k_cache, v_cache, s_stride, ri, 0, anc, hq, hkv, d, (hq / hkv) * n,
                                ctx_len + n, out, 0, w + offp, ws_bytes - offp, stream);

@@ -63,12 +63,19 @@ void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* 
 int pack_tiles(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hipStream_t stream,
                int32_t layout);
 
+// Tree preparation also clears the arrival counters at the start of the
+// attention scratch that launch_tree_attention is then given.
 int launch_tree_prep(const int32_t* parents, const ReqInfo& ri, int32_t s_req, uint64_t* anc,
-                     int32_t* pos, int32_t* slot, int32_t* status, hipStream_t stream);
+                     int32_t* pos, int32_t* slot, int32_t* status, void* attn_scratch, int hkv,
+                     hipStream_t stream);
 int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int64_t s_stride,
                           const ReqInfo& ri, int32_t s_req, const uint64_t* anc, int hq, int hkv, int d,
                           int r_max, int max_keys, uint16_t* out, int out_packed, void* scratch,
                           size_t scratch_bytes, hipStream_t stream);
 size_t attention_scratch_bytes(int hkv, int G, int d, int r_max, int n_total, int max_keys);
+// 32-row blocks per (request, kv head) at most (256 rows), and the attention's
+// arrival counters for n_req requests: one per (request, kv head, row block).
+constexpr int kAttnRowBlocks = 8;
+inline int attention_counters(int n_req, int hkv) { return n_req * hkv * kAttnRowBlocks; }
 
 }  // namespace tvp

@@ -467,7 +467,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   void* ascr = w + p->off_ascr;
   int st;
 
-  if ((st = launch_tree_prep(parents, ri, s_req, anc, pos, slot, tstat, stream))) return st;
+  if ((st = launch_tree_prep(parents, ri, s_req, anc, pos, slot, tstat, ascr, hkv, stream))) return st;
   float* rope = (float*)(w + p->off_rope);
   if ((st = launch_rope_table(pos, n_total, hd, d.rope_theta, rope, stream))) return st;
   embed_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(tokens, d.embed, H, d.vocab, h, p->ld_h, bad);
