@@ -212,7 +212,13 @@ typedef struct tvp_gemm_epilogue {
   int64_t ldl;
   int32_t x_packed;        /* x is in the packed activation layout (ldx unused) */
   int32_t y_packed;        /* SWIGLU: y is written in the packed layout (ldy unused) */
+  uint32_t* counters;      /* optional device uint32 [TVP_GEMM_COUNTERS], all zero: arrival counters
+                              of the channel groups whose K range is cut into slices (the slice that
+                              arrives last applies the epilogue); the call leaves them at zero, so one
+                              array serves any number of calls in stream order.  NULL: the counters
+                              live in ws and one small launch clears them before the GEMM. */
 } tvp_gemm_epilogue;
+#define TVP_GEMM_COUNTERS 256
 
 /* x_packed and y_packed need m <= 32 and every k_in <= 32256 (the
  * single-pass path); otherwise TVP_ERR_ARG. */

@@ -211,8 +211,9 @@ def test_gemm_fused_epilogues(tvp, cuda):
 @pytest.mark.parametrize("m", [9, 32])
 def test_gemm_remaining_groups_split_over_k(tvp, cuda, m):
     """More channel groups than CUs, not a multiple of them: the groups past
-    the last full round are computed as K slices and finished by a second
-    launch.  Each whole-K epilogue through that path against the oracle."""
+    the last full round are computed as K slices, and the slice of a group
+    that arrives last sums them and applies the epilogue.  Each whole-K
+    epilogue through that path against the oracle."""
     H, F, hq, hkv, d = 1000, 4200, 120, 8, 64  # 263, 263 and 272 tiles of 32 channels
     print(f"[gemm remaining groups] m={m} swiglu/resid/qkv", flush=True)
     rng = np.random.default_rng(m)
@@ -269,6 +270,43 @@ def test_gemm_remaining_groups_split_over_k(tvp, cuda, m):
                      (from_bits(_u16(vc)).transpose(1, 0, 2)[slot], v_ref)):
         assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-4 * np.abs(ref).max())
         assert np.mean(got == ref) > 0.97
+
+
+@pytest.mark.parametrize("m", [1, 16, 32])
+def test_gemm_caller_counters_match_and_stay_zero(tvp, cuda, m):
+    """Arrival counters held by the caller (as the verification pass holds
+    them): every call leaves them at zero, and the result is the same bits as
+    a call whose counters the library clears in its workspace.  Two weights
+    with remaining groups (263 and 272 tiles) alternate over four calls."""
+    H, F = 1000, 4200
+    print(f"[gemm caller counters] m={m}", flush=True)
+    w_gu = bf16_bits_numpy(gen_linear_bf16(make_generator(51), 2 * F, H, TINY_RECIPE))
+    w_pl = bf16_bits_numpy(gen_linear_bf16(make_generator(52), 8704, H, TINY_RECIPE))
+    xb = _x(m, H, 53, cuda)
+    pgu = _packed(tvp, w_gu, cuda, tvp.TVP_CHAN_GATEUP, F)
+    ppl = _packed(tvp, w_pl, cuda)
+    cnt = torch.zeros(tvp.TVP_GEMM_COUNTERS, dtype=torch.int32, device=cuda)
+
+    def run(counters):
+        u = torch.zeros(m, F, dtype=torch.bfloat16, device=cuda)
+        y = torch.zeros(m, 8704, dtype=torch.bfloat16, device=cuda)
+        tvp.w12_gemm_ex(xb, pgu, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=u.data_ptr(), ldy=F,
+                                                     counters=counters))
+        tvp.w12_gemm_ex(xb, ppl, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_BF16, y=y.data_ptr(), ldy=8704,
+                                                     counters=counters))
+        torch.cuda.synchronize()
+        return u, y
+
+    u0, y0 = run(None)
+    for _ in range(2):
+        u1, y1 = run(cnt.data_ptr())
+        assert torch.equal(u0, u1) and torch.equal(y0, y1)
+        assert int(cnt.abs().sum()) == 0
+    xv, wv = from_bits(_u16(xb)), from_bits(w_pl)
+    ref = xv @ wv.T
+    fp32_err = 4.0 * H * 2.0 ** -24 * (np.abs(xv) @ np.abs(wv).T)
+    got = from_bits(_u16(y0))
+    assert np.all(np.abs(got - round_bf16(ref)) <= 2.0 ** -7 * np.abs(ref) + 2.0 * fp32_err)
 
 
 @pytest.mark.parametrize("m", [4, 70])  # skinny kernel's epilogue; wide kernel's fix-up (8 threads per row)

@@ -31,6 +31,7 @@ TVP_ERR_CAPACITY, TVP_ERR_FORMAT, TVP_ERR_WORKSPACE, TVP_ERR_HIP = 4, 5, 6, 7
 TVP_CHAN_PLAIN, TVP_CHAN_GATEUP, TVP_CHAN_QKV = 0, 1, 2
 TVP_FMT_W12, TVP_FMT_HI8 = 0, 1
 TVP_EPI_F32, TVP_EPI_BF16, TVP_EPI_RESID, TVP_EPI_SWIGLU, TVP_EPI_QKV, TVP_EPI_ARGMAX = range(6)
+TVP_GEMM_COUNTERS = 256  # arrival counters of one GEMM call (tvp_gemm_epilogue.counters)
 
 c_i32, c_i64, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -63,7 +64,7 @@ class TvpGemmEpilogue(ctypes.Structure):
     _fields_ = [("mode", c_i32), ("y", c_vp), ("ldy", c_i64), ("resid", c_vp), ("ldr", c_i64),
                 ("pos", c_vp), ("slot", c_vp), ("k_cache", c_vp), ("v_cache", c_vp), ("s_stride", c_i64),
                 ("rope_theta", ctypes.c_double), ("argmax", c_vp), ("logits", c_vp), ("ldl", c_i64),
-                ("x_packed", c_i32), ("y_packed", c_i32)]
+                ("x_packed", c_i32), ("y_packed", c_i32), ("counters", c_vp)]
 
 
 class TvpLayer(ctypes.Structure):

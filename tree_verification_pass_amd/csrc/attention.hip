@@ -41,8 +41,7 @@ __global__ __launch_bounds__(64) void tree_prep_kernel(const int32_t* __restrict
                                                        uint32_t* __restrict__ cnt, int ncnt) {
   __shared__ int32_t par[64];
   const int r = blockIdx.x, i = threadIdx.x;
-  // the attention's arrival counters start every pass at zero (each launch
-  // leaves them at zero again)
+  // the in-launch hand-overs' arrival counters start at zero
   for (int c = r * 64 + i; c < ncnt; c += gridDim.x * 64) cnt[c] = 0u;
   const int nb = ri.node_ptr[r], n = ri.node_ptr[r + 1] - nb;
   const int L = ri.ctx_len[r];
@@ -144,22 +143,6 @@ __device__ inline void lds_fence() {
 
 // Wavefronts per attention workgroup (two per SIMD).
 constexpr int kAttnWaves = 8;
-
-// Device-scope stores and loads (cache-scope bits of the agent scope): a
-// store is written through to the device's coherence point before it
-// counts as complete, and a load is served from there, never from a stale
-// line of this XCD's L2.  The split partials travel this way, so the split
-// that merges them may run on any XCD without a write-back or invalidate of
-// a whole L2 (which a device-scope fence costs on this part).
-__device__ inline void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// s_waitcnt with vmcnt 0 (expcnt and lgkmcnt at their maxima): every vector
-// memory access of this wavefront, stores included, has completed.
-constexpr int kWaitVmcnt0 = 0x0F70;
 
 // One workgroup per (request, kv head, 32-row block, key split); its NW
 // wavefronts stream disjoint 32-key blocks of the split (wavefront w takes
@@ -449,22 +432,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void tree_attn_kernel(AttnArgs a) 
   }
   if (nsplit == 1) return;
 
-  // Arrival: once every wavefront's partial stores are complete, one
-  // device-scope atomic counts this split in; the split that brings the
-  // count to nsplit merges the row block (and resets its counter).  No
-  // workgroup waits for another.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
+  // The split of this row block that arrives last merges all of them.
   __shared__ int s_last;
-  if (tid == 0) {
-    uint32_t* c = a.cnt + ((int64_t)r * a.hkv + kh) * kAttnRowBlocks + rb;
-    const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old == (uint32_t)(nsplit - 1);
-    if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
+  if (!arrive_last(a.cnt + ((int64_t)r * a.hkv + kh) * kAttnRowBlocks + rb, (uint32_t)nsplit, &s_last)) return;
 
   // Merge of the row block's splits, in split order with a running exponent
   // base (one pass, so the loads of up to 8 splits are in flight together).
@@ -525,7 +495,7 @@ constexpr int kAttnStages = 2;
 
 struct AttnPlan {
   int kr, max_splits, rows_total, row_blocks;
-  size_t off_cnt, off_po, off_pm, off_pl, bytes;
+  size_t off_po, off_pm, off_pl, bytes;
 };
 
 // max_keys: largest ctx_len + n over the requests; r_max: largest G * n;
@@ -543,8 +513,6 @@ static AttnPlan attn_plan(int hkv, int d, int r_max, int rows_total, int max_key
   p.rows_total = rows_total;
   const size_t rows = (size_t)hkv * p.max_splits * p.rows_total;
   size_t off = 0;
-  p.off_cnt = off;  // the arrival counters come first: tree preparation clears them
-  off = align_up(off + (size_t)attention_counters(n_req, hkv) * 4, 256);
   p.off_po = off;
   off = align_up(off + rows * d * 4, 256);
   p.off_pm = off;
@@ -556,11 +524,10 @@ static AttnPlan attn_plan(int hkv, int d, int r_max, int rows_total, int max_key
 }
 
 int launch_tree_prep(const int32_t* parents, const ReqInfo& ri, int32_t s_req, uint64_t* anc,
-                     int32_t* pos, int32_t* slot, int32_t* status, void* attn_scratch, int hkv,
+                     int32_t* pos, int32_t* slot, int32_t* status, uint32_t* cnt, int ncnt,
                      hipStream_t stream) {
-  tree_prep_kernel<<<dim3(ri.n_req), dim3(64), 0, stream>>>(parents, ri, s_req, anc, pos, slot, status,
-                                                            (uint32_t*)attn_scratch,
-                                                            attention_counters(ri.n_req, hkv));
+  tree_prep_kernel<<<dim3(ri.n_req), dim3(64), 0, stream>>>(parents, ri, s_req, anc, pos, slot, status, cnt,
+                                                            ncnt);
   TVP_LAUNCH_CHECK();
   return TVP_OK;
 }
@@ -568,7 +535,7 @@ int launch_tree_prep(const int32_t* parents, const ReqInfo& ri, int32_t s_req, u
 int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int64_t s_stride,
                           const ReqInfo& ri, int32_t s_req, const uint64_t* anc, int hq, int hkv, int d,
                           int r_max, int max_keys, uint16_t* out, int out_packed, void* scratch,
-                          size_t scratch_bytes, hipStream_t stream) {
+                          size_t scratch_bytes, uint32_t* cnt, hipStream_t stream) {
   if (r_max > 256 || r_max < 1) return TVP_ERR_SHAPE;
   if (out_packed && ri.node_ptr[ri.n_req] > 32) return TVP_ERR_SHAPE;
   const int n_req = ri.n_req;
@@ -595,7 +562,7 @@ int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t*
   a.kr = p.kr;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
   uint8_t* sb = (uint8_t*)scratch;
-  a.cnt = (uint32_t*)(sb + p.off_cnt);
+  a.cnt = cnt;
   a.po = (float*)(sb + p.off_po);
   a.pm = (float*)(sb + p.off_pm);
   a.pl = (float*)(sb + p.off_pl);
@@ -641,9 +608,10 @@ using namespace tvp;
 // needed):
 //   [0, 512)        anc u64 [64]
 //   [512, 1024)     pos/slot i32 [64] each
+//   [1024, ...)     arrival counters u32 [attention_counters(1, hkv)] (cleared by tree preparation)
 //   then            attention partials
 static size_t ta_layout(int32_t n, int32_t hq, int32_t hkv, int32_t d, int32_t max_keys, size_t* off_part) {
-  const size_t off = align_up(64 * 8 + 2 * 64 * 4, 256);
+  const size_t off = align_up(64 * 8 + 2 * 64 * 4 + (size_t)attention_counters(1, std::max(hkv, 1)) * 4, 256);
   *off_part = off;
   const int G = hkv > 0 ? hq / hkv : 1;
   return off + attention_scratch_bytes(hkv, G, d, G * n, n, max_keys);
@@ -683,10 +651,11 @@ int tree_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v
   ri.ctx_len[0] = ctx_len;
   ri.node_ptr[0] = 0;
   ri.node_ptr[1] = n;
-  int st = launch_tree_prep(parents, ri, 0, anc, pos, slot, status, w + offp, hkv, stream);
+  uint32_t* cnt = (uint32_t*)(w + 64 * 8 + 2 * 64 * 4);
+  int st = launch_tree_prep(parents, ri, 0, anc, pos, slot, status, cnt, attention_counters(1, hkv), stream);
   if (st != TVP_OK) return st;
   return launch_tree_attention(q, k_cache, v_cache, s_stride, ri, 0, anc, hq, hkv, d, (hq / hkv) * n,
-                               ctx_len + n, out, 0, w + offp, ws_bytes - offp, stream);
+                               ctx_len + n, out, 0, w + offp, ws_bytes - offp, cnt, stream);
 }
 
 }  // extern "C"

@@ -74,6 +74,40 @@ __device__ inline uint4 load_nt(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Device-scope stores and loads (the agent-scope cache bits): a store is
+// written through to the device's coherence point before it counts as
+// complete, and a load is served from there, never from a stale line of this
+// XCD's L2.  Data that one workgroup hands to another inside a launch
+// travels this way, so the receiver may run on any XCD without a write-back
+// or invalidate of a whole L2 (which a device-scope fence costs on this part).
+__device__ inline void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival of one workgroup at a counter shared by `total` workgroups, after
+// every thread's device-scope stores: each wavefront waits for its own
+// stores to complete (s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their
+// maxima), the workgroup meets at a barrier, and one thread increments the
+// counter with a device-scope atomic.  Returns true (to every thread) in the
+// workgroup that arrives last, which also puts the counter back to zero; by
+// then every other workgroup's stores are complete, so its device-scope
+// loads see them.  No workgroup waits for another.  `flag` is an LDS word.
+__device__ inline bool arrive_last(uint32_t* counter, uint32_t total, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == total - 1u;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
 // Order every LDS access of this wavefront issued before the call ahead of
 // those issued after it, without waiting on outstanding global loads.
 __device__ inline void wave_lds_sync() {

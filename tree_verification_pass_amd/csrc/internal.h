@@ -26,6 +26,9 @@ struct I8EpiArgs {
   const float* r;      // [n_out] bound radius
   const float* fnorm;  // [m] ||f_row||_2
 };
+// epi->counters (optional): TVP_GEMM_COUNTERS zero arrival counters for the
+// K slices of the remaining groups; without them they live in the scratch and
+// a small launch clears them first.
 int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, const tvp_w12_packed* w,
              const tvp_gemm_epilogue* epi, int y_packed, void* scratch, size_t scratch_bytes,
              hipStream_t stream, int ksplit = 1, const float* rope_cs = nullptr, const I8EpiArgs* i8 = nullptr);
@@ -63,19 +66,24 @@ void gemm_requirements(int64_t m, const tvp_w12_packed* w, int* groups, size_t* 
 int pack_tiles(const tvp_w12* t, tvp_w12_packed* p, void* ws, size_t ws_bytes, hipStream_t stream,
                int32_t layout);
 
-// Tree preparation also clears the arrival counters at the start of the
-// attention scratch that launch_tree_attention is then given.
+// Arrival counters (see arrive_last) of the in-launch hand-overs: they must
+// be zero when a launch starts, and every launch leaves them at zero.  Tree
+// preparation sets the ncnt counters at cnt to zero first.
 int launch_tree_prep(const int32_t* parents, const ReqInfo& ri, int32_t s_req, uint64_t* anc,
-                     int32_t* pos, int32_t* slot, int32_t* status, void* attn_scratch, int hkv,
+                     int32_t* pos, int32_t* slot, int32_t* status, uint32_t* cnt, int ncnt,
                      hipStream_t stream);
+// cnt: attention_counters(n_req, hkv) arrival counters, zero.
 int launch_tree_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, int64_t s_stride,
                           const ReqInfo& ri, int32_t s_req, const uint64_t* anc, int hq, int hkv, int d,
                           int r_max, int max_keys, uint16_t* out, int out_packed, void* scratch,
-                          size_t scratch_bytes, hipStream_t stream);
+                          size_t scratch_bytes, uint32_t* cnt, hipStream_t stream);
 size_t attention_scratch_bytes(int hkv, int G, int d, int r_max, int n_total, int max_keys);
 // 32-row blocks per (request, kv head) at most (256 rows), and the attention's
 // arrival counters for n_req requests: one per (request, kv head, row block).
 constexpr int kAttnRowBlocks = 8;
 inline int attention_counters(int n_req, int hkv) { return n_req * hkv * kAttnRowBlocks; }
+// Arrival counters a skinny GEMM launch with remaining-group K slices uses
+// at most (one per remaining group: fewer groups than compute units).
+constexpr int kGemmRemCounters = TVP_GEMM_COUNTERS;
 
 }  // namespace tvp

@@ -302,6 +302,8 @@ struct tvp_plan {
   size_t off_part;  // K-slice partial sums of the O and down projections (packed path)
   int ks_o, ks_down;  // their K slices at 32 rows
   size_t off_ascr, ascr_bytes;
+  size_t off_cnt;  // arrival counters: the GEMMs' (kGemmRemCounters), then the attention's
+  int n_cnt;
   size_t bytes;
 };
 
@@ -349,7 +351,7 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   p->ld_q = (int)align_up((size_t)hq * hd, 8);
   p->ld_u = (int)align_up(F, 8);
   const int mn = max_nodes;
-  // counters and scratch over every GEMM at every row count up to max_nodes
+  // scratch over every GEMM at every row count up to max_nodes
   int gmax = 1;
   size_t gscr = 256;
   auto need = [&](const tvp_w12_packed& w, bool sliced) {
@@ -425,6 +427,9 @@ int tvp_plan_create(const tvp_model_desc* d, int32_t max_nodes, tvp_plan** out) 
   for (int nr = 1; nr <= std::min(mn, 64) && G * nr <= 256; ++nr)
     p->ascr_bytes = std::max(p->ascr_bytes, attention_scratch_bytes(hkv, G, hd, G * nr, mn, d->s_max));
   off = align_up(off + p->ascr_bytes, 256);
+  p->off_cnt = off;
+  p->n_cnt = kGemmRemCounters + attention_counters(std::min(mn, kMaxReq), hkv);
+  off = align_up(off + (size_t)p->n_cnt * 4, 256);
   p->bytes = off;
   *out = p;
   return TVP_OK;
@@ -465,9 +470,11 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
   int32_t* bad = (int32_t*)(w + p->off_bad);
   void* gscr = w + p->off_gscr;
   void* ascr = w + p->off_ascr;
+  uint32_t* gcnt = (uint32_t*)(w + p->off_cnt);  // GEMM arrival counters
+  uint32_t* acnt = gcnt + kGemmRemCounters;       // attention arrival counters
   int st;
 
-  if ((st = launch_tree_prep(parents, ri, s_req, anc, pos, slot, tstat, ascr, hkv, stream))) return st;
+  if ((st = launch_tree_prep(parents, ri, s_req, anc, pos, slot, tstat, gcnt, p->n_cnt, stream))) return st;
   float* rope = (float*)(w + p->off_rope);
   if ((st = launch_rope_table(pos, n_total, hd, d.rope_theta, rope, stream))) return st;
   embed_kernel<<<dim3(n_total), dim3(256), 0, stream>>>(tokens, d.embed, H, d.vocab, h, p->ld_h, bad);
@@ -491,11 +498,12 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     e.v_cache = L.v_cache;
     e.s_stride = d.s_max;
     e.rope_theta = d.rope_theta;
+    e.counters = gcnt;
     if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wqkv, &e, 0, gscr, p->gscr_bytes,
                        stream, 1, rope)))
       return st;
     if ((st = launch_tree_attention(q, L.k_cache, L.v_cache, d.s_max, ri, s_req, anc, hq, hkv, hd, G * max_n,
-                                    max_keys, o, pk, ascr, p->ascr_bytes, stream)))
+                                    max_keys, o, pk, ascr, p->ascr_bytes, acnt, stream)))
       return st;
     // O projection + residual, then the FFN norm
     e = tvp_gemm_epilogue{};
@@ -521,6 +529,7 @@ static int run_pass(tvp_plan* p, const ReqInfo& ri, int32_t s_req, const int32_t
     e.mode = TVP_EPI_SWIGLU;
     e.y = u;
     e.ldy = p->ld_u;
+    e.counters = gcnt;
     if ((st = gemm_run(a, pk ? a : nullptr, n_total, p->ld_h, &L.wgu, &e, pk, gscr, p->gscr_bytes,
                        stream)))
       return st;

@@ -17,9 +17,12 @@
 //    scratch so escape values (about 1% of weights) are patched with one
 //    16-bit LDS store each, then the fragments feed v_mfma_f32_32x32x16_bf16
 //    (m > 16) or v_mfma_f32_16x16x32_bf16 (m <= 16).
-//  * K split over workgroups: fp32 partial sums go to the workspace and the
-//    next launch (a fix-up kernel, or the fused residual + RMSNorm) adds them
-//    in split order, so results are bitwise reproducible; no atomics and no
+//  * K split over workgroups: fp32 partial sums go to the workspace and are
+//    added in split order, so results are bitwise reproducible: by the next
+//    launch (the wide kernel's fix-up, or the fused residual + RMSNorm), or,
+//    for the K slices of a skinny launch's remaining groups, inside the
+//    launch by the slice that arrives last on a device-scope counter (the
+//    sums travel as device-scope stores and loads).  No float atomics and no
 //    device-scope fences.
 #include <math.h>
 
@@ -72,10 +75,12 @@ struct GemmArgs {
   // Skinny, whole-K epilogues: workgroups 0 .. full_groups-1 take whole
   // groups; the remaining groups are cut into rem_splits K slices of rem_kps
   // blocks (rem_kbs per wavefront) whose sums go to rpart [slice][row][ldrp]
-  // and are finished by w12_rem_fixup_kernel.
+  // (device-scope stores); the slice of a group that arrives last on
+  // rcnt[group - full_groups] sums them all and applies the epilogue.
   int full_groups, rem_splits, rem_kps, rem_kbs, rem_tpw;
   float* rpart;
   int ldrp;
+  uint32_t* rcnt;
   const float* rope_cs;  // QKV: optional per-pass (cos, sin) table, see gemm_run
   int cache_rowmap;      // epilogue: stage the group's channel rows in LDS first (many rows per thread)
 };
@@ -84,6 +89,11 @@ constexpr int kArgmaxMaxRows = 192;
 // Compute units the skinny decomposition balances over (MI355X: 256).
 constexpr int kNumCUs = 256;
 constexpr int kRemMaxSplits = 16;  // K slices of a remaining group (whole-K epilogues)
+
+// n arrival counters to zero (one workgroup).
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
+}
 
 // Row-major x [m][ldx] -> packed (rows >= m and columns >= k_in are zero).
 __global__ __launch_bounds__(256) void pack_x_kernel(const uint16_t* __restrict__ x, int64_t ldx, int m,
@@ -638,36 +648,56 @@ __global__ __launch_bounds__(512) void w12_skinny_kernel(GemmArgs a) {
     return v;
   };
   const int nc = min(NC, a.n_pad - t0 * 32);
-  if (MODE != kEpiPartial && rem) {  // this K slice's sums, [slice][row][channel - first remaining channel]
-    const int cb = t0 * 32 - a.full_groups * TPW * 32;
-    for (int idx = threadIdx.x; idx < M * nc; idx += KW * 64) {
-      const int row = idx / nc, c = idx % nc;
-      a.rpart[((int64_t)slice * M + row) * a.ldrp + cb + c] = sum_waves(row, t0 * 32 + c);
+  const int nthr = KW * 64;
+  float* S = nullptr;  // set: the epilogue reads the group's slice sums [M][nc] from LDS
+  if constexpr (MODE != kEpiPartial && MODE != TVP_EPI_ARGMAX && MODE != kEpiI8Approx) {
+    if (rem) {  // this K slice's sums, [slice][row][channel - first remaining channel]
+      const int cb = t0 * 32 - a.full_groups * TPW * 32;
+      const int ne = M * nc;
+      for (int idx = threadIdx.x; idx < ne; idx += nthr) {
+        const int row = idx / nc, c = idx % nc;
+        st_dev(a.rpart + ((int64_t)slice * M + row) * a.ldrp + cb + c, sum_waves(row, t0 * 32 + c));
+      }
+      // The slice that arrives last sums the group's slices in slice order
+      // (each thread the elements it stored; 8 slices x 8 elements in
+      // flight), stages the sums in LDS and applies the group's epilogue.
+      __shared__ int s_last;
+      if (!arrive_last(a.rcnt + (grp - a.full_groups), (uint32_t)a.rem_splits, &s_last)) return;
+      S = (float*)dsm;  // the partial tiles are no longer read
+      const int64_t sst = (int64_t)M * a.ldrp;
+      for (int e0 = 0; e0 < ne; e0 += 8 * nthr) {
+        float acc[8];
+        for (int s0 = 0; s0 < a.rem_splits; s0 += 8) {
+          float v[8][8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int64_t so = (int64_t)min(s0 + j, a.rem_splits - 1) * sst;  // past the last slice: repeated, unused
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int idx = min(e0 + i * nthr + (int)threadIdx.x, ne - 1);
+              v[j][i] = ld_dev(a.rpart + so + (int64_t)(idx / nc) * a.ldrp + cb + idx % nc);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              if (s0 + j == 0) acc[i] = v[j][i];
+              else if (s0 + j < a.rem_splits) acc[i] += v[j][i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int idx = e0 + i * nthr + (int)threadIdx.x;
+          if (idx < ne) S[idx] = acc[i];
+        }
+      }
+      __syncthreads();
     }
-    return;
   }
-  epilogue<MODE>(a, t0 * 32, nc, M, threadIdx.x, KW * 64, blockIdx.x, sum_waves, slice);
-}
-
-// One workgroup per tile of the remaining groups: the K slices summed in
-// slice order, then the same epilogue as a whole group.
-template <int MODE>
-__global__ __launch_bounds__(512) void w12_rem_fixup_kernel(GemmArgs a) {
-  const int cfirst = a.full_groups * a.rem_tpw * 32;
-  const int c0 = cfirst + blockIdx.x * 32;
-  const int nc = min(32, a.n_pad - c0);
-  auto sum_slices = [&](int row, int col) {
-    const float* src = a.rpart + (int64_t)row * a.ldrp + (col - cfirst);
-    const int64_t sstride = (int64_t)a.m * a.ldrp;
-    float v[kRemMaxSplits];
-#pragma unroll
-    for (int sl = 0; sl < kRemMaxSplits; ++sl) v[sl] = sl < a.rem_splits ? src[sl * sstride] : 0.0f;  // all in flight
-    float acc = v[0];
-#pragma unroll
-    for (int sl = 1; sl < kRemMaxSplits; ++sl) acc = sl < a.rem_splits ? acc + v[sl] : acc;
-    return acc;
-  };
-  epilogue<MODE>(a, c0, nc, a.m, threadIdx.x, 512, 0, sum_slices, 0);
+  // one epilogue instantiation for both sources (its LDS arrays exist once)
+  epilogue<MODE>(a, t0 * 32, nc, M, threadIdx.x, nthr, blockIdx.x,
+                 [&](int row, int col) { return S ? S[row * nc + (col - t0 * 32)] : sum_waves(row, col); }, slice);
 }
 
 // ----------------------------------------------------------------------------
@@ -975,7 +1005,7 @@ struct GemmPlan {
   int MT, RB, TPW, RD, KW, TG, groups, splits, kbs, kps, ntasks, grid;
   int kbs_split, key_slots;
   int full_groups, rem_groups, rem_splits, rem_kps, rem_kbs;  // whole-K epilogues, see GemmArgs
-  size_t keys_off, rem_off, scratch_bytes;
+  size_t keys_off, rem_off, cnt_off, scratch_bytes;
 };
 
 // Work decomposition.  Skinny (m <= 32): one workgroup per TPW tiles whose KW
@@ -1015,8 +1045,9 @@ static double slice_cost(int gsplit, int s, int kps) {
   return per_cu <= 1 ? kSliceSingle * cost : cost;
 }
 
-// rem_ok: the epilogue can be finished by w12_rem_fixup_kernel (not argmax,
-// whose per-row reduction over 32 columns would run on too few lanes).
+// rem_ok: the epilogue can be applied by the slice of a remaining group that
+// arrives last (not argmax, whose per-row reduction over 32 columns would
+// run on too few lanes).
 static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bool rem_ok = true) {
   GemmPlan p{};
   const int64_t n_pad = (int64_t)w->n_tiles * 32;
@@ -1066,11 +1097,14 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
     const int R = p.groups > kNumCUs ? p.groups % kNumCUs : 0;
     if (!partial && rem_ok && R > 0 && nkb >= 4) {
       // slices per remaining group: the fewest that minimise the busiest
-      // CU's share of slices, ceil(R * s / CUs) / s
+      // CU's slices, ceil(R * s / CUs), times each slice's blocks plus the
+      // fixed cost of a workgroup (measured: the 4B-like gate/up's 96
+      // remaining groups in 2 slices of 20 blocks instead of 8 of 5 made
+      // its verify step 3% faster; 27B-like shapes keep 8 slices)
       int sl = 1;
-      double best = 1.0;
+      double best = 1e30;
       for (int c = 2; c <= std::min(kRemMaxSplits, nkb / 2); ++c) {
-        const double v = (double)ceil_div((int64_t)R * c, kNumCUs) / c;
+        const double v = (double)ceil_div((int64_t)R * c, kNumCUs) * ((double)ceil_div(nkb, c) + kSliceFixed);
         if (v < best - 1e-9) best = v, sl = c;
       }
       p.rem_kps = (int)ceil_div(nkb, sl);
@@ -1116,7 +1150,8 @@ static GemmPlan make_plan(int64_t m, const tvp_w12_packed* w, int ksplit = 1, bo
   p.keys_off = p.skinny ? align_up((size_t)std::max(nkb, 1) * 4096, 256)
                         : align_up((size_t)p.splits * m * n_pad * 4, 256);
   p.rem_off = p.keys_off + align_up((size_t)std::max(p.key_slots, 1) * m * 8, 256);
-  p.scratch_bytes = p.rem_off + align_up((size_t)p.rem_splits * m * p.rem_groups * p.TPW * 32 * 4, 256);
+  p.cnt_off = p.rem_off + align_up((size_t)p.rem_splits * m * p.rem_groups * p.TPW * 32 * 4, 256);
+  p.scratch_bytes = p.cnt_off + align_up((size_t)p.rem_groups * 4, 256);
   return p;
 }
 
@@ -1143,17 +1178,6 @@ template <int MT, int TPW, int RD>
 static void launch_skinny(const GemmArgs& a, const GemmPlan& p, hipStream_t stream) {
   if (a.fmt == TVP_FMT_W12) launch_skinny_fmt<MT, TPW, RD, TVP_FMT_W12>(a, p, stream);
   else launch_skinny_fmt<MT, TPW, RD, TVP_FMT_HI8>(a, p, stream);
-  if (p.rem_groups > 0) {  // launch errors of both are read by the caller's check
-    const dim3 fgrid((unsigned)(a.n_tiles - p.full_groups * TPW));
-    switch (a.mode) {
-      case TVP_EPI_F32: w12_rem_fixup_kernel<TVP_EPI_F32><<<fgrid, 512, 0, stream>>>(a); break;
-      case TVP_EPI_BF16: w12_rem_fixup_kernel<TVP_EPI_BF16><<<fgrid, 512, 0, stream>>>(a); break;
-      case TVP_EPI_RESID: w12_rem_fixup_kernel<TVP_EPI_RESID><<<fgrid, 512, 0, stream>>>(a); break;
-      case TVP_EPI_SWIGLU: w12_rem_fixup_kernel<TVP_EPI_SWIGLU><<<fgrid, 512, 0, stream>>>(a); break;
-      case TVP_EPI_QKV: w12_rem_fixup_kernel<TVP_EPI_QKV><<<fgrid, 512, 0, stream>>>(a); break;
-      default: break;  // argmax and partial-sum launches never split their remaining groups
-    }
-  }
 }
 
 template <int RB>
@@ -1279,6 +1303,13 @@ int gemm_run(const uint16_t* x, const uint16_t* xp, int64_t m, int64_t ldx, cons
   a.rem_tpw = p.TPW;
   a.rpart = (float*)((uint8_t*)scratch + p.rem_off);
   a.ldrp = p.rem_groups * p.TPW * 32;
+  a.rcnt = epi->counters;
+  if (p.rem_groups > kGemmRemCounters) return TVP_ERR_SHAPE;  // fewer remaining groups than CUs by construction
+  if (p.rem_groups > 0 && !a.rcnt) {  // the arrival counters live in the scratch: clear them first
+    a.rcnt = (uint32_t*)((uint8_t*)scratch + p.cnt_off);
+    zero_u32_kernel<<<dim3(1), dim3(256), 0, stream>>>(a.rcnt, p.rem_groups);
+    TVP_LAUNCH_CHECK();
+  }
   a.rope_cs = epi->mode == TVP_EPI_QKV ? rope_cs : nullptr;
   a.ntasks = p.ntasks;
   a.keys = (unsigned long long*)((uint8_t*)scratch + p.keys_off);
