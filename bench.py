@@ -1156,7 +1156,7 @@ def main() -> int:
                    "ffn": cfg.ffn, "vocab": cfg.vocab, "nodes": cfg.n_nodes, "ctx_len": cfg.ctx_len,
                    "weights": "W12 (random-init bf16, per-channel sigma log-uniform [0.005,0.05], 1% zeros, "
                               "0.05% outliers x1000)", "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": (f"w12_skinny_kernel<32,2,2,SWIGLU> (fused gate/up, {2 * cfg.ffn}x{cfg.hidden}; "
+        "roofline": {"kernel": (f"w12_skinny_kernel, SWIGLU epilogue (fused gate/up, {2 * cfg.ffn}x{cfg.hidden}; "
                                 "the remaining groups' K slices finished in the launch)"), "bound": "hbm",
                      "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(g_gbs / HBM_PEAK_GBS, 4), "probe_frac": round(g_gbs / probe, 4),
