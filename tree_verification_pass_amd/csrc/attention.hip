@@ -508,7 +508,7 @@ static AttnPlan attn_plan(int hkv, int d, int r_max, int rows_total, int max_key
   const int target = std::max(1, kAttnTargetGroups / std::max(1, n_req * hkv * p.row_blocks));
   const int unit = 32 * kAttnWaves;
   p.kr = unit * (int)ceil_div(std::max(max_keys, 1), (int64_t)unit * target);
-  while (max_keys > 64 * p.kr) p.kr *= 2;  // at most 64 splits (merge weights live in LDS)
+  while (max_keys > 64 * p.kr) p.kr *= 2;  // at most 64 splits (the merge reads 8 per pass)
   p.max_splits = max_keys > 0 ? (max_keys + p.kr - 1) / p.kr : 1;
   p.rows_total = rows_total;
   const size_t rows = (size_t)hkv * p.max_splits * p.rows_total;
