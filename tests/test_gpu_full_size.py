@@ -257,3 +257,19 @@ def test_verify_step_4b_full_depth(cuda):
     assert int(res.n_accepted.item()) == a_own and int(res.bonus.item()) == b_own
     assert res.path.cpu().numpy()[: a_own + 1].tolist() == p_own
     assert acceptance_ok(am, ref["argmax"], tokens, parents, chk["decidable"])
+    # The in-launch hand-overs (tree attention's split merge, the gate/up
+    # GEMM's remaining groups) with two trees alternating on one workspace:
+    # a stale read of the other tree's partials, or of another layer's, would
+    # change bits; every pass must reproduce its tree's first result exactly.
+    rng2 = np.random.default_rng(14)
+    parents_b, _, _ = best_first_topology(rng2, n)
+    tokens_b = rng2.integers(0, cfg.vocab, n).astype(np.int32)
+    tokens_b[0] = root
+    first_b = tvp.verify_step(dm.plan, L, to_i32(tokens_b), to_i32(parents_b), commit=False, want_logits=True)
+    torch.cuda.synchronize()
+    print("  alternating trees, 16 passes", flush=True)
+    for it in range(8):
+        for tk, pa, want in ((tokens, parents, res.logits), (tokens_b, parents_b, first_b.logits)):
+            again = tvp.verify_step(dm.plan, L, to_i32(tk), to_i32(pa), commit=False, want_logits=True)
+            torch.cuda.synchronize()
+            assert torch.equal(again.logits, want), it
