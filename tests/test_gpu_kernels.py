@@ -353,7 +353,10 @@ def _attn_ref(parents, q, kc, vc, L):
                                           (5, 10, 2, 128, 513),
                                           # two 32-row blocks per workgroup: three blocks (one pair
                                           # half empty), one pair with a single split, four blocks
-                                          (13, 5, 1, 128, 300), (32, 8, 4, 128, 100), (20, 12, 2, 128, 1500)])
+                                          (13, 5, 1, 128, 300), (32, 8, 4, 128, 100), (20, 12, 2, 128, 1500),
+                                          # merges over more than one pass of 8 splits: one-node decoding
+                                          # (15 splits of 288 keys) and 32 splits of 256 keys
+                                          (1, 40, 8, 128, 4096), (2, 8, 2, 64, 8000)])
 def test_tree_attention_matches_oracle(tvp, cuda, n, hq, hkv, d, L):
     print(f"[tree_attention] n={n} hq={hq} hkv={hkv} d={d} L={L}", flush=True)
     parents, q, kc, vc = _attn_case(cuda, n, hq, hkv, d, L, seed=n + L)
