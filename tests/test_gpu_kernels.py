@@ -370,6 +370,23 @@ def test_tree_attention_matches_oracle(tvp, cuda, n, hq, hkv, d, L):
     assert torch.equal(out, out2)
 
 
+def test_tree_attention_merge_repeatable(tvp, cuda):
+    """The in-launch split merge (device-scope partial stores, an arrival
+    counter per row block, the last split merging every split in split
+    order) at the 27B-like shape, 32 nodes over 4096 keys, over many
+    launches in a row: every launch gives the same bits."""
+    n, hq, hkv, d, L, reps = 32, 40, 8, 128, 4096, 48
+    print(f"[tree_attention] merge over {reps} launches n={n} hq={hq} hkv={hkv} L={L}", flush=True)
+    parents, q, kc, vc = _attn_case(cuda, n, hq, hkv, d, L, seed=7)
+    qd, kd, vd = q.to(cuda), kc.to(cuda), vc.to(cuda)
+    pd = torch.as_tensor(parents, device=cuda)
+    outs = [tvp.tree_attention(qd, kd, vd, L, pd) for _ in range(reps)]
+    torch.cuda.synchronize()
+    assert all(int(st.item()) == 0 for _, st in outs)
+    same = [torch.equal(outs[0][0], o) for o, _ in outs[1:]]
+    assert all(same), f"{same.count(False)} of {reps - 1} launches differ from the first"
+
+
 def test_tree_attention_chain_equals_causal_and_star(tvp, cuda):
     n, hq, hkv, d, L = 16, 8, 2, 128, 100
     for parents in (np.arange(-1, n - 1, dtype=np.int32), np.array([-1] + [0] * (n - 1), dtype=np.int32)):

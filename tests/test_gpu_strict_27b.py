@@ -2,9 +2,10 @@
 own inputs (seeded synthetic tensors; nothing computed on the GPU is fed back):
 
 * the fused gate/up GEMM with SwiGLU (34816 x 5120: two tiles per workgroup,
-  the channel groups past the last full round as K slices finished by a
-  second launch) from packed activations to packed output, at 1, 16 and 32
-  rows -- the 16-row MFMA shape below 17 rows, the 32-row shape above;
+  the channel groups past the last full round as K slices, each group
+  finished inside the launch by its slice that arrives last) from packed
+  activations to packed output, at 1, 16 and 32 rows -- the 16-row MFMA
+  shape below 17 rows, the 32-row shape above;
 * the LM head (151936 x 5120) with its argmax and the fp32 logits dump, at 1,
   16 and 32 rows;
 * the O (5120 x 5120) and down (5120 x 17408) projections with the residual
@@ -122,6 +123,30 @@ def test_gateup_swiglu_27b_strict(tvp, cuda, gateup, m):
     assert torch.equal(outs[0][: F * 32].view(torch.int16), outs[1][: F * 32].view(torch.int16))
     got = from_bits(unpack_rows_host(_u16(outs[0]), m, F))
     _same_bf16(got, u_ref[:m], f"swiglu m={m}")
+
+
+def test_gateup_handover_repeatable_27b(tvp, cuda, gateup):
+    """The remaining groups' in-launch hand-over (device-scope slice stores,
+    an arrival counter, the last slice summing them) over many launches in a
+    row on one caller-held counter array, as the pass runs it: every launch
+    gives the same bits and leaves the counters at zero."""
+    F = CFG.ffn
+    pw, x, _ = gateup
+    m, reps = 32, 48
+    print(f"[strict 27b] gate/up hand-over, {reps} launches, m={m}", flush=True)
+    xp = _dev(pack_rows_host(x[:m]), cuda)
+    cnt = torch.zeros(tvp.TVP_GEMM_COUNTERS, dtype=torch.int32, device=cuda)
+    outs = []
+    for _ in range(reps):
+        yp = torch.full((tvp.w12_packed_x_elems(F),), float("nan"), dtype=torch.bfloat16, device=cuda)
+        tvp.w12_gemm_px(xp, m, pw, tvp.TvpGemmEpilogue(mode=tvp.TVP_EPI_SWIGLU, y=yp.data_ptr(), y_packed=1,
+                                                      counters=cnt.data_ptr()))
+        outs.append(yp)
+    torch.cuda.synchronize()
+    assert int(cnt.abs().sum()) == 0
+    ref = outs[0][: F * 32].view(torch.int16)
+    same = [torch.equal(ref, o[: F * 32].view(torch.int16)) for o in outs[1:]]
+    assert all(same), f"{same.count(False)} of {reps - 1} launches differ from the first"
 
 
 # ----------------------------------------------------------------- LM head
