@@ -506,8 +506,12 @@ static AttnPlan attn_plan(int hkv, int d, int r_max, int rows_total, int max_key
   AttnPlan p{};
   p.row_blocks = (r_max + 31) / 32;
   const int target = std::max(1, kAttnTargetGroups / std::max(1, n_req * hkv * p.row_blocks));
-  const int unit = 32 * kAttnWaves;
-  p.kr = unit * (int)ceil_div(std::max(max_keys, 1), (int64_t)unit * target);
+  // whole 32-key blocks, at least one per wavefront: sized in blocks rather
+  // than in one block per wavefront, the 4B-like step (6 -> 8 splits, 192 ->
+  // 256 workgroups) ran 2.9% faster and the 8-node step (8 -> 15 splits)
+  // 1.2%; with fewer keys than one block per wavefront (one-node decoding:
+  // 26 splits of 160 keys) decoding ran 1.9% slower, hence the floor
+  p.kr = std::max(32 * kAttnWaves, 32 * (int)ceil_div(std::max(max_keys, 1), (int64_t)32 * target));
   while (max_keys > 64 * p.kr) p.kr *= 2;  // at most 64 splits (the merge reads 8 per pass)
   p.max_splits = max_keys > 0 ? (max_keys + p.kr - 1) / p.kr : 1;
   // A last split under a quarter of the others (one-node decoding over 4096
